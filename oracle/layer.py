@@ -1,0 +1,100 @@
+"""The quantized linear layer in fp64 (test infrastructure only).
+
+Structure from the SVDQuant Guide (aifetchly):
+* "The Three Pillars of SVDQuant", 1. Mathematical Outlier Factorization: the
+  forward projection is the 4-bit GEMM of the quantized weight and the quantized
+  activation, plus the low-rank branch L1 (L2 X) applied to the *unquantized*
+  activation.
+* "Step 2: The SVDQuant Dual-Branch Linear Layer": the low-rank branch is evaluated
+  right to left (down-projection to rank r first), the two branches are summed,
+  the bias is added last.
+
+Orientation used here: X [M, K] (tokens x in-features), the weight as W^T [N, K]
+(out-features x in-features), Y [M, N].  The low-rank factors are taken as
+L1 [K, r] (the down-projection, applied first) and L2 [r, N]; in the page's
+notation (W of shape d_out x d_in acting on column activations) these are the
+transposes of its L2 and L1.
+"""
+
+import numpy as np
+
+from .formats import bf16_to_f64, bf16_ulp
+
+GEMM_REL_TOL = 1e-3
+
+
+def gemm_ref(a_deq, b_deq, bias=None, x=None, l1=None, l2=None):
+    """Y = A_deq B_deq^T (+ (X L1) L2) (+ bias) in fp64, and the per-element bound.
+
+    a_deq [M, K], b_deq [N, K]: dequantized operands (fp64, exact).
+    x [M, K], l1 [K, r], l2 [r, N]: the low-rank branch on the unquantized X.
+    bias [N].
+
+    Returns (y, bound) where bound[m, n] is the sum of the magnitudes of every
+    product that enters y[m, n]:
+        sum_k |a_mk b_nk| + sum_j (sum_k |x_mk l1_kj|) |l2_jn| + |bias_n|.
+    """
+    a_deq = np.asarray(a_deq, dtype=np.float64)
+    b_deq = np.asarray(b_deq, dtype=np.float64)
+    y = a_deq @ b_deq.T
+    bound = np.abs(a_deq) @ np.abs(b_deq).T
+    if l1 is not None:
+        x = np.asarray(x, dtype=np.float64)
+        l1 = np.asarray(l1, dtype=np.float64)
+        l2 = np.asarray(l2, dtype=np.float64)
+        t = x @ l1                       # rank-r down-projection first
+        y = y + t @ l2
+        bound = bound + (np.abs(x) @ np.abs(l1)) @ np.abs(l2)
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float64)
+        y = y + bias[None, :]
+        bound = bound + np.abs(bias)[None, :]
+    return y, bound
+
+
+def lowrank_down(x, l1):
+    """t = X L1 in fp64: the low-rank branch's rank-r intermediate."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(l1, dtype=np.float64)
+
+
+def tolerance(y_ref, bound, out_bf16):
+    """Allowed |Y_gpu - Y_ref| per element.
+
+    fp32 output: 1e-3 * bound (the bound of ``gemm_ref``).
+    bf16 output: the stored value is the bf16 rounding of a result that is itself
+    within 1e-3 * bound, so half a bf16 ulp at that result is added; the ulp is
+    taken at |y_ref| + 1e-3 * bound, which is at least the result's magnitude.
+    """
+    tol = GEMM_REL_TOL * np.asarray(bound, dtype=np.float64)
+    if out_bf16:
+        tol = tol + 0.5 * bf16_ulp(np.abs(y_ref) + tol)
+    return tol
+
+
+def check_close(y_gpu, y_ref, bound, out_bf16):
+    """Returns (ok, worst_ratio, index): worst |err| / tol over all elements."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    tol = tolerance(y_ref, bound, out_bf16)
+    err = np.abs(y_gpu - y_ref)
+    # an exact zero tolerance only admits an exact match
+    ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1.0), np.where(err > 0, np.inf, 0.0))
+    if not np.all(np.isfinite(y_gpu)):
+        return False, np.inf, None
+    i = np.unravel_index(np.argmax(ratio), ratio.shape) if ratio.size else None
+    worst = float(ratio[i]) if ratio.size else 0.0
+    return worst <= 1.0, worst, i
+
+
+def relative_error(y, y_exact):
+    """Quality context (not pass/fail): ||Y - Y_exact||_F / ||Y_exact||_F."""
+    y = np.asarray(y, dtype=np.float64)
+    y_exact = np.asarray(y_exact, dtype=np.float64)
+    return float(np.linalg.norm(y - y_exact) / max(np.linalg.norm(y_exact), 1e-300))
+
+
+def unquantized_ref(x_bits, wt_bits, bias_bits=None):
+    """The unquantized bf16 layer X W^T (+ bias) in fp64: the quality context."""
+    y = bf16_to_f64(x_bits) @ bf16_to_f64(wt_bits).T
+    if bias_bits is not None:
+        y = y + bf16_to_f64(bias_bits)[None, :]
+    return y
