@@ -1,0 +1,133 @@
+// The C ABI of libq4lin (declared in include/q4lin.h): argument checks on the
+// host, then the launches, queued on the caller's stream.  No allocation, no
+// synchronization, no state.
+#include "q4lin.h"
+
+#include "q4_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+q4_status launched(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_LAUNCH; }
+
+bool rank_ok(int32_t r) { return r == 0 || r == 16 || r == 32; }
+
+// Checks shared by the two W4A4 entry points.
+q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                     const float* a_tscale, const uint8_t* b_codes, const uint8_t* b_scales,
+                     const float* b_tscale, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy,
+                     q4_out out) {
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4) return Q4_ERR_FORMAT;
+  if (out != Q4_OUT_BF16 && out != Q4_OUT_F32) return Q4_ERR_FORMAT;
+  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || ldy < N) return Q4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return Q4_ERR_NULL;
+  if (fmt == Q4_NVFP4 && (!a_tscale || !b_tscale)) return Q4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(y, 16) || (ldy % 8) != 0)
+    return Q4_ERR_ALIGN;
+  if (fmt == Q4_NVFP4 && (!aligned(a_tscale, 4) || !aligned(b_tscale, 4))) return Q4_ERR_ALIGN;
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_status_string(q4_status s) {
+  switch (s) {
+    case Q4_OK: return "Q4_OK";
+    case Q4_ERR_NULL: return "Q4_ERR_NULL";
+    case Q4_ERR_SHAPE: return "Q4_ERR_SHAPE";
+    case Q4_ERR_ALIGN: return "Q4_ERR_ALIGN";
+    case Q4_ERR_FORMAT: return "Q4_ERR_FORMAT";
+    case Q4_ERR_LAUNCH: return "Q4_ERR_LAUNCH";
+  }
+  return "unknown";
+}
+
+q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                       uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                       const uint16_t* l1t, int32_t r, float* t, void* stream) {
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4) return Q4_ERR_FORMAT;
+  if (M < 0 || K < 0 || (K % 32) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (!x || !codes || !scales) return Q4_ERR_NULL;
+  if (fmt == Q4_NVFP4 && !tensor_scale) return Q4_ERR_NULL;
+  if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
+  if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(codes, 16) || !aligned(scales, 4))
+    return Q4_ERR_ALIGN;
+  if (fmt == Q4_NVFP4 && !aligned(tensor_scale, 4)) return Q4_ERR_ALIGN;
+  if (r > 0 && (!aligned(l1t, 16) || !aligned(t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0) return Q4_OK;
+  return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t,
+                                          (int)r, t, static_cast<hipStream_t>(stream)));
+}
+
+q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, int64_t stride_k,
+                       int64_t stride_n, uint8_t* codes, void* scales, uint16_t* zeros,
+                       float* tensor_scale, void* stream) {
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_G64) return Q4_ERR_FORMAT;
+  const int64_t blk = fmt == Q4_INT4_G64 ? 64 : 32;
+  if (K < 0 || N < 0 || (K % blk) != 0 || stride_k < 1 || stride_n < 1) return Q4_ERR_SHAPE;
+  if (!w || !codes || !scales) return Q4_ERR_NULL;
+  if (fmt == Q4_INT4_G64 && !zeros) return Q4_ERR_NULL;
+  if (fmt == Q4_NVFP4 && !tensor_scale) return Q4_ERR_NULL;
+  if (!aligned(w, 2) || !aligned(codes, 16) || !aligned(scales, 4)) return Q4_ERR_ALIGN;
+  if (fmt == Q4_INT4_G64 && !aligned(zeros, 2)) return Q4_ERR_ALIGN;
+  if (fmt == Q4_NVFP4 && !aligned(tensor_scale, 4)) return Q4_ERR_ALIGN;
+  if (N == 0) return Q4_OK;
+  return launched(q4::launch_pack_weights((int)fmt, w, K, N, stride_k, stride_n, codes, scales, zeros,
+                                          tensor_scale, static_cast<hipStream_t>(stream)));
+}
+
+q4_status gemm_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                    const float* a_tscale, const uint8_t* b_codes, const uint8_t* b_scales,
+                    const float* b_tscale, int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                    void* y, int64_t ldy, q4_out out, void* stream) {
+  q4_status st = check_w4a4(fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K,
+                            y, ldy, out);
+  if (st != Q4_OK) return st;
+  if (M == 0 || N == 0) return Q4_OK;
+  q4::EpilogueArgs ep{nullptr, nullptr, 0, bias, y, ldy, out == Q4_OUT_F32 ? 1 : 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt == Q4_MXFP4) return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
+  return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
+}
+
+q4_status gemm_w4a4_lowrank(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales,
+                            const float* a_tscale, const uint8_t* b_codes, const uint8_t* b_scales,
+                            const float* b_tscale, int64_t M, int64_t N, int64_t K, const float* t,
+                            const uint16_t* l2t, int32_t r, const uint16_t* bias, void* y,
+                            int64_t ldy, q4_out out, void* stream) {
+  q4_status st = check_w4a4(fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K,
+                            y, ldy, out);
+  if (st != Q4_OK) return st;
+  if (!rank_ok(r)) return Q4_ERR_SHAPE;
+  if (r > 0 && (!t || !l2t)) return Q4_ERR_NULL;
+  if (r > 0 && (!aligned(t, 16) || !aligned(l2t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0 || N == 0) return Q4_OK;
+  q4::EpilogueArgs ep{r > 0 ? t : nullptr, r > 0 ? l2t : nullptr, (int)r, bias, y, ldy,
+                      out == Q4_OUT_F32 ? 1 : 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt == Q4_MXFP4) return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
+  return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
+}
+
+q4_status gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* w_codes,
+                     const uint16_t* w_scales, const uint16_t* w_zeros, int64_t M, int64_t N,
+                     int64_t K, int32_t group, const uint16_t* bias, void* y, int64_t ldy,
+                     q4_out out, void* stream) {
+  if (out != Q4_OUT_BF16 && out != Q4_OUT_F32) return Q4_ERR_FORMAT;
+  if (group != 64) return Q4_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || (K % 64) != 0 || ldx < K || ldy < N) return Q4_ERR_SHAPE;
+  if (!x || !w_codes || !w_scales || !w_zeros || !y) return Q4_ERR_NULL;
+  if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(w_codes, 16) || !aligned(w_scales, 2) ||
+      !aligned(w_zeros, 2) || !aligned(y, 16) || (ldy % 8) != 0)
+    return Q4_ERR_ALIGN;
+  if (M == 0 || N == 0) return Q4_OK;
+  q4::EpilogueArgs ep{nullptr, nullptr, 0, bias, y, ldy, out == Q4_OUT_F32 ? 1 : 0};
+  return launched(q4::launch_gemm_w4a16(x, ldx, w_codes, w_scales, w_zeros, M, N, K, ep,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

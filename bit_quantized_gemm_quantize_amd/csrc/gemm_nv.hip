@@ -1,0 +1,125 @@
+// NVFP4-style GEMM, exact: every operand value e2m1 * s_b (two significant bits
+// times the four of an E4M3 scale) fits bf16 exactly, so each K-tile is dequantized
+// to bf16 in LDS and multiplied on the bf16 MFMA; the two fp32 tensor scales
+// multiply the fp32 result in the epilogue.  The block-scaled FP4 MFMA cannot take
+// this format directly: its scales are powers of two per 32 elements, while an
+// NVFP4 block scale carries mantissa bits and covers 16 elements.
+#include "gemm_bf16_core.h"
+
+namespace q4 {
+
+// Two E2M1 codes (byte B of a dword) times the block scale -> a bf16 pair.  The
+// products are exact bf16 values, so keeping the upper halves is exact.
+template <int B>
+__device__ __forceinline__ uint32_t nv_dequant_pair(uint32_t codes, float s) {
+  const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B);
+  const uint32_t lo = __float_as_uint(v[0] * s), hi = __float_as_uint(v[1] * s);
+  return (lo >> 16) | (hi & 0xFFFF0000u);
+}
+
+// 32 E2M1 codes (one 16-byte chunk) times their two block scales -> 4 chunks of bf16.
+__device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x4* out4) {
+  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)(sc2 & 0xFFu), 0);
+  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)((sc2 >> 8) & 0xFFu), 0);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float s = d < 2 ? s0 : s1;
+    out4[d] = u32x4{nv_dequant_pair<0>(codes[d], s), nv_dequant_pair<1>(codes[d], s),
+                    nv_dequant_pair<2>(codes[d], s), nv_dequant_pair<3>(codes[d], s)};
+  }
+}
+
+struct NvLoader {
+  const uint8_t* ac; const uint8_t* as; const uint8_t* bc; const uint8_t* bs;
+  int64_t M, N, K, m0, n0;
+  int tid;
+  u32x4 ca[2], cb[2];
+  uint32_t sa[2], sb[2];
+
+  // chunk (row, c): row = tid/2 + 128 j, c = tid & 1 (two 16-byte code chunks per row)
+  __device__ __forceinline__ void load(int kt) {
+    const int64_t kb = K >> 1, sbytes = K >> 4;
+    const int c = tid & 1;
+    const int64_t blk32 = (int64_t)kt * 2 + c;       // 32-element chunk index along K
+    const bool kok = blk32 < (K >> 5);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = (tid >> 1) + 128 * j;
+      const bool aok = kok && m0 + row < M, bok = kok && n0 + row < N;
+      ca[j] = aok ? ld16(ac + (m0 + row) * kb + blk32 * 16) : u32x4{0, 0, 0, 0};
+      cb[j] = bok ? ld16(bc + (n0 + row) * kb + blk32 * 16) : u32x4{0, 0, 0, 0};
+      sa[j] = aok ? *reinterpret_cast<const uint16_t*>(as + (m0 + row) * sbytes + 2 * blk32) : 0u;
+      sb[j] = bok ? *reinterpret_cast<const uint16_t*>(bs + (n0 + row) * sbytes + 2 * blk32) : 0u;
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb) {
+    const int c = tid & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = (tid >> 1) + 128 * j;
+      u32x4 o[4];
+      nv_dequant_chunk(ca[j], sa[j], o);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) st16(la + lds_chunk_off(row, 4 * c + d), o[d]);
+      nv_dequant_chunk(cb[j], sb[j], o);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) st16(lb + lds_chunk_off(row, 4 * c + d), o[d]);
+    }
+  }
+};
+
+template <int R, bool OUT_F32>
+__global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ t, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kBf16BM * kBf16RowBytes];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
+  NvLoader ld;
+  ld.ac = ac; ld.as = as; ld.bc = bc; ld.bs = bs;
+  ld.M = M; ld.N = N; ld.K = K;
+  ld.m0 = (int64_t)tm * kBf16BM; ld.n0 = (int64_t)tn * kBf16BN;
+  ld.tid = tid;
+  v16f acc[4][4];
+  bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
+
+  const float scale = ats[0] * bts[0];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = acc[f][g] * scale;
+  const int64_t n_base = ld.n0 + wy * 128, m_base = ld.m0 + wx * 128;
+  if (R > 0) epilogue_lowrank<R>(acc, n_base, m_base, M, N, t, l2t, lane);
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane);
+}
+
+template <int R, bool F32>
+static void queue(const uint8_t* ac, const uint8_t* as, const float* ats, const uint8_t* bc,
+                  const uint8_t* bs, const float* bts, int64_t M, int64_t N, int64_t K,
+                  const EpilogueArgs& ep, hipStream_t s) {
+  const int tiles_m = (int)((M + kBf16BM - 1) / kBf16BM), tiles_n = (int)((N + kBf16BN - 1) / kBf16BN);
+  hipLaunchKernelGGL((gemm_nv_kernel<R, F32>), dim3(tiles_m * tiles_n), dim3(kBf16Threads), 0, s,
+                     ac, as, ats, bc, bs, bts, M, N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m,
+                     tiles_n);
+}
+
+hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats,
+                          const uint8_t* bc, const uint8_t* bs, const float* bts, int64_t M,
+                          int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
+  if (ep.out_f32) {
+    if (ep.r == 0) queue<0, true>(ac, as, ats, bc, bs, bts, M, N, K, ep, s);
+    else if (ep.r == 16) queue<16, true>(ac, as, ats, bc, bs, bts, M, N, K, ep, s);
+    else queue<32, true>(ac, as, ats, bc, bs, bts, M, N, K, ep, s);
+  } else {
+    if (ep.r == 0) queue<0, false>(ac, as, ats, bc, bs, bts, M, N, K, ep, s);
+    else if (ep.r == 16) queue<16, false>(ac, as, ats, bc, bs, bts, M, N, K, ep, s);
+    else queue<32, false>(ac, as, ats, bc, bs, bts, M, N, K, ep, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,128 @@
+// Device-side building blocks shared by the q4lin kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (wave64, verified on the device):
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands: lane l supplies row l%32
+//    of its operand and the 32 consecutive K elements of group l/32 (16 bytes, low
+//    nibble first, in the first four dwords of the 8-dword operand), plus one E8M0
+//    scale byte for those 32 elements, picked out of a dword by the op_sel index.
+//  * v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 and K elements
+//    8*(l/32) .. 8*(l/32)+7.
+//  * Both write the 32x32 fp32 result so that lane l holds column l%32 and, in
+//    register v (0..15), row 8*(v/4) + 4*(l/32) + v%4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFmtFP4 = 4;   // f8f6f4 MFMA operand format code for E2M1
+
+// 2**E as an fp32 value for E in [-127, 127] (2**-127 is an fp32 subnormal).
+__device__ __forceinline__ float exp2i(int E) {
+  uint32_t bits = (E >= -126) ? (uint32_t)(E + 127) << 23 : 0x00400000u;
+  return __uint_as_float(bits);
+}
+
+// floor(log2 v) of a positive bf16 magnitude given as its 15-bit pattern.
+// Normal: exponent field - 127; subnormal m * 2**-133: floor(log2 m) - 133.
+__device__ __forceinline__ int bf16_floor_log2(uint32_t mag) {
+  uint32_t e = mag >> 7;
+  if (e != 0) return (int)e - 127;
+  return (31 - __builtin_clz(mag & 0x7Fu)) - 133;
+}
+
+// Largest 15-bit magnitude pattern among the 2*n bf16 values packed in w[0..n).
+// For non-negative bf16 patterns the integer order is the value order.
+template <int N>
+__device__ __forceinline__ uint32_t bf16_amax_bits(const uint32_t* w) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    lo = max(lo, w[i] & 0x7FFFu);
+    hi = max(hi, (w[i] >> 16) & 0x7FFFu);
+  }
+  return max(lo, hi);
+}
+
+// MXFP4 shared exponent of a block (OCP MX: floor(log2 amax) - 2, clamped).
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  int E = bf16_floor_log2(amax_bits) - 2;
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// Encode 8 bf16 values (4 dwords) to one dword of E2M1 codes, dividing by the
+// power of two `scale` with the hardware converter (round to nearest even,
+// saturating at 6, sign kept).
+__device__ __forceinline__ uint32_t fp4_encode8_pow2(const uint32_t* w, float scale) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[0]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[1]), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[2]), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[3]), scale, 3);
+  return r;
+}
+
+// bf16 pattern -> fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The FP4 scaled MFMA: four dwords of E2M1 codes per operand.
+template <int OPSEL_A, int OPSEL_B>
+__device__ __forceinline__ v16f mfma_fp4_32x32x64(u32x4 a, u32x4 b, v16f c, int sa, int sb) {
+  v8i A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  v8i B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, kFmtFP4, kFmtFP4, OPSEL_A, sa,
+                                                          OPSEL_B, sb);
+}
+
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(u32x4 a, u32x4 b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// Row index (within the 32x32 MFMA result) of accumulator register v of lane l.
+__device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace q4
+
+namespace q4 {
+
+// Workgroup -> output tile.  Workgroups are dispatched round-robin over the 8
+// XCDs (each with its own L2), so consecutive tiles are first handed to one XCD
+// as a contiguous range, then laid out in groups of `group_m` tile rows so the
+// tiles an XCD runs together share operand panels in its L2.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int group_m, int* tm,
+                                        int* tn) {
+  const int ntiles = tiles_m * tiles_n;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q = ntiles >> 3, rem = ntiles & 7;
+  const int lid = xcd * q + (xcd < rem ? xcd : rem) + local;
+  const int per_group = group_m * tiles_n;
+  const int grp = lid / per_group;
+  const int first_m = grp * group_m;
+  const int gm = min(group_m, tiles_m - first_m);
+  const int in = lid - grp * per_group;
+  *tm = first_m + in % gm;
+  *tn = in / gm;
+}
+
+}  // namespace q4

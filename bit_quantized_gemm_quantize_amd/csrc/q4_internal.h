@@ -1,0 +1,42 @@
+// Host-side launchers behind the C ABI (internal to libq4lin).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+// Activation quantizer (+ t = X L1 when r > 0).  fmt 0 = MXFP4, 1 = NVFP4.
+// NVFP4 queues: clear tensor_scale, tensor amax, encode, amax -> s_t.
+hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                               const uint16_t* l1t, int r, float* t, hipStream_t s);
+
+// Weight packer over a strided logical [K, N] bf16 matrix.  fmt 0/1/2.
+hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N, int64_t sk,
+                               int64_t sn, uint8_t* codes, void* scales, uint16_t* zeros,
+                               float* tensor_scale, hipStream_t s);
+
+struct EpilogueArgs {
+  const float* t;         // [M, r] fp32 or nullptr
+  const uint16_t* l2t;    // [N, r] bf16 or nullptr
+  int r;                  // 0, 16, 32
+  const uint16_t* bias;   // [N] bf16 or nullptr
+  void* y;
+  int64_t ldy;
+  int out_f32;            // 0: bf16, 1: fp32
+};
+
+hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
+                          const uint8_t* bs, int64_t M, int64_t N, int64_t K,
+                          const EpilogueArgs& ep, hipStream_t s);
+
+hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats,
+                          const uint8_t* bc, const uint8_t* bs, const float* bts, int64_t M,
+                          int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s);
+
+hipError_t launch_gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* wc,
+                             const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
+                             int64_t K, const EpilogueArgs& ep, hipStream_t s);
+
+}  // namespace q4

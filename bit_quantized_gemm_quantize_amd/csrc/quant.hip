@@ -1,0 +1,339 @@
+// Activation quantizer (MXFP4 / NVFP4) fused with the low-rank down-projection,
+// and the offline weight packers.
+//
+// Activation pass (one read of X):
+//   * a workgroup owns 32 rows and all of K; its 8 waves stride over K in pairs of
+//     32-element blocks, so a lane (row l%32, half l/32) owns one whole block per
+//     step: 64 contiguous bytes of X in, 16 bytes of codes and its scale out.
+//     The block maximum therefore needs no cross-lane exchange.
+//   * the same 64 bytes are the bf16 MFMA operand of t = X L1: the 32 block
+//     elements feed four 32x32x16 steps (K order permuted identically for X and L1,
+//     which a sum over K allows); L1^T rows are read 16 bytes at a time.
+//   * per-wave partial t tiles are summed through LDS in a fixed order, so t is
+//     deterministic.
+#include "q4_device.h"
+#include "q4_internal.h"
+
+namespace q4 {
+
+constexpr int kQWaves = 8;
+constexpr int kQRows = 32;
+constexpr float kNvTensorDiv = 2688.0f;   // 6 (largest E2M1) * 448 (largest E4M3)
+
+// ---------------------------------------------------------------------------- NVFP4 helpers
+// E4M3FN code of a non-negative fp32 value, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  v = fminf(v, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFu;
+}
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+__device__ __forceinline__ float nv_tensor_scale(float amax_t) {
+  return amax_t > 0.0f ? amax_t / kNvTensorDiv : 1.0f;
+}
+
+// x / den in fp32 (IEEE division, round to nearest even) for the two bf16 values of
+// a dword, then E2M1 codes into byte SEL of r.  den = s_b * s_t, or 0 when the
+// block scale is 0: every code is then a signed zero.
+template <int SEL>
+__device__ __forceinline__ uint32_t nv_encode_pair(uint32_t r, uint32_t pair, float den) {
+  const float x0 = bf16_lo(pair), x1 = bf16_hi(pair);
+  const float v0 = den > 0.0f ? x0 / den : __builtin_copysignf(0.0f, x0);
+  const float v1 = den > 0.0f ? x1 / den : __builtin_copysignf(0.0f, x1);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v0, v1, 1.0f, SEL);
+}
+
+// Encode 16 bf16 values (8 dwords) of one NVFP4 block.
+__device__ __forceinline__ void nv_encode16(const uint32_t* w, float den, uint32_t* out2) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t r = 0;
+    r = nv_encode_pair<0>(r, w[4 * d + 0], den);
+    r = nv_encode_pair<1>(r, w[4 * d + 1], den);
+    r = nv_encode_pair<2>(r, w[4 * d + 2], den);
+    r = nv_encode_pair<3>(r, w[4 * d + 3], den);
+    out2[d] = r;
+  }
+}
+
+// One NVFP4 pair of blocks (32 values): two scale bytes and 16 bytes of codes.
+__device__ __forceinline__ uint32_t nv_encode32(const uint32_t* w, float s_t, float d6, u32x4* codes) {
+  uint32_t sc = 0;
+  uint32_t c[4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float amax = __uint_as_float(bf16_amax_bits<8>(w + 8 * b) << 16);
+    uint32_t code = e4m3_code(amax / d6);
+    float den = e4m3_value(code) * s_t;
+    nv_encode16(w + 8 * b, den, c + 2 * b);
+    sc |= code << (8 * b);
+  }
+  *codes = u32x4{c[0], c[1], c[2], c[3]};
+  return sc;
+}
+
+// ---------------------------------------------------------------------------- activation pass
+template <int FMT, int R>
+__global__ __launch_bounds__(512) void quant_act_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, const float* __restrict__ amax_t, const uint16_t* __restrict__ l1t,
+    float* __restrict__ t) {
+  __shared__ float red[R > 0 ? kQWaves * 32 * 32 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * kQRows;
+  const int64_t row = m0 + i;
+  const bool row_ok = row < M;
+  const int64_t nblk = K >> 5;
+  const int64_t npair = (nblk + 1) >> 1;
+  const int64_t sbytes = FMT == 0 ? nblk : 2 * nblk;   // scale bytes per row
+
+  float s_t = 1.0f, d6 = 6.0f;
+  if (FMT == 1) {
+    s_t = nv_tensor_scale(*amax_t);
+    d6 = 6.0f * s_t;
+  }
+  v16f acc = {};
+
+  for (int64_t p = wave; p < npair; p += kQWaves) {
+    const int64_t blk = 2 * p + h;
+    const bool blk_ok = blk < nblk;
+    uint32_t w[16];
+    if (row_ok && blk_ok) {
+      const uint16_t* src = x + row * ldx + blk * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 v = ld16(src + 8 * q);
+        w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+      }
+      u32x4 c;
+      if (FMT == 0) {
+        const int E = mx_block_exponent(bf16_amax_bits<16>(w));
+        const float sc = exp2i(E);
+        c = u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
+                  fp4_encode8_pow2(w + 8, sc), fp4_encode8_pow2(w + 12, sc)};
+        scales[row * sbytes + blk] = (uint8_t)(E + 127);
+      } else {
+        const uint32_t sc = nv_encode32(w, s_t, d6, &c);
+        *reinterpret_cast<uint16_t*>(scales + row * sbytes + 2 * blk) = (uint16_t)sc;
+      }
+      st16(codes + row * (K >> 1) + blk * 16, c);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) w[q] = 0;
+    }
+    if (R > 0) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 a = u32x4{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]};
+        u32x4 b = u32x4{0, 0, 0, 0};
+        if (i < R && blk_ok) b = ld16(l1t + (int64_t)i * K + blk * 32 + 8 * s);
+        acc = mfma_bf16_32x32x16(a, b, acc);
+      }
+    }
+  }
+
+  if (R > 0) {
+    // acc: rows = x rows (8*(v/4) + 4*h + v%4), column = t column (lane % 32)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave * 1024 + acc_row(v, lane) * 32 + i] = acc[v];
+    __syncthreads();
+    constexpr int kR = R > 0 ? R : 1;
+    for (int idx = threadIdx.x; idx < 32 * R; idx += 512) {
+      const int rr = idx / kR, cc = idx % kR;
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kQWaves; ++wv) sum += red[wv * 1024 + rr * 32 + cc];
+      if (m0 + rr < M) t[(m0 + rr) * R + cc] = sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- tensor amax
+__global__ void clear_f32_kernel(float* p) { *p = 0.0f; }
+
+__global__ void nv_finalize_kernel(float* p) { *p = nv_tensor_scale(*p); }
+
+// Largest |x| over a strided [rows, cols] bf16 matrix (element (r, c) at
+// x[r * sr + c * sc]); accumulated with an integer atomic max on the fp32 bit
+// pattern (valid for non-negative values).
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t sr, int64_t sc,
+                                                   float* amax) {
+  uint32_t m = 0;
+  const int64_t total = rows * cols;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (sc == 1 && (cols & 7) == 0 && (sr & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    const int64_t per_row = cols >> 3;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < rows * per_row; q += stride) {
+      const int64_t r = q / per_row, c = q % per_row;
+      u32x4 v = ld16(x + r * sr + c * 8);
+      m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v)));
+    }
+  } else {
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
+      const int64_t r = q / cols, c = q % cols;
+      m = max(m, (uint32_t)(x[r * sr + c * sc] & 0x7FFFu));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(reinterpret_cast<unsigned int*>(amax), m << 16);
+}
+
+static hipError_t queue_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t sr,
+                                    int64_t sc, float* amax, hipStream_t s) {
+  hipLaunchKernelGGL(clear_f32_kernel, dim3(1), dim3(1), 0, s, amax);
+  const int64_t work = (rows * cols + 7) / 8;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, sr, sc, amax);
+  return hipGetLastError();
+}
+
+template <int FMT, int R>
+static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                        uint8_t* scales, const float* amax, const uint16_t* l1t, float* t,
+                        hipStream_t s) {
+  const unsigned grid = (unsigned)((M + kQRows - 1) / kQRows);
+  hipLaunchKernelGGL((quant_act_kernel<FMT, R>), dim3(grid), dim3(512), 0, s, x, M, K, ldx, codes,
+                     scales, amax, l1t, t);
+}
+
+hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                               const uint16_t* l1t, int r, float* t, hipStream_t s) {
+  if (fmt == 1) {
+    hipError_t e = queue_tensor_amax(x, M, K, ldx, 1, tensor_scale, s);
+    if (e != hipSuccess) return e;
+  }
+  if (fmt == 0) {
+    if (r == 0) queue_quant<0, 0>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
+    else if (r == 16) queue_quant<0, 16>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
+    else queue_quant<0, 32>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
+  } else {
+    if (r == 0) queue_quant<1, 0>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
+    else if (r == 16) queue_quant<1, 16>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
+    else queue_quant<1, 32>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(nv_finalize_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- weight packers
+// One thread per (output column n, K group); consecutive threads take consecutive
+// n, so a [K, N] row-major weight is read coalesced and a [N, K] one row-wise.
+__device__ __forceinline__ void load_strided(const uint16_t* w, int64_t k0, int64_t n, int64_t sk,
+                                             int64_t sn, int count, uint32_t* out) {
+  for (int j = 0; j < count; j += 2) {
+    uint32_t lo = w[(k0 + j) * sk + n * sn];
+    uint32_t hi = w[(k0 + j + 1) * sk + n * sn];
+    out[j >> 1] = lo | (hi << 16);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restrict__ w, int64_t K,
+                                                       int64_t N, int64_t sk, int64_t sn,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ amax_t) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nblk = K >> 5;
+  if (q >= N * nblk) return;
+  const int64_t n = q % N, blk = q / N;
+  uint32_t v[16];
+  load_strided(w, blk * 32, n, sk, sn, 32, v);
+  u32x4 c;
+  if (FMT == 0) {
+    const int E = mx_block_exponent(bf16_amax_bits<16>(v));
+    const float sc = exp2i(E);
+    c = u32x4{fp4_encode8_pow2(v, sc), fp4_encode8_pow2(v + 4, sc), fp4_encode8_pow2(v + 8, sc),
+              fp4_encode8_pow2(v + 12, sc)};
+    scales[n * nblk + blk] = (uint8_t)(E + 127);
+  } else {
+    const float s_t = nv_tensor_scale(*amax_t);
+    const uint32_t sc = nv_encode32(v, s_t, 6.0f * s_t, &c);
+    scales[n * 2 * nblk + 2 * blk] = (uint8_t)(sc & 0xFF);
+    scales[n * 2 * nblk + 2 * blk + 1] = (uint8_t)(sc >> 8);
+  }
+  st16(codes + n * (K >> 1) + blk * 16, c);
+}
+
+// Asymmetric int4, group 64: s = bf16(fp32(hi - lo) / 15) (1 if 0),
+// z = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).
+__global__ __launch_bounds__(256) void pack_int4_kernel(const uint16_t* __restrict__ w, int64_t K,
+                                                        int64_t N, int64_t sk, int64_t sn,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint16_t* __restrict__ scales,
+                                                        uint16_t* __restrict__ zeros) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t ngrp = K >> 6;
+  if (q >= N * ngrp) return;
+  const int64_t n = q % N, g = q / N;
+  uint32_t v[32];
+  load_strided(w, g * 64, n, sk, sn, 64, v);
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float a = bf16_lo(v[j]), b = bf16_hi(v[j]);
+    lo = fminf(lo, fminf(a, b));
+    hi = fmaxf(hi, fmaxf(a, b));
+  }
+  const uint32_t sbits = f32_to_bf16_rne((hi - lo) / 15.0f);
+  float s = __uint_as_float(sbits << 16);
+  uint32_t sstore = sbits;
+  if (s == 0.0f) { s = 1.0f; sstore = 0x3F80u; }
+  const float z = fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f);
+  uint32_t out[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pair = v[4 * d + j];
+      const float q0 = fminf(fmaxf(rintf(bf16_lo(pair) / s) + z, 0.0f), 15.0f);
+      const float q1 = fminf(fmaxf(rintf(bf16_hi(pair) / s) + z, 0.0f), 15.0f);
+      r |= ((uint32_t)q0 | ((uint32_t)q1 << 4)) << (8 * j);
+    }
+    out[d] = r;
+  }
+  uint8_t* dst = codes + n * (K >> 1) + g * 32;
+  st16(dst, u32x4{out[0], out[1], out[2], out[3]});
+  st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
+  scales[n * ngrp + g] = (uint16_t)sstore;
+  zeros[n * ngrp + g] = (uint16_t)f32_to_bf16_rne(z + 0.0f);   // never -0
+}
+
+hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N, int64_t sk,
+                               int64_t sn, uint8_t* codes, void* scales, uint16_t* zeros,
+                               float* tensor_scale, hipStream_t s) {
+  if (fmt == 2) {
+    const int64_t work = N * (K >> 6);
+    hipLaunchKernelGGL(pack_int4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, w, K,
+                       N, sk, sn, codes, static_cast<uint16_t*>(scales), zeros);
+    return hipGetLastError();
+  }
+  const int64_t work = N * (K >> 5);
+  const unsigned grid = (unsigned)((work + 255) / 256);
+  if (fmt == 0) {
+    hipLaunchKernelGGL(pack_fp4_kernel<0>, dim3(grid), dim3(256), 0, s, w, K, N, sk, sn, codes,
+                       static_cast<uint8_t*>(scales), nullptr);
+    return hipGetLastError();
+  }
+  // logical [K, N]: rows k (stride sk), columns n (stride sn)
+  hipError_t e = queue_tensor_amax(w, K, N, sk, sn, tensor_scale, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_fp4_kernel<1>, dim3(grid), dim3(256), 0, s, w, K, N, sk, sn, codes,
+                     static_cast<uint8_t*>(scales), tensor_scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nv_finalize_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,202 @@
+/*
+ * q4lin -- the 4-bit quantized linear layer of a diffusion transformer, for one
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The layer (SVDQuant Guide, aifetchly: "The Three Pillars of SVDQuant",
+ * 1. Mathematical Outlier Factorization, forward-projection equation, and
+ * "Step 2: The SVDQuant Dual-Branch Linear Layer") is
+ *
+ *     Y = deq(Q(X)) deq(Q(W))^T  +  (X L1) L2  +  bias
+ *
+ * with X [M, K] the activations (tokens x in-features, bf16), W^T [N, K] the
+ * weight (out-features x in-features), Q a 4-bit block quantizer along K, and the
+ * optional rank-r low-rank branch applied to the unquantized X, evaluated right to
+ * left (down-projection L1 [K, r] first, then up-projection L2 [r, N]).  Y [M, N].
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer on the current HIP device, owned
+ *     by the caller.  The library never allocates and keeps no state.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - 4-bit codes are packed two per byte along K: element 2j in the low nibble,
+ *     element 2j+1 in the high nibble; a row of K elements is K/2 bytes.  FP4 codes
+ *     are E2M1 (sign in bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   - Matrices are row-major.  Packed codes and scales are dense (row stride
+ *     K/2 bytes, K/32 or K/16 bytes, K/64 elements).
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Work is queued on it
+ *     and the call returns without synchronizing.
+ *   - Arguments are checked on the host before anything is queued; a failed check
+ *     returns its status and queues nothing.  Q4_ERR_LAUNCH reports a launch the
+ *     HIP runtime refused.  Device-side faults are not reported here.
+ *   - Inputs must be finite; results for NaN or infinite inputs are unspecified.
+ *   - M = 0 or N = 0 is an empty problem: Q4_OK, nothing queued.
+ *   - Calls are thread-safe; calls that write the same buffers must be ordered by
+ *     the caller.
+ */
+#ifndef Q4LIN_H
+#define Q4LIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define Q4_API __attribute__((visibility("default")))
+#else
+#define Q4_API
+#endif
+
+typedef enum q4_status {
+  Q4_OK = 0,
+  Q4_ERR_NULL = 1,    /* a required pointer is NULL                                  */
+  Q4_ERR_SHAPE = 2,   /* negative size, K not a multiple of the block, bad rank/stride */
+  Q4_ERR_ALIGN = 3,   /* a pointer or leading dimension breaks the stated alignment   */
+  Q4_ERR_FORMAT = 4,  /* format not valid for this call                              */
+  Q4_ERR_LAUNCH = 5   /* the HIP runtime rejected a kernel launch                    */
+} q4_status;
+
+typedef enum q4_format {
+  /* MXFP4: E2M1 elements, one E8M0 scale byte (2**(byte-127)) per 32 consecutive K
+   * elements; OCP Microscaling Formats v1.0 conversion (shared exponent
+   * floor(log2 amax) - 2, clamped to [-127, 127]; elements rounded to nearest
+   * even, saturating at 6).  The pages name FP4 E2M1 in "Quantization for the
+   * impatient" (bitsandbytes backend). */
+  Q4_MXFP4 = 0,
+  /* NVFP4-style: E2M1 elements, one FP8 E4M3 scale byte per 16 consecutive K
+   * elements and one fp32 per-tensor scale s_t = amax/2688 (2688 = 6 * 448, 448
+   * being the E4M3 limit the stability table of "Quantization for the impatient"
+   * gives).  Block scale s_b = E4M3_RNE_SAT(amax_b / (6 s_t)), element
+   * E2M1_RNE_SAT(x / (s_b s_t)), every step in fp32.  NVFP4 is named in the NVIDIA
+   * Technical Blog summary (first optimization layer). */
+  Q4_NVFP4 = 1,
+  /* Weight-only asymmetric uint4 with a bf16 scale s and a bf16 (integer) zero
+   * point z per 64 consecutive K elements: s = bf16(fp32(hi - lo)/15) over the
+   * group range [lo, hi] widened to hold 0, z = clamp(RNE(-lo/s), 0, 15),
+   * q = clamp(RNE(w/s) + z, 0, 15); the GEMM operand is bf16((q - z) s).  The
+   * weight-only (W4A16) path the SVDQuant Guide contrasts with W4A4 in
+   * "Why Standard Low-Bit Quantization Fails on DiTs". */
+  Q4_INT4_G64 = 2
+} q4_format;
+
+typedef enum q4_out {
+  Q4_OUT_BF16 = 0,   /* y is bf16, rounded to nearest even from the fp32 result */
+  Q4_OUT_F32 = 1     /* y is fp32                                               */
+} q4_out;
+
+/*
+ * quantize_act -- dynamic activation quantization, run on every call (outliers move
+ * with the timestep: SVDQuant Guide, "Why Standard Low-Bit Quantization Fails on
+ * DiTs"), fused with the low-rank down-projection t = X L1 of the same pass over X
+ * (SVDQuant Guide, "3. The Nunchaku Fused Kernel Engine": one pass, no second read).
+ *
+ *   fmt           Q4_MXFP4 or Q4_NVFP4 (else Q4_ERR_FORMAT).
+ *   x             bf16 [M, K], row stride ldx elements.  16-byte aligned, ldx a
+ *                 multiple of 8, ldx >= K.
+ *   M, K          M >= 0; K >= 0 and a multiple of 32.
+ *   codes  (out)  uint8 [M, K/2].  16-byte aligned.
+ *   scales (out)  MXFP4: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16].
+ *   tensor_scale  NVFP4: float[1], written with s_t (also used as the amax
+ *                 accumulator while the call runs).  MXFP4: ignored, may be NULL.
+ *   l1t           r > 0: bf16 L1^T [r, K] (the down-projection stored
+ *                 in-features-contiguous, nn.Linear layout), 16-byte aligned.
+ *                 r = 0: ignored.
+ *   r             rank of the low-rank branch: 0, 16 or 32.
+ *   t      (out)  r > 0: fp32 [M, r], 16-byte aligned, t = X L1 accumulated in fp32.
+ */
+Q4_API q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                       uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                       const uint16_t* l1t, int32_t r, float* t, void* stream);
+
+/*
+ * pack_weights -- offline weight quantization and packing, once per model (the
+ * SVDQuant Guide's "Step 1: Low-Rank Outlier Decomposition in PyTorch" quantizes
+ * the residual weight once; "Quantization for the impatient" packs 4-bit weights
+ * several to a word).  The same encoders as quantize_act, along K for every output
+ * column n.
+ *
+ *   fmt               Q4_MXFP4, Q4_NVFP4 or Q4_INT4_G64.
+ *   w                 bf16, logical [K, N]: element (k, n) at w[k*stride_k + n*stride_n]
+ *                     (stride_k = 1, stride_n = K for nn.Linear's [out, in] storage;
+ *                     stride_k = N, stride_n = 1 for row-major [K, N]).  Strides >= 1.
+ *   K, N              K a multiple of 32 (MXFP4, NVFP4) or 64 (INT4_G64).
+ *   codes  (out)      uint8 [N, K/2].
+ *   scales (out)      MXFP4: uint8 [N, K/32]; NVFP4: uint8 E4M3 [N, K/16];
+ *                     INT4_G64: bf16 [N, K/64].
+ *   zeros  (out)      INT4_G64: bf16 [N, K/64] (integers 0..15); else ignored.
+ *   tensor_scale(out) NVFP4: float[1] (s_t of the weight); else ignored.
+ */
+Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N,
+                       int64_t stride_k, int64_t stride_n, uint8_t* codes, void* scales,
+                       uint16_t* zeros, float* tensor_scale, void* stream);
+
+/*
+ * gemm_w4a4 -- Y = deq(A) deq(B)^T (+ bias), the 4-bit x 4-bit GEMM of the forward
+ * equation (SVDQuant Guide, "1. Mathematical Outlier Factorization"; the 4-bit
+ * branch carries about 95% of the compute per the decomposition figure).
+ *
+ *   fmt       Q4_MXFP4: block-scaled FP4 MFMA.  Q4_NVFP4: exact dequantization
+ *             to bf16 (every E2M1 x E4M3 product fits bf16) and bf16 MFMA; the two
+ *             tensor scales multiply the fp32 result.
+ *   a_*       activation codes [M, K/2] and scales (layout as quantize_act);
+ *             a_tscale: NVFP4 float[1], else ignored.
+ *   b_*       weight codes [N, K/2] and scales (layout as pack_weights).
+ *   K         a multiple of 128.
+ *   bias      bf16 [N] or NULL.
+ *   y   (out) [M, N] with row stride ldy >= N elements; bf16 or fp32 per `out`.
+ *             16-byte aligned, ldy a multiple of 8.
+ * Accumulation is fp32; |Y - Y_exact| stays within 1e-3 of the sum of the
+ * magnitudes of the products that form each element (plus the bf16 store
+ * rounding for Q4_OUT_BF16).
+ */
+Q4_API q4_status gemm_w4a4(q4_format fmt,
+                    const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
+                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
+                    int64_t M, int64_t N, int64_t K, const uint16_t* bias,
+                    void* y, int64_t ldy, q4_out out, void* stream);
+
+/*
+ * gemm_w4a4_lowrank -- gemm_w4a4 plus the low-rank up-projection t L2 fused into
+ * the epilogue (SVDQuant Guide, "3. The Nunchaku Fused Kernel Engine": the 4-bit
+ * GEMM and the 16-bit low-rank GEMM in one kernel).  t comes from quantize_act.
+ *
+ *   t     fp32 [M, r], 16-byte aligned.  It enters the bf16 MFMA as a pair of
+ *         bf16 values (t = hi + lo), which keeps 16 significant bits.
+ *   l2t   bf16 L2^T [N, r] (the up-projection stored rank-contiguous, nn.Linear
+ *         layout), 16-byte aligned.
+ *   r     16 or 32 (r = 0 is gemm_w4a4).
+ * Other arguments as gemm_w4a4.
+ */
+Q4_API q4_status gemm_w4a4_lowrank(q4_format fmt,
+                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tscale,
+                            const uint8_t* b_codes, const uint8_t* b_scales, const float* b_tscale,
+                            int64_t M, int64_t N, int64_t K,
+                            const float* t, const uint16_t* l2t, int32_t r,
+                            const uint16_t* bias, void* y, int64_t ldy, q4_out out, void* stream);
+
+/*
+ * gemm_w4a16 -- the weight-only comparison path: Y = X w_hat^T (+ bias) with
+ * w_hat = bf16((q - z) s) dequantized tile by tile in LDS and a bf16 MFMA GEMM
+ * (SVDQuant Guide, "Why Standard Low-Bit Quantization Fails on DiTs", third point,
+ * and the dilemma figure: weights unpacked before every multiplication;
+ * "Quantization for the impatient", "Why fewer bits != faster").
+ *
+ *   x         bf16 [M, K], row stride ldx (multiple of 8), 16-byte aligned.
+ *   w_codes   uint8 [N, K/2]; w_scales, w_zeros bf16 [N, K/group] from pack_weights.
+ *   group     64.
+ *   K         a multiple of 64.
+ * Other arguments as gemm_w4a4.
+ */
+Q4_API q4_status gemm_w4a16(const uint16_t* x, int64_t ldx,
+                     const uint8_t* w_codes, const uint16_t* w_scales, const uint16_t* w_zeros,
+                     int64_t M, int64_t N, int64_t K, int32_t group,
+                     const uint16_t* bias, void* y, int64_t ldy, q4_out out, void* stream);
+
+/* Static, NUL-terminated name of a status ("Q4_OK", ...); "unknown" otherwise. */
+Q4_API const char* q4_status_string(q4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4LIN_H */

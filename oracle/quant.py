@@ -71,21 +71,25 @@ def mx_dequantize(codes, scales):
 
 
 # ----------------------------------------------------------------------------- NVFP4
-def nv_tensor_scale(bits):
+def nv_tensor_scale(bits, amax_t=None):
     """Per-tensor fp32 scale s_t = fp32(amax_t / 2688), or 1 for an all-zero tensor.
 
     2688 = 6 * 448 maps the tensor's largest magnitude onto the largest E2M1 value
-    times the largest E4M3 scale, so every block scale fits E4M3.
+    times the largest E4M3 scale, so every block scale fits E4M3.  amax_t, when
+    given, is the largest magnitude of the whole tensor that ``bits`` is a slice
+    of (so a subset of rows can be quantized as part of the full tensor).
     """
-    x = bf16_to_f32(bits)
-    check_finite(x, "activation/weight")
-    amax_t = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    if amax_t is None:
+        x = bf16_to_f32(bits)
+        check_finite(x, "activation/weight")
+        amax_t = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    amax_t = np.float32(amax_t)
     if amax_t == 0:
         return np.float32(1.0)
     return np.float32(amax_t / NV_TENSOR_DIVISOR)                    # fp32 division
 
 
-def nv_quantize(bits):
+def nv_quantize(bits, amax_t=None):
     """NVFP4-style: E2M1 elements, one E4M3 scale per 16 K elements, one fp32
     tensor scale, every step in fp32 with round to nearest even:
 
@@ -93,11 +97,14 @@ def nv_quantize(bits):
         s_b  = E4M3_RNE_SAT(fp32(amax_b / fp32(6 * s_t)))
         code = E2M1_RNE_SAT(fp32(x / fp32(s_b * s_t)))   if s_b != 0, else signed 0
 
+    amax_t: the whole tensor's largest magnitude when ``bits`` holds only some of
+    its rows (see ``nv_tensor_scale``).
+
     Returns (codes uint8 [rows, K/2], scales uint8 E4M3 [rows, K/16], s_t float32).
     """
     bits = _rows(bits, NV_BLOCK)
     rows, K = bits.shape
-    s_t = nv_tensor_scale(bits)
+    s_t = nv_tensor_scale(bits, amax_t)
     x = bf16_to_f32(bits).reshape(rows, K // NV_BLOCK, NV_BLOCK)
     amax_b = np.abs(x).max(axis=-1)                                   # float32, exact
     ratio = amax_b / (np.float32(6.0) * s_t)                          # fp32 mul, fp32 div
