@@ -13,11 +13,12 @@
 // 4-byte scale word (the op_sel index), one aligned dword load per fragment.
 //
 // LDS: the two operand tiles (256 rows x 128 bytes each) are stored with 16-byte
-// chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)), so both the
-// row-contiguous global->LDS writes and the 16-byte fragment reads are free of
-// bank conflicts.  The next K-tile is fetched from global into registers while
-// the current one is multiplied: two LDS stages, one barrier per K-tile, and the
-// global loads for tile kt+2 in flight while tile kt is multiplied.
+// chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)), so the 16-byte
+// fragment reads are free of bank conflicts.  Tiles go from HBM/L2 straight into
+// LDS (buffer loads with the LDS destination, no staging registers; rows and
+// K blocks past the matrix read as zero).  Two LDS stages: tile kt+1 is in
+// flight while tile kt is multiplied, one barrier per K-tile, and the fragments
+// of the next MFMA step are read from LDS while the current step's MFMAs run.
 #include "q4_epilogue.h"
 
 namespace q4 {
@@ -34,8 +35,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int tiles_m, int tiles_n) {
-  // two stages x (activation tile, weight tile), 256 rows x 128 bytes each
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBM * kKTB];
+  // LDS: two stages x (activation tile, weight tile) of 256 rows x 128 bytes, then
+  // two stages x (activation, weight) of scale rows (256 rows x 16 bytes: the scale
+  // bytes of two consecutive K-tiles); the epilogue reuses the space for the output
+  constexpr int kCodeLds = 2 * 2 * kBM * kKTB;          // 131072
+  constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
+  constexpr int kMainLds = kCodeLds + kScaleLds;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds > kEpilogueLdsBytes ? kMainLds : kEpilogueLdsBytes];
+  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
+  auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
 
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, kGroupM, &tm, &tn);
@@ -43,41 +51,68 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;       // wave's n half, m half
   const int r32 = lane & 31, h = lane >> 5;
-  const int64_t kbytes = K >> 1, nblk = K >> 5;
+  const uint32_t kbytes = (uint32_t)(K >> 1), nblk = (uint32_t)(K >> 5);
   const int nkt = (int)((K + kKT - 1) / kKT);
+  const uint32_t rows_a = (uint32_t)min<int64_t>(kBM, M - m0), rows_b = (uint32_t)min<int64_t>(kBN, N - n0);
 
-  // global -> LDS mapping: 16-byte chunk (row, c) with c = tid & 7, rows tid/8 + 32 j
-  const int lrow = tid >> 3, lc = tid & 7;
-  u32x4 ra[8], rb[8];
-  uint32_t sa_next[4], sb_next[4];
-  auto gload = [&](int kt) {
-    const int64_t blk = (int64_t)kt * 8 + lc;
+  // buffer views of this tile's rows: rows past M / N read as zero
+  const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
+  const auto rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
+  const auto rs_a = make_rsrc(as + m0 * nblk, rows_a * nblk);
+  const auto rs_b = make_rsrc(bs + n0 * nblk, rows_b * nblk);
+
+  // codes, global -> LDS: each wave moves 8 rows x 128 bytes per instruction straight
+  // into LDS (lane i -> row i/8, stored position i%8, which holds global chunk
+  // (i%8) ^ (row & 7), the swizzle).  Wave w covers rows 64 w .. 64 w + 63.
+  const int lr = lane >> 3, lp = lane & 7;
+  auto gload = [&](int kt, int stage, int operand) {
+    const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
+    const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
+    const auto rc = operand == 0 ? rc_a : rc_b;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int row = lrow + 32 * j;
-      ra[j] = (m0 + row < M && blk < nblk) ? ld16(ac + (m0 + row) * kbytes + blk * 16) : u32x4{0, 0, 0, 0};
-      rb[j] = (n0 + row < N && blk < nblk) ? ld16(bc + (n0 + row) * kbytes + blk * 16) : u32x4{0, 0, 0, 0};
+      const uint32_t row = 64 * wave + 8 * j + lr;
+      // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
+      buf_ld16_lds(rc, &lds[stage][operand][(64 * wave + 8 * j) * kKTB], row * kbytes + koff);
     }
-    // scale words: bytes for blocks 8kt + 4h .. 8kt + 4h + 3 of the lane's fragment rows
-    const int64_t blk0 = (int64_t)kt * 8 + 4 * h;
+  };
+  // scales, global -> LDS: lane i of wave w takes row 64 w + i, 16 bytes = the scale
+  // bytes of K-tiles kt and kt+1 (the second half is unused when kt+1 is past K)
+  auto sload = [&](int kt, int stage) {
+    const uint32_t b0 = (uint32_t)kt * 8;
+    const uint32_t koff = b0 < nblk ? b0 : kOOB;
+    const uint32_t off = (64 * wave + lane) * nblk + koff;
+    buf_ld16_lds(rs_a, &lsc[stage][0][64 * wave * 16], off);
+    buf_ld16_lds(rs_b, &lsc[stage][1][64 * wave * 16], off);
+  };
+  // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3
+  uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
+  auto read_scales = [&](int kt, int stage, uint32_t* xa, uint32_t* xb) {
+    const bool kin = (uint32_t)kt * 8 + 4 * h < nblk;      // past K: codes are 0; keep 2**0
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int64_t m = m0 + wx * 128 + 32 * g + r32;
-      sa_next[g] = (m < M && blk0 < nblk) ? *reinterpret_cast<const uint32_t*>(as + m * nblk + blk0) : 0x7F7F7F7Fu;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wx * 128 + 32 * g + r32) * 16 + 4 * h]);
+      xa[g] = kin ? v : 0x7F7F7F7Fu;
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const int64_t n = n0 + wy * 128 + 32 * f + r32;
-      sb_next[f] = (n < N && blk0 < nblk) ? *reinterpret_cast<const uint32_t*>(bs + n * nblk + blk0) : 0x7F7F7F7Fu;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wy * 128 + 32 * f + r32) * 16 + 4 * h]);
+      xb[f] = kin ? v : 0x7F7F7F7Fu;
     }
   };
-  auto lstore = [&](int stage) {
+
+  // fragment registers, double-buffered across MFMA steps
+  u32x4 fa[2][4], fb[2][4];
+  auto read_frags = [&](int buf, int stage, int s) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = lrow + 32 * j;
-      const int off = row * kKTB + ((lc ^ (row & 7)) << 4);
-      st16(&lds[stage][0][off], ra[j]);
-      st16(&lds[stage][1][off], rb[j]);
+    for (int g = 0; g < 4; ++g) {
+      const int row = wx * 128 + 32 * g + r32;
+      fa[buf][g] = ld16(&lds[stage][0][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int row = wy * 128 + 32 * f + r32;
+      fb[buf][f] = ld16(&lds[stage][1][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
   };
 
@@ -87,54 +122,76 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
-  uint32_t sa[4], sb[4];
+#define Q4_MX_MMA(S, BUF)                                                                       \
+  _Pragma("unroll") for (int f = 0; f < 4; ++f)                                                 \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g)                                               \
+      acc[f][g] = mfma_fp4_32x32x64<S, S>(fb[BUF][f], fa[BUF][g], acc[f][g], (int)sb[f],       \
+                                          (int)sa[g]);
+// within a region: the LDS reads for the next step go out first, then the MFMAs
+#define Q4_READS_THEN_MMA(NREADS)                          \
+  __builtin_amdgcn_sched_group_barrier(0x100, NREADS, 0); \
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+
   if (nkt > 0) {
-    gload(0);
-    lstore(0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) { sa[g] = sa_next[g]; sb[g] = sb_next[g]; }
-    if (nkt > 1) gload(1);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nkt) {
-      lstore(stage ^ 1);                 // tile kt+1 (its loads were issued one iteration ago)
-    }
-    uint32_t sa_cur[4], sb_cur[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) { sa_cur[g] = sa[g]; sb_cur[g] = sb[g]; sa[g] = sa_next[g]; sb[g] = sb_next[g]; }
-    if (kt + 2 < nkt) gload(kt + 2);
-    const uint8_t* la = lds[stage][0];
-    const uint8_t* lb = lds[stage][1];
-
-#define Q4_MX_STEP(S)                                                                  \
-  {                                                                                    \
-    u32x4 pa[4], pb[4];                                                                \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                    \
-      const int row = wx * 128 + 32 * g + r32;                                         \
-      pa[g] = ld16(la + row * kKTB + (((4 * h + (S)) ^ (row & 7)) << 4));              \
-    }                                                                                  \
-    _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                    \
-      const int row = wy * 128 + 32 * f + r32;                                         \
-      pb[f] = ld16(lb + row * kKTB + (((4 * h + (S)) ^ (row & 7)) << 4));              \
-    }                                                                                  \
-    _Pragma("unroll") for (int f = 0; f < 4; ++f)                                      \
-      _Pragma("unroll") for (int g = 0; g < 4; ++g)                                    \
-        acc[f][g] = mfma_fp4_32x32x64<S, S>(pb[f], pa[g], acc[f][g], (int)sb_cur[f], (int)sa_cur[g]); \
-  }
-    Q4_MX_STEP(0)
-    Q4_MX_STEP(1)
-    Q4_MX_STEP(2)
-    Q4_MX_STEP(3)
-#undef Q4_MX_STEP
+    gload(0, 0, 0);
+    gload(0, 0, 1);
+    sload(0, 0);
+    wait_vmem();
     __syncthreads();
+    read_frags(0, 0, 0);
+    read_scales(0, 0, sa, sb);
   }
+
+  // The loop body is one basic block (no branches), so the sched barriers pin the
+  // order: each MFMA step runs with the next step's fragment reads in flight, and
+  // the loads of tile kt+1 are slotted between the MFMAs of steps 0 and 1 (issuing
+  // them in a burst would hold the in-order MFMA stream behind them).  On the last
+  // tile the "next" loads fall past K and read zeros, harmlessly.
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int st = kt & 1;
+    read_frags(1, st, 1);
+    gload(kt + 1, st ^ 1, 0);
+    sload(kt + 1, st ^ 1);
+    Q4_MX_MMA(0, 0)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, st, 2);
+    gload(kt + 1, st ^ 1, 1);
+    Q4_MX_MMA(1, 1)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(1, st, 3);
+    Q4_MX_MMA(2, 0)
+    Q4_READS_THEN_MMA(8)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem();
+    // every wave's tile kt+1 has landed, and every read of tile kt has completed
+    __syncthreads();
+    read_frags(0, st ^ 1, 0);
+    read_scales(kt + 1, st ^ 1, sa_n, sb_n);
+    Q4_MX_MMA(3, 1)
+    Q4_READS_THEN_MMA(16)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) { sa[g] = sa_n[g]; sb[g] = sb_n[g]; }
+  }
+#undef Q4_MX_MMA
+#undef Q4_READS_THEN_MMA
 
   const int64_t n_base = n0 + wy * 128, m_base = m0 + wx * 128;
   if (R > 0) epilogue_lowrank<R>(acc, n_base, m_base, M, N, t, l2t, lane);
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane);
+  __syncthreads();                           // all waves are done reading operand tiles
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds_raw + wave * kStageWaveBytes);
 }
 
 template <int R, bool F32>

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ t, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kBf16BM * kBf16RowBytes];
+  constexpr int kMainLds = 4 * kBf16BM * kBf16RowBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainLds > kEpilogueLdsBytes ? kMainLds : kEpilogueLdsBytes];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,7 +95,8 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
     for (int g = 0; g < 4; ++g) acc[f][g] = acc[f][g] * scale;
   const int64_t n_base = ld.n0 + wy * 128, m_base = ld.m0 + wx * 128;
   if (R > 0) epilogue_lowrank<R>(acc, n_base, m_base, M, N, t, l2t, lane);
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane);
+  __syncthreads();                           // all waves are done reading operand tiles
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
 }
 
 template <int R, bool F32>

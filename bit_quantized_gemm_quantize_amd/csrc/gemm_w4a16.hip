@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kBf16BM * kBf16RowBytes];
+  constexpr int kMainLds = 4 * kBf16BM * kBf16RowBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainLds > kEpilogueLdsBytes ? kMainLds : kEpilogueLdsBytes];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -95,7 +96,8 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
   v16f acc[4][4];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
   const int64_t n_base = ld.n0 + wy * 128, m_base = ld.m0 + wx * 128;
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane);
+  __syncthreads();                           // all waves are done reading operand tiles
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
 }
 
 hipError_t launch_gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* wc,

@@ -126,3 +126,38 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
 }
 
 }  // namespace q4
+
+namespace q4 {
+
+// Raw buffer access: loads whose byte offset lies at or beyond `bytes` return 0,
+// so tile edges need no branches (an out-of-range chunk gets offset kOOB).
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+}  // namespace q4
+
+namespace q4 {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes land at
+// lds_wave_base + 16 i (the base is wave-uniform).  Out-of-range offsets write 0.
+__device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, (int)off, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including loads into
+// LDS) have completed: s_waitcnt vmcnt(0), other counters untouched.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+}  // namespace q4

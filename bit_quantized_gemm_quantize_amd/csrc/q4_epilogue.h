@@ -1,8 +1,7 @@
 // Epilogue shared by the GEMM kernels.  The main loop leaves a wave with a 4 x 4
 // grid of 32x32 fp32 accumulators laid out as D[n][m] (MFMA A operand = weight
 // rows n, B operand = activation rows m), so lane l holds output row m = l%32 of
-// each tile and, per register group v/4, four consecutive output columns n: the
-// stores are 8-byte (bf16) or 16-byte (fp32) runs along a row of Y.
+// each tile and, per register group v/4, four consecutive output columns n.
 //
 // Order of the epilogue: (optional) scale, low-rank up-projection t L2 as bf16
 // MFMAs on the same accumulators with t split into bf16 hi + lo, bias, store.
@@ -61,17 +60,27 @@ __device__ __forceinline__ void epilogue_lowrank(v16f (&acc)[4][4], int64_t n_ba
   }
 }
 
+// Output staging through LDS: each wave writes its 128 x 128 region (bf16: all of
+// it; fp32: half the columns per pass) into LDS rows of 272 bytes, then reads it
+// back so that every store instruction writes 4 full rows of 256 contiguous bytes.
+// Direct stores from the MFMA layout would write 16-byte pieces of 32 different
+// rows per instruction.
+constexpr int kStageRowBytes = 272;                         // 256 + 16 bytes of padding
+constexpr int kStageWaveBytes = 128 * kStageRowBytes;       // 34816
+constexpr int kEpilogueLdsBytes = 4 * kStageWaveBytes;      // 139264 for 4 waves
+
 template <bool OUT_F32>
 __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base, int64_t m_base,
                                                int64_t M, int64_t N,
                                                const uint16_t* __restrict__ bias, void* y,
-                                               int64_t ldy, int lane) {
+                                               int64_t ldy, int lane, uint8_t* stage) {
   const int r32 = lane & 31, h = lane >> 5;
+  // bias, per accumulator group of 4 consecutive columns
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int vq = 0; vq < 4; ++vq) {
-      const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;   // first of 4 consecutive columns
+      const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
       float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (bias) {
 #pragma unroll
@@ -79,37 +88,65 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base
           if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t m = m_base + 32 * g + r32;
-        if (m >= M) continue;
-        float v[4];
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[f][g][4 * vq + j] + b[j];
-        if (OUT_F32) {
-          float* dst = static_cast<float*>(y) + m * ldy + n;
-          if (n + 3 < N) {
-            *reinterpret_cast<v4f*>(dst) = v4f{v[0], v[1], v[2], v[3]};
+        for (int j = 0; j < 4; ++j) acc[f][g][4 * vq + j] += b[j];
+    }
+
+  constexpr int kPasses = OUT_F32 ? 2 : 1;       // fp32: 64 columns per pass
+  constexpr int kFPerPass = 4 / kPasses;
+  constexpr int kColsPerPass = 32 * kFPerPass;   // 128 (bf16) or 64 (fp32)
+  constexpr int kElem = OUT_F32 ? 4 : 2;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    // registers -> LDS: row m_local = 32 g + lane%32, columns 32 f' + 8 vq + 4 h .. +3
+#pragma unroll
+    for (int fp = 0; fp < kFPerPass; ++fp) {
+      const int f = pass * kFPerPass + fp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          uint8_t* dst = stage + (32 * g + r32) * kStageRowBytes + (32 * fp + 8 * vq + 4 * h) * kElem;
+          const v16f& a = acc[f][g];
+          if (OUT_F32) {
+            *reinterpret_cast<v4f*>(dst) = v4f{a[4 * vq], a[4 * vq + 1], a[4 * vq + 2], a[4 * vq + 3]};
           } else {
-            for (int j = 0; j < 4; ++j)
-              if (n + j < N) dst[j] = v[j];
-          }
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(y) + m * ldy + n;
-          const v2bf p0 = {(__bf16)v[0], (__bf16)v[1]};
-          const v2bf p1 = {(__bf16)v[2], (__bf16)v[3]};
-          if (n + 3 < N) {
+            const v2bf p0 = {(__bf16)a[4 * vq], (__bf16)a[4 * vq + 1]};
+            const v2bf p1 = {(__bf16)a[4 * vq + 2], (__bf16)a[4 * vq + 3]};
             typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
             *reinterpret_cast<u32x2*>(dst) =
                 u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-          } else {
-            const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
-            const uint16_t e[4] = {(uint16_t)(w0 & 0xFFFF), (uint16_t)(w0 >> 16), (uint16_t)(w1 & 0xFFFF),
-                                   (uint16_t)(w1 >> 16)};
-            for (int j = 0; j < 4; ++j)
-              if (n + j < N) dst[j] = e[j];
+          }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    // LDS -> global: 16 lanes per row (16 bytes each), 4 rows per instruction
+    const int col_bytes = (lane & 15) * 16;
+    const int64_t n = n_base + pass * kColsPerPass + col_bytes / kElem;
+    constexpr int kPer16 = 16 / kElem;          // elements per 16 bytes
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int ml = 4 * it + (lane >> 4);
+      const int64_t m = m_base + ml;
+      const u32x4 v = ld16(stage + ml * kStageRowBytes + col_bytes);
+      if (m < M) {
+        uint8_t* dst = static_cast<uint8_t*>(y) + (m * ldy + n) * kElem;
+        if (n + kPer16 <= N) {
+          st16(dst, v);
+        } else if (n < N) {
+          const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+          for (int j = 0; j < kPer16 && n + j < N; ++j) {
+            if (OUT_F32) reinterpret_cast<uint32_t*>(dst)[j] = w[j];
+            else reinterpret_cast<uint16_t*>(dst)[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
           }
         }
       }
+    }
+    if (kPasses > 1) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
