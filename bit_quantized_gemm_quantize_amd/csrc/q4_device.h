@@ -161,3 +161,58 @@ __device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace q4
+
+namespace q4 {
+
+// 4 bytes per lane from a buffer straight into LDS (lane i -> lds_wave_base + 4 i).
+__device__ __forceinline__ void buf_ld4_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 4, (int)off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), 0 <= N <= 63 (gfx9 encoding: low 4 bits in [3:0], high 2
+// bits in [15:14]), expcnt and lgkmcnt untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+}  // namespace q4
+
+namespace q4 {
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also waits for
+// every outstanding global access of the wave (vmcnt(0)), which would drain the
+// loads kept in flight several K-tiles ahead; loads into LDS are waited for
+// explicitly (wait_vmcnt) before this barrier instead.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace q4
+
+namespace q4 {
+
+// The same loads into LDS written as instructions the compiler does not see as
+// LDS writes.  Its automatic waits would otherwise drain every load in flight
+// (vmcnt(0)) before any LDS read, since it cannot tell which ring stage a load
+// targets; with these, the kernel waits explicitly (wait_vmcnt) for exactly the
+// stage it reads next and never reads or reuses a stage a load may still write.
+// No register is written by these instructions; M0 carries the wave's LDS base.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_ld16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t off) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(off), "s"(base), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_ld4(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t off) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+               :: "v"(off), "s"(base), "s"(r) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+}  // namespace q4

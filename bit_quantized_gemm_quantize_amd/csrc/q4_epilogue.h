@@ -60,14 +60,15 @@ __device__ __forceinline__ void epilogue_lowrank(v16f (&acc)[4][4], int64_t n_ba
   }
 }
 
-// Output staging through LDS: each wave writes its 128 x 128 region (bf16: all of
-// it; fp32: half the columns per pass) into LDS rows of 272 bytes, then reads it
-// back so that every store instruction writes 4 full rows of 256 contiguous bytes.
-// Direct stores from the MFMA layout would write 16-byte pieces of 32 different
-// rows per instruction.
-constexpr int kStageRowBytes = 272;                         // 256 + 16 bytes of padding
-constexpr int kStageWaveBytes = 128 * kStageRowBytes;       // 34816
-constexpr int kEpilogueLdsBytes = 4 * kStageWaveBytes;      // 139264 for 4 waves
+// Output staging through LDS: each wave writes a 128-row x 128-byte slab of its
+// 128 x 128 output region into LDS (rows padded to 144 bytes), then reads it back
+// so that every store instruction writes 8 full 128-byte row segments; bf16 takes
+// 2 such passes (64 columns each), fp32 takes 4 (32 columns).  Direct stores from
+// the MFMA layout would write 8- or 16-byte pieces of 32 different rows per
+// instruction.
+constexpr int kStageRowBytes = 144;                         // 128 + 16 bytes of padding
+constexpr int kStageWaveBytes = 128 * kStageRowBytes;       // 18432
+constexpr int kEpilogueLdsBytes = 4 * kStageWaveBytes;      // for 4 waves
 
 template <bool OUT_F32>
 __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base, int64_t m_base,
@@ -93,12 +94,17 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base
         for (int j = 0; j < 4; ++j) acc[f][g][4 * vq + j] += b[j];
     }
 
-  constexpr int kPasses = OUT_F32 ? 2 : 1;       // fp32: 64 columns per pass
-  constexpr int kFPerPass = 4 / kPasses;
-  constexpr int kColsPerPass = 32 * kFPerPass;   // 128 (bf16) or 64 (fp32)
   constexpr int kElem = OUT_F32 ? 4 : 2;
+  constexpr int kFPerPass = OUT_F32 ? 1 : 2;     // 32-column accumulator blocks per pass
+  constexpr int kPasses = 4 / kFPerPass;
+  constexpr int kColsPerPass = 32 * kFPerPass;   // 128 bytes of output per row
+  constexpr int kPer16 = 16 / kElem;             // elements per 16-byte store
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass > 0) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): previous pass read back
+      __builtin_amdgcn_wave_barrier();
+    }
     // registers -> LDS: row m_local = 32 g + lane%32, columns 32 f' + 8 vq + 4 h .. +3
 #pragma unroll
     for (int fp = 0; fp < kFPerPass; ++fp) {
@@ -122,13 +128,12 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    // LDS -> global: 16 lanes per row (16 bytes each), 4 rows per instruction
-    const int col_bytes = (lane & 15) * 16;
+    // LDS -> global: 8 lanes per row (16 bytes each), 8 rows per instruction
+    const int col_bytes = (lane & 7) * 16;
     const int64_t n = n_base + pass * kColsPerPass + col_bytes / kElem;
-    constexpr int kPer16 = 16 / kElem;          // elements per 16 bytes
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int ml = 4 * it + (lane >> 4);
+    for (int it = 0; it < 16; ++it) {
+      const int ml = 8 * it + (lane >> 3);
       const int64_t m = m_base + ml;
       const u32x4 v = ld16(stage + ml * kStageRowBytes + col_bytes);
       if (m < M) {
@@ -143,10 +148,6 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base
           }
         }
       }
-    }
-    if (kPasses > 1) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
     }
   }
 }
