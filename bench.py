@@ -91,13 +91,212 @@ def cpu_baseline(d, budget_s=12.0):
                       f"(+ low-rank, + error bound) against all {N} columns; {dt:.1f} s"}
 
 
+GEMM_KERNEL_PREFIX = "void q4::gemm_mx_kernel<32, false>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+CAL_BYTES = 256 * 2 ** 20          # the calibration copy below: 64 Mi fp32 in, 64 Mi fp32 out
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(stats_csv, fetch_csv, write_csv, command):
+    """Turns the rocprofv3 outputs of a bench run (one --kernel-trace --stats run,
+    one --pmc FETCH_SIZE run, one --pmc WRITE_SIZE run) into the committed text
+    summary and the traffic record read by measured_traffic().  HBM bytes of the
+    GEMM are the counters' per-dispatch KiB, each scaled by the ratio of the bytes
+    the calibration copy really moves to what the same counter reports for it."""
+    lines = [f"# rocprofv3 summary: MXFP4 W4A4 GEMM + low-rank epilogue, M={M} K={K} N={N} r={RANK}",
+             "", "command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    lines += ["    " + c for c in command]
+    lines += ["", "## kernel stats (--kernel-trace --stats)", "",
+              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    gemm_avg_ns = None
+    for r in _csv_rows(stats_csv):
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+        if name.startswith(GEMM_KERNEL_PREFIX):
+            gemm_avg_ns = float(r["AverageNs"])
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in _csv_rows(path):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        gemm = [v for k, d in vals.items() if k.startswith(GEMM_KERNEL_PREFIX) for v in d.values()]
+        cal = [v for k, d in vals.items() if k.startswith(COPY_KERNEL) for v in d.values()]
+        return float(np.mean(gemm)), float(np.max(cal))
+
+    fetch_kib, cal_fetch_kib = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write_kib, cal_write_kib = per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale = CAL_BYTES / (cal_fetch_kib * 1024.0)
+    w_scale = CAL_BYTES / (cal_write_kib * 1024.0)
+    fetch_b, write_b = fetch_kib * 1024.0 * f_scale, write_kib * 1024.0 * w_scale
+    alg_in = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * RANK * 4 + N * RANK * 2
+    alg_out = M * N * 2
+    lines += ["", "## HBM traffic of the GEMM (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"calibration copy `{COPY_KERNEL}` of {CAL_BYTES} bytes: FETCH_SIZE {cal_fetch_kib:.0f} KiB, "
+              f"WRITE_SIZE {cal_write_kib:.0f} KiB -> scale {f_scale:.4f} (fetch), {w_scale:.4f} (write)", "",
+              f"GEMM per dispatch: FETCH_SIZE {fetch_kib:.0f} KiB -> {fetch_b / 1e6:.2f} MB; "
+              f"WRITE_SIZE {write_kib:.0f} KiB -> {write_b / 1e6:.2f} MB", "",
+              f"algorithmic bytes per launch: read {alg_in / 1e6:.2f} MB (A, B codes + scales, t, L2^T), "
+              f"write {alg_out / 1e6:.2f} MB (Y bf16); measured / algorithmic = "
+              f"{(fetch_b + write_b) / (alg_in + alg_out):.3f}"]
+    if gemm_avg_ns:
+        lines += ["", f"GEMM average duration {gemm_avg_ns / 1e3:.2f} us -> "
+                      f"{2.0 * M * N * K / (gemm_avg_ns * 1e-9) / 1e12:.1f} TFLOP/s "
+                      f"({100 * 2.0 * M * N * K / (gemm_avg_ns * 1e-9) / 1e12 / MXFP4_PEAK_TFLOPS:.1f}% "
+                      f"of {MXFP4_PEAK_TFLOPS:.0f})"]
+    rec = {"kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": round(fetch_b + write_b),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "fetch_scale": f_scale, "write_scale": w_scale, "gemm_avg_us": gemm_avg_ns and gemm_avg_ns / 1e3}
+    return "\n".join(lines) + "\n", rec
+
+
+def bench_rows(reps=20):
+    """Times every other step of the path on its own workload and prints one JSON
+    line per row: the quantizers and packers against the HBM peak (algorithmic
+    bytes: X read once, codes and scales written once), the GEMMs against their MFMA
+    peak, and W4A16 next to a plain bf16 GEMM (torch, hipBLASLt) of the same shape."""
+    import torch
+    from bit_quantized_gemm_quantize_amd import binding as B
+    from bit_quantized_gemm_quantize_amd import synth
+
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed(fn, n_sets):
+        for i in range(3):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i % n_sets)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def emit(row, ms, bytes_=None, flops=None, peak=None, note=""):
+        rec = {"row": row, "us": round(ms * 1e3, 2)}
+        if bytes_ is not None:
+            gbs = bytes_ / (ms * 1e-3) / 1e9
+            rec.update({"GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes": int(bytes_)})
+        if flops is not None:
+            tf = flops / (ms * 1e-3) / 1e12
+            rec.update({"TFLOP/s": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4)})
+        if note:
+            rec["note"] = note
+        print(json.dumps(rec), flush=True)
+
+    # ---- a1 + a3: MXFP4 activation quantizer (+ t = X L1), rotating 10 copies of X
+    Mq, Kq = 4608, 3072
+    x0 = bf16_dev(synth.activations(Mq, Kq, seed=0, dist="student_t3")[0])
+    xs = [x0] + [x0.clone() for _ in range(9)]
+    l1t = bf16_dev(synth.to_bf16_bits(np.random.default_rng(1).standard_normal((RANK, Kq)) * 0.05))
+    ac, asc, _ = B.empty_quant("mxfp4", Mq, Kq, dev)
+    tq = torch.empty((Mq, RANK), dtype=torch.float32, device=dev)
+    for r in (0, RANK):
+        ms = timed(lambda i: B.quantize_act("mxfp4", xs[i], ac, asc, None, l1t if r else None,
+                                            tq if r else None, stream), len(xs))
+        nbytes = 2 * Mq * Kq + Mq * Kq // 2 + Mq * Kq // 32 + (4 * Mq * r + 2 * Kq * r)
+        emit(f"quantize_act mxfp4 r={r} {Mq}x{Kq}", ms, bytes_=nbytes,
+             note="10 rotating copies of X (283 MB)")
+    del xs
+
+    # ---- a2: NVFP4 activation quantizer, QKV shape, 3 rotating copies of X (311 MB)
+    Mn, Kn, Nn = 16896, 3072, 9216
+    xn0 = bf16_dev(synth.qkv_nvfp4(step=0)["x"])
+    xns = [xn0, xn0.clone(), xn0.clone()]
+    nc, nsc, nts = B.empty_quant("nvfp4", Mn, Kn, dev)
+    ms = timed(lambda i: B.quantize_act("nvfp4", xns[i], nc, nsc, nts, stream=stream), len(xns))
+    emit(f"quantize_act nvfp4 {Mn}x{Kn}", ms, bytes_=2 * Mn * Kn + Mn * Kn // 2 + Mn * Kn // 16 + 4,
+         note="algorithmic bytes count one read of X; the tensor amax pass reads it a second time")
+
+    # ---- a7: NVFP4 GEMM, QKV shape
+    wq = bf16_dev(synth.qkv_nvfp4_weight())
+    bnc, bnsc, bnts = B.empty_quant("nvfp4", Nn, Kn, dev)
+    B.pack_weights("nvfp4", wq, Kn, Nn, 1, Kn, bnc, bnsc, tensor_scale=bnts, stream=stream)
+    yq = torch.empty((Mn, Nn), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda i: B.gemm_w4a4("nvfp4", nc, nsc, nts, bnc, bnsc, bnts, Mn, Nn, Kn, yq,
+                                     stream=stream), 1)
+    emit(f"gemm_w4a4 nvfp4 {Mn}x{Kn}x{Nn}", ms, flops=2.0 * Mn * Nn * Kn, peak=2500.0,
+         note="exact bf16 dequant + bf16 MFMA; peak = dense bf16")
+    del xns, xn0, yq, wq
+
+    # ---- a4: packers, MLP up-projection residual weight [N, K]
+    Np = 12288
+    wt = bf16_dev(synth.weights(Np, Kq, seed=0))
+    bc, bsc, _ = B.empty_quant("mxfp4", Np, Kq, dev)
+    ms = timed(lambda i: B.pack_weights("mxfp4", wt, Kq, Np, 1, Kq, bc, bsc, stream=stream), 1)
+    emit(f"pack_weights mxfp4 {Np}x{Kq}", ms, bytes_=2 * Np * Kq + Np * Kq // 2 + Np * Kq // 32,
+         note="offline step")
+    ic, isc, izc = B.empty_quant("int4_g64", Np, Kq, dev)
+    ms = timed(lambda i: B.pack_weights("int4_g64", wt, Kq, Np, 1, Kq, ic, isc, izc, stream=stream), 1)
+    emit(f"pack_weights int4_g64 {Np}x{Kq}", ms, bytes_=2 * Np * Kq + Np * Kq // 2 + Np * Kq // 16,
+         note="offline step")
+
+    # ---- a5: MXFP4 GEMM without the branch, MLP and attention-projection shapes
+    B.quantize_act("mxfp4", x0, ac, asc, stream=stream)
+    for n in (12288, 3072):
+        y = torch.empty((Mq, n), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda i: B.gemm_w4a4("mxfp4", ac, asc, None, bc[:n], bsc[:n], None, Mq, n, Kq, y,
+                                         stream=stream), 1)
+        emit(f"gemm_w4a4 mxfp4 {Mq}x{Kq}x{n} bf16 out", ms, flops=2.0 * Mq * n * Kq,
+             peak=MXFP4_PEAK_TFLOPS, note="inputs warm in L2/MALL")
+
+    # ---- a8: W4A16 against a plain bf16 GEMM of the same shape
+    wbf = wt
+    for m in (512, 4608):
+        xw = x0[:m].contiguous()
+        y = torch.empty((m, Np), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda i: B.gemm_w4a16(xw, ic, isc, izc, Np, y, stream=stream), 1)
+        emit(f"gemm_w4a16 {m}x{Kq}x{Np}", ms, flops=2.0 * m * Np * Kq, peak=2500.0,
+             note="int4 g64 dequant in LDS + bf16 MFMA")
+        ms = timed(lambda i: torch.matmul(xw, wbf.t(), out=y), 1)
+        emit(f"torch bf16 matmul {m}x{Kq}x{Np}", ms, flops=2.0 * m * Np * Kq, peak=2500.0,
+             note="comparison: hipBLASLt via torch, unquantized bf16 weight")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", action="store_true",
+                    help="time every other step of the path, one JSON line per row")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the rocprofv3 summary under profiles/ (no GPU needed)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize: a command line that produced the inputs")
     a = ap.parse_args()
+    if a.summarize:
+        text, rec = summarize_profiles(*a.summarize, a.command)
+        with open(os.path.join(ROOT, "profiles", "gemm_mx_mlp_up_4608x3072x12288.md"), "w") as f:
+            f.write(text)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(text)
+        return
+    if a.rows:
+        bench_rows()
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
