@@ -1,9 +1,12 @@
-// MXFP4 x MXFP4 GEMM on the CDNA4 block-scaled MFMA, low-rank branch and bias
-// fused into the epilogue.
+// MXFP4 x MXFP4 GEMM on the CDNA4 block-scaled MFMA with the low-rank branch
+// fused in (its bf16 MFMAs seed the accumulators before the K loop) and the bias
+// and store in the epilogue.
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), 128 x 128 per
-// wave as 4 x 4 MFMA tiles of v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4, one
-// E8M0 scale per 32 K elements per row, applied by the MFMA itself).  K advances in
+// Tiling: 256 x 256 output tile per workgroup of 8 waves, two per SIMD, so that
+// one wave's MFMAs run while the other waits on an LDS read or a load issue.  Wave
+// (wm, wn) owns m in [128 wm, +128) and n in [64 wn, +64) as 2 x 4 tiles of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4, one E8M0 scale per 32 K elements
+// per row, applied by the MFMA itself); 128 accumulators per lane.  K advances in
 // tiles of 256 elements (128 bytes per row; 8 scale bytes per row).
 //
 // K order inside a K-tile: lane half h (= lane/32) of every fragment owns the
@@ -26,11 +29,11 @@ namespace q4 {
 constexpr int kBM = 256, kBN = 256;
 constexpr int kKT = 256;          // K elements per K-tile
 constexpr int kKTB = kKT / 2;     // bytes per row per K-tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kGroupM = 4;
 
 template <int R, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
+__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
     const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
@@ -41,15 +44,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
   constexpr int kCodeLds = 2 * 2 * kBM * kKTB;          // 131072
   constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
   constexpr int kMainLds = kCodeLds + kScaleLds;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds > kEpilogueLdsBytes ? kMainLds : kEpilogueLdsBytes];
+  static_assert((kThreads / 64) * kStageWaveBytes <= kMainLds, "the epilogue stages each wave's output in the operand LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
   auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
 
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, kGroupM, &tm, &tn);
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wy = wave >> 1, wx = wave & 1;       // wave's n half, m half
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 1, wm = wave & 1;       // wave's n quarter, m half
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t kbytes = (uint32_t)(K >> 1), nblk = (uint32_t)(K >> 5);
   const int nkt = (int)((K + kKT - 1) / kKT);
@@ -63,81 +68,107 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
 
   // codes, global -> LDS: each wave moves 8 rows x 128 bytes per instruction straight
   // into LDS (lane i -> row i/8, stored position i%8, which holds global chunk
-  // (i%8) ^ (row & 7), the swizzle).  Wave w covers rows 64 w .. 64 w + 63.
+  // (i%8) ^ (row & 7), the swizzle).  Wave w covers rows 32 w .. 32 w + 31 of
+  // each operand.
   const int lr = lane >> 3, lp = lane & 7;
   auto gload = [&](int kt, int stage, int operand) {
     const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
     const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
     const auto rc = operand == 0 ? rc_a : rc_b;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t row = 64 * wave + 8 * j + lr;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = 32 * wave + 8 * j + lr;
       // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
-      buf_ld16_lds(rc, &lds[stage][operand][(64 * wave + 8 * j) * kKTB], row * kbytes + koff);
+      buf_ld16_lds(rc, &lds[stage][operand][(32 * wave + 8 * j) * kKTB], row * kbytes + koff);
     }
   };
-  // scales, global -> LDS: lane i of wave w takes row 64 w + i, 16 bytes = the scale
-  // bytes of K-tiles kt and kt+1 (the second half is unused when kt+1 is past K)
+  // scales, global -> LDS: waves 0-3 take the activation rows, waves 4-7 the weight
+  // rows; lane i of wave w takes row 64 (w % 4) + i, 16 bytes = the scale bytes of
+  // K-tiles kt and kt+1 (the second half is unused when kt+1 is past K)
+  const int sop = wave >> 2, sw = wave & 3;
+  const auto rs_op = sop == 0 ? rs_a : rs_b;
   auto sload = [&](int kt, int stage) {
     const uint32_t b0 = (uint32_t)kt * 8;
     const uint32_t koff = b0 < nblk ? b0 : kOOB;
-    const uint32_t off = (64 * wave + lane) * nblk + koff;
-    buf_ld16_lds(rs_a, &lsc[stage][0][64 * wave * 16], off);
-    buf_ld16_lds(rs_b, &lsc[stage][1][64 * wave * 16], off);
+    const uint32_t off = (64 * sw + lane) * nblk + koff;
+    buf_ld16_lds(rs_op, &lsc[stage][sop][64 * sw * 16], off);
   };
   // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3
-  uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
+  uint32_t sa[4], sb[2], sa_n[4], sb_n[2];
   auto read_scales = [&](int kt, int stage, uint32_t* xa, uint32_t* xb) {
     const bool kin = (uint32_t)kt * 8 + 4 * h < nblk;      // past K: codes are 0; keep 2**0
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wx * 128 + 32 * g + r32) * 16 + 4 * h]);
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wm * 128 + 32 * g + r32) * 16 + 4 * h]);
       xa[g] = kin ? v : 0x7F7F7F7Fu;
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wy * 128 + 32 * f + r32) * 16 + 4 * h]);
+    for (int f = 0; f < 2; ++f) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 64 + 32 * f + r32) * 16 + 4 * h]);
       xb[f] = kin ? v : 0x7F7F7F7Fu;
     }
   };
 
   // fragment registers, double-buffered across MFMA steps
-  u32x4 fa[2][4], fb[2][4];
+  u32x4 fa[2][4], fb[2][2];
   auto read_frags = [&](int buf, int stage, int s) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int row = wx * 128 + 32 * g + r32;
+      const int row = wm * 128 + 32 * g + r32;
       fa[buf][g] = ld16(&lds[stage][0][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int row = wy * 128 + 32 * f + r32;
+    for (int f = 0; f < 2; ++f) {
+      const int row = wn * 64 + 32 * f + r32;
       fb[buf][f] = ld16(&lds[stage][1][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
   };
 
-  v16f acc[4][4];
+  v16f acc[2][4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
 #define Q4_MX_MMA(S, BUF)                                                                       \
-  _Pragma("unroll") for (int f = 0; f < 4; ++f)                                                 \
+  _Pragma("unroll") for (int f = 0; f < 2; ++f)                                                 \
     _Pragma("unroll") for (int g = 0; g < 4; ++g)                                               \
       acc[f][g] = mfma_fp4_32x32x64<S, S>(fb[BUF][f], fa[BUF][g], acc[f][g], (int)sb[f],       \
                                           (int)sa[g]);
 // within a region: the LDS reads for the next step go out first, then the MFMAs
 #define Q4_READS_THEN_MMA(NREADS)                          \
   __builtin_amdgcn_sched_group_barrier(0x100, NREADS, 0); \
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 
+  const int64_t n_base = n0 + wn * 64, m_base = m0 + wm * 128;
   if (nkt > 0) {
     gload(0, 0, 0);
     gload(0, 0, 1);
     sload(0, 0);
-    wait_vmem();
-    __syncthreads();
+  }
+  // The low-rank term t L2 goes into the accumulators first.  The tile's t rows
+  // and L2^T rows (contiguous in memory) are loaded into the second, still unused
+  // operand stage together with the first K-tile, so the epilogue is left with the
+  // bias and the store.
+  if (R > 0) {
+    const auto rt = make_rsrc(t + m0 * R, rows_a * (uint32_t)(4 * R));
+    const auto rl = make_rsrc(l2t + n0 * R, rows_b * (uint32_t)(2 * R));
+    uint8_t* lt = &lds[1][0][0];
+    uint8_t* ll = lt + kBM * 4 * R;
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j)              // kBM * 4R bytes in 1 KB pieces
+      buf_ld16_lds(rt, lt + (wave * (R / 8) + j) * 1024, (wave * (R / 8) + j) * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < R / 16; ++j)             // kBN * 2R bytes
+      buf_ld16_lds(rl, ll + (wave * (R / 16) + j) * 1024, (wave * (R / 16) + j) * 1024 + lane * 16);
+  }
+  wait_vmem();
+  __syncthreads();
+  if (R > 0) {
+    lowrank_accumulate_lds<R>(acc, &lds[1][0][0], &lds[1][0][0] + kBM * 4 * R, 128 * wm, 64 * wn, lane);
+    lds_barrier();                           // stage 1 is free again for K-tile 1
+  }
+  if (nkt > 0) {
     read_frags(0, 0, 0);
     read_scales(0, 0, sa, sb);
   }
@@ -153,26 +184,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     gload(kt + 1, st ^ 1, 0);
     sload(kt + 1, st ^ 1);
     Q4_MX_MMA(0, 0)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    for (int i = 0; i < 10; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    for (int i = 0; i < 5; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, st, 2);
     gload(kt + 1, st ^ 1, 1);
     Q4_MX_MMA(1, 1)
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(1, st, 3);
     Q4_MX_MMA(2, 0)
-    Q4_READS_THEN_MMA(8)
+    Q4_READS_THEN_MMA(6)
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem();
     // every wave's tile kt+1 has landed, and every read of tile kt has completed
@@ -180,16 +211,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(
     read_frags(0, st ^ 1, 0);
     read_scales(kt + 1, st ^ 1, sa_n, sb_n);
     Q4_MX_MMA(3, 1)
-    Q4_READS_THEN_MMA(16)
+    Q4_READS_THEN_MMA(12)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) { sa[g] = sa_n[g]; sb[g] = sb_n[g]; }
+    for (int g = 0; g < 4; ++g) sa[g] = sa_n[g];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) sb[f] = sb_n[f];
   }
 #undef Q4_MX_MMA
 #undef Q4_READS_THEN_MMA
 
-  const int64_t n_base = n0 + wy * 128, m_base = m0 + wx * 128;
-  if (R > 0) epilogue_lowrank<R>(acc, n_base, m_base, M, N, t, l2t, lane);
   __syncthreads();                           // all waves are done reading operand tiles
   epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds_raw + wave * kStageWaveBytes);
 }

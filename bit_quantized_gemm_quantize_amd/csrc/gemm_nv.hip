@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = acc[f][g] * scale;
   const int64_t n_base = ld.n0 + wy * 128, m_base = ld.m0 + wx * 128;
-  if (R > 0) epilogue_lowrank<R>(acc, n_base, m_base, M, N, t, l2t, lane);
+  if (R > 0) lowrank_accumulate<R>(acc, n_base, m_base, M, N, t, l2t, lane);
   __syncthreads();                           // all waves are done reading operand tiles
   epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
 }

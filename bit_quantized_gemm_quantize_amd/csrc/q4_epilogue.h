@@ -1,10 +1,12 @@
-// Epilogue shared by the GEMM kernels.  The main loop leaves a wave with a 4 x 4
-// grid of 32x32 fp32 accumulators laid out as D[n][m] (MFMA A operand = weight
-// rows n, B operand = activation rows m), so lane l holds output row m = l%32 of
-// each tile and, per register group v/4, four consecutive output columns n.
+// Epilogue shared by the GEMM kernels.  The main loop leaves a wave with an F x 4
+// grid of 32x32 fp32 accumulators (F = 4 or 2 weight sub-tiles) laid out as
+// D[n][m] (MFMA A operand = weight rows n, B operand = activation rows m), so lane
+// l holds output row m = l%32 of each tile and, per register group v/4, four
+// consecutive output columns n.
 //
-// Order of the epilogue: (optional) scale, low-rank up-projection t L2 as bf16
-// MFMAs on the same accumulators with t split into bf16 hi + lo, bias, store.
+// The low-rank up-projection t L2 runs as bf16 MFMAs on the same accumulators,
+// with t split into bf16 hi + lo (before the K loop or after it); the store adds
+// the bias and writes bf16 or fp32.
 #pragma once
 
 #include "q4_device.h"
@@ -13,15 +15,15 @@
 namespace q4 {
 
 // acc[f][g]: f = weight (n) sub-tile, g = activation (m) sub-tile, 32 x 32 each.
-// n_base / m_base: first n / m of the wave's 128 x 128 region.
-template <int R>
-__device__ __forceinline__ void epilogue_lowrank(v16f (&acc)[4][4], int64_t n_base, int64_t m_base,
+// n_base / m_base: first n / m of the wave's (32 F) x 128 region.
+template <int R, int F>
+__device__ __forceinline__ void lowrank_accumulate(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
                                                  int64_t M, int64_t N, const float* __restrict__ t,
                                                  const uint16_t* __restrict__ l2t, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < R / 16; ++ks) {
-    u32x4 thi[4], tlo[4], l2f[4];
+    u32x4 thi[4], tlo[4], l2f[F];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t m = m_base + 32 * g + r32;
@@ -46,12 +48,55 @@ __device__ __forceinline__ void epilogue_lowrank(v16f (&acc)[4][4], int64_t n_ba
       }
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < F; ++f) {
       const int64_t n = n_base + 32 * f + r32;
       l2f[f] = (n < N) ? ld16(l2t + n * R + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        acc[f][g] = mfma_bf16_32x32x16(l2f[f], thi[g], acc[f][g]);
+        acc[f][g] = mfma_bf16_32x32x16(l2f[f], tlo[g], acc[f][g]);
+      }
+  }
+}
+
+// The same t L2 term with both operands already in LDS: lds_t holds the tile's t
+// rows (fp32, 4R bytes each, row m_local at m_local * 4R), lds_l2 its L2^T rows
+// (bf16, 2R bytes each).  m_loc / n_loc: first row of the wave's region within
+// the tile.
+template <int R, int F>
+__device__ __forceinline__ void lowrank_accumulate_lds(v16f (&acc)[F][4], const uint8_t* lds_t,
+                                                       const uint8_t* lds_l2, int m_loc, int n_loc,
+                                                       int lane) {
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < R / 16; ++ks) {
+    u32x4 thi[4], tlo[4], l2f[F];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint8_t* src = lds_t + (m_loc + 32 * g + r32) * (4 * R) + (16 * ks + 8 * h) * 4;
+      const u32x4 a = ld16(src), b = ld16(src + 16);
+      const uint32_t tv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = __uint_as_float(tv[j]);
+        hi[j] = f32_to_bf16_rne(v);
+        lo[j] = f32_to_bf16_rne(v - __uint_as_float(hi[j] << 16));
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        thi[g][d] = hi[2 * d] | (hi[2 * d + 1] << 16);
+        tlo[g][d] = lo[2 * d] | (lo[2 * d + 1] << 16);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+      l2f[f] = ld16(lds_l2 + (n_loc + 32 * f + r32) * (2 * R) + (16 * ks + 8 * h) * 2);
+#pragma unroll
+    for (int f = 0; f < F; ++f)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         acc[f][g] = mfma_bf16_32x32x16(l2f[f], thi[g], acc[f][g]);
@@ -61,24 +106,23 @@ __device__ __forceinline__ void epilogue_lowrank(v16f (&acc)[4][4], int64_t n_ba
 }
 
 // Output staging through LDS: each wave writes a 128-row x 128-byte slab of its
-// 128 x 128 output region into LDS (rows padded to 144 bytes), then reads it back
-// so that every store instruction writes 8 full 128-byte row segments; bf16 takes
-// 2 such passes (64 columns each), fp32 takes 4 (32 columns).  Direct stores from
-// the MFMA layout would write 8- or 16-byte pieces of 32 different rows per
-// instruction.
+// 128 x (32 F) output region into LDS (rows padded to 144 bytes), then reads it
+// back so that every store instruction writes 8 full 128-byte row segments; a pass
+// covers 64 bf16 or 32 fp32 columns.  Direct stores from the MFMA layout would
+// write 8- or 16-byte pieces of 32 different rows per instruction.
 constexpr int kStageRowBytes = 144;                         // 128 + 16 bytes of padding
 constexpr int kStageWaveBytes = 128 * kStageRowBytes;       // 18432
 constexpr int kEpilogueLdsBytes = 4 * kStageWaveBytes;      // for 4 waves
 
-template <bool OUT_F32>
-__device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base, int64_t m_base,
+template <bool OUT_F32, int F>
+__device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
                                                int64_t M, int64_t N,
                                                const uint16_t* __restrict__ bias, void* y,
                                                int64_t ldy, int lane, uint8_t* stage) {
   const int r32 = lane & 31, h = lane >> 5;
   // bias, per accumulator group of 4 consecutive columns
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int vq = 0; vq < 4; ++vq) {
       const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
@@ -96,7 +140,7 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[4][4], int64_t n_base
 
   constexpr int kElem = OUT_F32 ? 4 : 2;
   constexpr int kFPerPass = OUT_F32 ? 1 : 2;     // 32-column accumulator blocks per pass
-  constexpr int kPasses = 4 / kFPerPass;
+  constexpr int kPasses = F / kFPerPass;
   constexpr int kColsPerPass = 32 * kFPerPass;   // 128 bytes of output per row
   constexpr int kPer16 = 16 / kElem;             // elements per 16-byte store
 #pragma unroll
