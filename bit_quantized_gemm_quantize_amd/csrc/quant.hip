@@ -2,15 +2,18 @@
 // and the offline weight packers.
 //
 // Activation pass (one read of X):
-//   * a workgroup owns 32 rows and all of K; its 8 waves stride over K in pairs of
-//     32-element blocks, so a lane (row l%32, half l/32) owns one whole block per
-//     step: 64 contiguous bytes of X in, 16 bytes of codes and its scale out.
-//     The block maximum therefore needs no cross-lane exchange.
+//   * a workgroup owns up to 32 rows (as many as spread M evenly over the CUs) and
+//     all of K; its 8 waves stride over K in pairs of 32-element blocks, so a lane
+//     (row l%32, half l/32) owns one whole block per step: 64 contiguous bytes of X
+//     in, 16 bytes of codes and its scale out.  The block maximum therefore needs
+//     no cross-lane exchange.
 //   * the same 64 bytes are the bf16 MFMA operand of t = X L1: the 32 block
 //     elements feed four 32x32x16 steps (K order permuted identically for X and L1,
 //     which a sum over K allows); L1^T rows are read 16 bytes at a time.
 //   * per-wave partial t tiles are summed through LDS in a fixed order, so t is
 //     deterministic.
+#include <algorithm>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -74,17 +77,38 @@ __device__ __forceinline__ uint32_t nv_encode32(const uint32_t* w, float s_t, fl
 }
 
 // ---------------------------------------------------------------------------- activation pass
+// One pair of 32-element blocks per lane half: the 64 bytes of X of block `blk` of
+// `row` (zeros past M or K).
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t row, int64_t ldx,
+                                           int64_t blk, bool ok, uint32_t* w) {
+  if (ok) {
+    const uint16_t* src = x + row * ldx + blk * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = ld16(src + 8 * q);
+      w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = 0;
+  }
+}
+
+// A workgroup owns `rows` (<= 32) consecutive rows and all of K; rows is chosen
+// so the workgroups spread evenly over the CUs (lanes past it idle).  Each of the 8
+// waves takes every 8th pair of blocks, keeping the X bytes of three pairs in
+// flight per lane.
 template <int FMT, int R>
 __global__ __launch_bounds__(512) void quant_act_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, const float* __restrict__ amax_t, const uint16_t* __restrict__ l1t,
-    float* __restrict__ t) {
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int rows,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax_t,
+    const uint16_t* __restrict__ l1t, float* __restrict__ t) {
   __shared__ float red[R > 0 ? kQWaves * 32 * 32 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.x * kQRows;
+  const int64_t m0 = (int64_t)blockIdx.x * rows;
   const int64_t row = m0 + i;
-  const bool row_ok = row < M;
+  const bool row_ok = i < rows && row < M;
   const int64_t nblk = K >> 5;
   const int64_t npair = (nblk + 1) >> 1;
   const int64_t sbytes = FMT == 0 ? nblk : 2 * nblk;   // scale bytes per row
@@ -96,17 +120,14 @@ __global__ __launch_bounds__(512) void quant_act_kernel(
   }
   v16f acc = {};
 
-  for (int64_t p = wave; p < npair; p += kQWaves) {
+  auto load = [&](int64_t p, uint32_t* w) {
+    load_block(x, row, ldx, 2 * p + h, row_ok && p < npair && 2 * p + h < nblk, w);
+  };
+  auto step = [&](int64_t p, uint32_t* w) {
+    if (p >= npair) return;
     const int64_t blk = 2 * p + h;
     const bool blk_ok = blk < nblk;
-    uint32_t w[16];
     if (row_ok && blk_ok) {
-      const uint16_t* src = x + row * ldx + blk * 32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 v = ld16(src + 8 * q);
-        w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
-      }
       u32x4 c;
       if (FMT == 0) {
         const int E = mx_block_exponent(bf16_amax_bits<16>(w));
@@ -119,9 +140,6 @@ __global__ __launch_bounds__(512) void quant_act_kernel(
         *reinterpret_cast<uint16_t*>(scales + row * sbytes + 2 * blk) = (uint16_t)sc;
       }
       st16(codes + row * (K >> 1) + blk * 16, c);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) w[q] = 0;
     }
     if (R > 0) {
 #pragma unroll
@@ -132,6 +150,17 @@ __global__ __launch_bounds__(512) void quant_act_kernel(
         acc = mfma_bf16_32x32x16(a, b, acc);
       }
     }
+    load(p + 3 * kQWaves, w);                 // refill this buffer three steps ahead
+  };
+  uint32_t w0[16], w1[16], w2[16];
+  const int64_t p0 = wave;
+  load(p0, w0);
+  load(p0 + kQWaves, w1);
+  load(p0 + 2 * kQWaves, w2);
+  for (int64_t p = p0; p < npair; p += 3 * kQWaves) {
+    step(p, w0);
+    step(p + kQWaves, w1);
+    step(p + 2 * kQWaves, w2);
   }
 
   if (R > 0) {
@@ -145,7 +174,7 @@ __global__ __launch_bounds__(512) void quant_act_kernel(
       float sum = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < kQWaves; ++wv) sum += red[wv * 1024 + rr * 32 + cc];
-      if (m0 + rr < M) t[(m0 + rr) * R + cc] = sum;
+      if (rr < rows && m0 + rr < M) t[(m0 + rr) * R + cc] = sum;
     }
   }
 }
@@ -156,20 +185,28 @@ __global__ void clear_f32_kernel(float* p) { *p = 0.0f; }
 __global__ void nv_finalize_kernel(float* p) { *p = nv_tensor_scale(*p); }
 
 // Largest |x| over a strided [rows, cols] bf16 matrix (element (r, c) at
-// x[r * sr + c * sc]); accumulated with an integer atomic max on the fp32 bit
-// pattern (valid for non-negative values).
+// x[r * sr + c * sc]), reduced per workgroup (wave shuffles, then LDS) and then
+// folded into *amax with one integer atomic max on the fp32 bit pattern per
+// workgroup (valid for non-negative values).
+constexpr int kAmaxBlocks = 1024;
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                    int64_t cols, int64_t sr, int64_t sc,
                                                    float* amax) {
+  __shared__ uint32_t part[4];
   uint32_t m = 0;
   const int64_t total = rows * cols;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  if (sc == 1 && (cols & 7) == 0 && (sr & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-    const int64_t per_row = cols >> 3;
+  if (sc == 1 && (cols & 31) == 0 && (sr & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    // 64 bytes per thread per step, four 16-byte loads in flight
+    const int64_t per_row = cols >> 5;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < rows * per_row; q += stride) {
       const int64_t r = q / per_row, c = q % per_row;
-      u32x4 v = ld16(x + r * sr + c * 8);
-      m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v)));
+      const uint16_t* src = x + r * sr + c * 32;
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = ld16(src + 8 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v[j])));
     }
   } else {
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
@@ -179,15 +216,20 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(reinterpret_cast<unsigned int*>(amax), m << 16);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(part[0], part[1]), max(part[2], part[3]));
+    if (m != 0) atomicMax(reinterpret_cast<unsigned int*>(amax), m << 16);
+  }
 }
 
 static hipError_t queue_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t sr,
                                     int64_t sc, float* amax, hipStream_t s) {
   hipLaunchKernelGGL(clear_f32_kernel, dim3(1), dim3(1), 0, s, amax);
-  const int64_t work = (rows * cols + 7) / 8;
+  const int64_t work = (rows * cols + 31) / 32;
   int64_t blocks = (work + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, sr, sc, amax);
   return hipGetLastError();
@@ -197,9 +239,20 @@ template <int FMT, int R>
 static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
                         uint8_t* scales, const float* amax, const uint16_t* l1t, float* t,
                         hipStream_t s) {
-  const unsigned grid = (unsigned)((M + kQRows - 1) / kQRows);
-  hipLaunchKernelGGL((quant_act_kernel<FMT, R>), dim3(grid), dim3(512), 0, s, x, M, K, ldx, codes,
-                     scales, amax, l1t, t);
+  // rows per workgroup: the fewest whole waves of workgroups over the CUs, at most
+  // 32 rows each (M = 4608 on 256 CUs: 18 rows, one workgroup per CU)
+  int cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+  }
+  int64_t waves = 1;
+  while ((M + cus * waves - 1) / (cus * waves) > kQRows) ++waves;
+  const int rows = (int)std::max<int64_t>(1, (M + cus * waves - 1) / (cus * waves));
+  const unsigned grid = (unsigned)((M + rows - 1) / rows);
+  hipLaunchKernelGGL((quant_act_kernel<FMT, R>), dim3(grid), dim3(512), 0, s, x, M, K, ldx, rows,
+                     codes, scales, amax, l1t, t);
 }
 
 hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
