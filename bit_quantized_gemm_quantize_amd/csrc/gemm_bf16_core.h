@@ -6,10 +6,13 @@
 // 16-byte chunks XOR-swizzled by row, two stages, one barrier per K-tile.
 //
 // A loader policy turns global data into bf16 LDS rows:
-//   Loader::load(kt)         issue the global reads of K-tile kt into registers
-//   Loader::store(lds_a, lds_b)  convert those registers and write both tiles
-// The conversion of tile kt+1 is issued in the same basic block as the MFMAs of
-// tile kt, so the VALU work can overlap the matrix pipe.
+//   Loader::issue(kt, lds_a, lds_b)   issue the global reads of K-tile kt (into
+//                                    registers, or straight into LDS)
+//   Loader::store<P>(lds_a, lds_b)    convert half P (0, 1) of the registers and
+//                                    write it
+// Pipeline: the reads of tile kt+1 go out before tile kt is multiplied; its
+// conversion is spread over the last two MFMA steps of tile kt; the fragments of
+// the next MFMA step are read while the current step's MFMAs run.
 #pragma once
 
 #include "q4_epilogue.h"
@@ -21,60 +24,105 @@ constexpr int kBf16KT = 64;                 // K elements per K-tile
 constexpr int kBf16RowBytes = kBf16KT * 2;  // 128 bytes of bf16 per tile row
 constexpr int kBf16Threads = 256;
 constexpr int kBf16GroupM = 4;
+constexpr int kBf16TileBytes = kBf16BM * kBf16RowBytes;      // one operand tile
+constexpr int kBf16MainLds = 4 * kBf16TileBytes;             // [A0][A1][B0][B1]
 
 __device__ __forceinline__ int lds_chunk_off(int row, int chunk) {
   return row * kBf16RowBytes + ((chunk ^ (row & 7)) << 4);
 }
 
-// 16 MFMAs per step, 4 steps: the wave's 128 x 128 region over one 64-K tile.
-// acc[f][g] holds D[n][m] (A operand = weight rows, B operand = activation rows).
-__device__ __forceinline__ void bf16_tile_mma(v16f (&acc)[4][4], const uint8_t* la, const uint8_t* lb,
-                                              int wx, int wy, int lane) {
+struct Bf16Frags {
+  u32x4 a[2][4], b[2][4];
+};
+
+// fragments of MFMA step s (16 K) of the tile at la / lb into buffer BUF.  Rows
+// 32 g + r32 all have row & 7 == lane & 7, so one swizzled chunk offset per step
+// serves every sub-tile; the sub-tiles are 4 KB apart.
+template <int BUF>
+__device__ __forceinline__ void bf16_read_frags(Bf16Frags& fr, const uint8_t* la, const uint8_t* lb,
+                                                int s, int wx, int wy, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
+  const int chunk = ((2 * s + h) ^ (lane & 7)) << 4;
+  const uint8_t* pa = la + (wx * 128 + r32) * kBf16RowBytes + chunk;
+  const uint8_t* pb = lb + (wy * 128 + r32) * kBf16RowBytes + chunk;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 pa[4], pb[4];
+  for (int g = 0; g < 4; ++g) fr.a[BUF][g] = ld16(pa + g * 32 * kBf16RowBytes);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int row = wx * 128 + 32 * g + r32;
-      pa[g] = ld16(la + lds_chunk_off(row, 2 * s + h));
-    }
+  for (int f = 0; f < 4; ++f) fr.b[BUF][f] = ld16(pb + f * 32 * kBf16RowBytes);
+}
+
+// acc[f][g] holds D[n][m] (A operand = weight rows, B operand = activation rows).
+template <int BUF>
+__device__ __forceinline__ void bf16_mma(v16f (&acc)[4][4], const Bf16Frags& fr) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int row = wy * 128 + 32 * f + r32;
-      pb[f] = ld16(lb + lds_chunk_off(row, 2 * s + h));
-    }
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[f][g] = mfma_bf16_32x32x16(pb[f], pa[g], acc[f][g]);
-  }
+    for (int g = 0; g < 4; ++g) acc[f][g] = mfma_bf16_32x32x16(fr.b[BUF][f], fr.a[BUF][g], acc[f][g]);
+}
+
+// One K-tile: multiply stage `cur` while tile kt+1 is read and converted into `nxt`.
+// Stage st of the operand tiles: A at lds + st * tile, B at lds + (2 + st) * tile,
+// so the stage offsets fold into the LDS instructions' immediate offsets.
+template <int ST>
+__device__ __forceinline__ uint8_t* bf16_a(uint8_t* lds) { return lds + ST * kBf16TileBytes; }
+template <int ST>
+__device__ __forceinline__ uint8_t* bf16_b(uint8_t* lds) { return lds + (2 + ST) * kBf16TileBytes; }
+
+// One K-tile: multiply stage CUR while tile kt+1 is read and converted into the other.
+template <int CUR, class Loader>
+__device__ __forceinline__ void bf16_ktile(v16f (&acc)[4][4], Bf16Frags& fr, Loader& ld, int kt,
+                                           uint8_t* lds, int wx, int wy, int lane) {
+  constexpr int NXT = CUR ^ 1;
+  ld.issue(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  bf16_read_frags<1>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
+  bf16_mma<0>(acc, fr);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16_read_frags<0>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
+  bf16_mma<1>(acc, fr);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16_read_frags<1>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
+  ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  bf16_mma<0>(acc, fr);
+  __builtin_amdgcn_sched_barrier(0);
+  ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  bf16_mma<1>(acc, fr);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmem();                               // loads straight into LDS have landed
+  // every wave has written stage NXT and finished reading stage CUR
+  lds_barrier();
+  bf16_read_frags<0>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
 }
 
 template <class Loader>
 __device__ __forceinline__ void bf16_mainloop(v16f (&acc)[4][4], Loader& ld, int64_t K, uint8_t* lds,
                                               int wx, int wy, int lane) {
-  constexpr int kTile = kBf16BM * kBf16RowBytes;   // bytes per operand tile
-  uint8_t* stage_ptr[2] = {lds, lds + 2 * kTile};
   const int nkt = (int)((K + kBf16KT - 1) / kBf16KT);
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
-  if (nkt > 0) {
-    ld.load(0);
-    ld.store(stage_ptr[0], stage_ptr[0] + kTile);
-    if (nkt > 1) ld.load(1);
+  if (nkt == 0) return;
+  Bf16Frags fr;
+  ld.issue(0, bf16_a<0>(lds), bf16_b<0>(lds));
+  ld.template store<0>(bf16_a<0>(lds), bf16_b<0>(lds));
+  ld.template store<1>(bf16_a<0>(lds), bf16_b<0>(lds));
+  wait_vmem();
+  lds_barrier();
+  bf16_read_frags<0>(fr, bf16_a<0>(lds), bf16_b<0>(lds), 0, wx, wy, lane);
+  // two K-tiles per trip so that the stages are static; reads past K return zeros,
+  // which are converted into a stage nobody multiplies
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    bf16_ktile<0>(acc, fr, ld, kt, lds, wx, wy, lane);
+    bf16_ktile<1>(acc, fr, ld, kt + 1, lds, wx, wy, lane);
   }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    uint8_t* cur = stage_ptr[kt & 1];
-    uint8_t* nxt = stage_ptr[(kt & 1) ^ 1];
-    if (kt + 1 < nkt) ld.store(nxt, nxt + kTile);
-    if (kt + 2 < nkt) ld.load(kt + 2);
-    bf16_tile_mma(acc, cur, cur + kTile, wx, wy, lane);
-    __syncthreads();
-  }
+  if (kt < nkt) bf16_ktile<0>(acc, fr, ld, kt, lds, wx, wy, lane);
+}
+
+// Byte offset `off` when idx < limit, else an offset past any buffer (top bit set),
+// without a branch (idx, limit < 2^31, off < 2^31).
+__device__ __forceinline__ uint32_t in_range_or_oob(uint32_t off, uint32_t idx, uint32_t limit) {
+  return off | (((limit - 1u - idx) >> 31) << 31);
 }
 
 }  // namespace q4

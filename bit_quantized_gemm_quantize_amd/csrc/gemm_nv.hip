@@ -29,42 +29,53 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
   }
 }
 
+// Per K-tile (64 K) and operand: 256 rows x 2 chunks of 32 codes; thread tid owns
+// chunk c = tid & 1 of rows tid/2 and tid/2 + 128, with the two E4M3 scale bytes of
+// each chunk.  Reads past M / N / K return zeros (buffer range checks).
 struct NvLoader {
-  const uint8_t* ac; const uint8_t* as; const uint8_t* bc; const uint8_t* bs;
-  int64_t M, N, K, m0, n0;
+  __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
+  uint32_t kb, sbytes, nchunk;
   int tid;
   u32x4 ca[2], cb[2];
   uint32_t sa[2], sb[2];
 
-  // chunk (row, c): row = tid/2 + 128 j, c = tid & 1 (two 16-byte code chunks per row)
-  __device__ __forceinline__ void load(int kt) {
-    const int64_t kb = K >> 1, sbytes = K >> 4;
-    const int c = tid & 1;
-    const int64_t blk32 = (int64_t)kt * 2 + c;       // 32-element chunk index along K
-    const bool kok = blk32 < (K >> 5);
+  __device__ __forceinline__ void init(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
+                                       const uint8_t* bs, int64_t M, int64_t N, int64_t K,
+                                       int64_t m0, int64_t n0, int t) {
+    kb = (uint32_t)(K >> 1); sbytes = (uint32_t)(K >> 4); nchunk = (uint32_t)(K >> 5);
+    const uint32_t ra = (uint32_t)min<int64_t>(kBf16BM, M - m0), rb = (uint32_t)min<int64_t>(kBf16BN, N - n0);
+    rca = make_rsrc(ac + m0 * kb, ra * kb);
+    rcb = make_rsrc(bc + n0 * kb, rb * kb);
+    rsa = make_rsrc(as + m0 * sbytes, ra * sbytes);
+    rsb = make_rsrc(bs + n0 * sbytes, rb * sbytes);
+    tid = t;
+  }
+  __device__ __forceinline__ void issue(int kt, uint8_t*, uint8_t*) {
+    const uint32_t chunk = (uint32_t)kt * 2 + (tid & 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row = (tid >> 1) + 128 * j;
-      const bool aok = kok && m0 + row < M, bok = kok && n0 + row < N;
-      ca[j] = aok ? ld16(ac + (m0 + row) * kb + blk32 * 16) : u32x4{0, 0, 0, 0};
-      cb[j] = bok ? ld16(bc + (n0 + row) * kb + blk32 * 16) : u32x4{0, 0, 0, 0};
-      sa[j] = aok ? *reinterpret_cast<const uint16_t*>(as + (m0 + row) * sbytes + 2 * blk32) : 0u;
-      sb[j] = bok ? *reinterpret_cast<const uint16_t*>(bs + (n0 + row) * sbytes + 2 * blk32) : 0u;
+      const uint32_t row = (tid >> 1) + 128 * j;
+      const uint32_t co = in_range_or_oob(row * kb + chunk * 16, chunk, nchunk);
+      const uint32_t so = in_range_or_oob(row * sbytes + chunk * 2, chunk, nchunk);
+      ca[j] = buf_ld16(rca, co);
+      cb[j] = buf_ld16(rcb, co);
+      sa[j] = __builtin_amdgcn_raw_buffer_load_b16(rsa, (int)so, 0, 0);
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rsb, (int)so, 0, 0);
     }
   }
+  // half P: both operands' chunks of row group P
+  template <int P>
   __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb) {
-    const int c = tid & 1;
+    // row (tid >> 1) + 128 P: row & 7 does not depend on P
+    const int c = tid & 1, r = tid >> 1;
+    const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
+    u32x4 o[4];
+    nv_dequant_chunk(ca[P], sa[P], o);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = (tid >> 1) + 128 * j;
-      u32x4 o[4];
-      nv_dequant_chunk(ca[j], sa[j], o);
+    for (int d = 0; d < 4; ++d) st16(la + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
+    nv_dequant_chunk(cb[P], sb[P], o);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) st16(la + lds_chunk_off(row, 4 * c + d), o[d]);
-      nv_dequant_chunk(cb[j], sb[j], o);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) st16(lb + lds_chunk_off(row, 4 * c + d), o[d]);
-    }
+    for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
   }
 };
 
@@ -74,29 +85,31 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ t, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
-  constexpr int kMainLds = 4 * kBf16BM * kBf16RowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainLds > kEpilogueLdsBytes ? kMainLds : kEpilogueLdsBytes];
+  static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;
+  const int64_t m0 = (int64_t)tm * kBf16BM, n0 = (int64_t)tn * kBf16BN;
   NvLoader ld;
-  ld.ac = ac; ld.as = as; ld.bc = bc; ld.bs = bs;
-  ld.M = M; ld.N = N; ld.K = K;
-  ld.m0 = (int64_t)tm * kBf16BM; ld.n0 = (int64_t)tn * kBf16BN;
-  ld.tid = tid;
+  ld.init(ac, as, bc, bs, M, N, K, m0, n0, tid);
   v16f acc[4][4];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
 
+  // the tensor scales multiply the 4-bit product only, before the low-rank term
   const float scale = ats[0] * bts[0];
+  const int64_t n_base = n0 + wy * 128, m_base = m0 + wx * 128;
+  if (R > 0) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) acc[f][g] = acc[f][g] * scale;
-  const int64_t n_base = ld.n0 + wy * 128, m_base = ld.m0 + wx * 128;
-  if (R > 0) lowrank_accumulate<R>(acc, n_base, m_base, M, N, t, l2t, lane);
+      for (int g = 0; g < 4; ++g) acc[f][g] = acc[f][g] * scale;
+    lowrank_accumulate<R>(acc, n_base, m_base, M, N, t, l2t, lane);
+  }
   __syncthreads();                           // all waves are done reading operand tiles
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes,
+                          R > 0 ? 1.0f : scale);
 }
 
 template <int R, bool F32>

@@ -25,55 +25,61 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
   }
 }
 
+// Per K-tile (one quantization group of 64 K): the activation tile (256 rows x 128
+// bytes of bf16) goes straight into LDS, each wave moving rows 64 w .. 64 w + 63 as
+// 8 rows x 128 bytes per instruction (lane i -> row i/8, stored position i%8, which
+// holds global chunk (i%8) ^ (row & 7)); the weight tile is 256 rows x 2 chunks of
+// 32 codes, thread tid owning chunk tid & 1 of rows tid/2 and tid/2 + 128, with each
+// row's (s, z).  Reads past M / N / K return zeros.
 struct W4A16Loader {
-  const uint16_t* x; int64_t ldx;
-  const uint8_t* wc; const uint16_t* ws; const uint16_t* wz;
-  int64_t M, N, K, m0, n0;
+  __amdgpu_buffer_rsrc_t rx, rc, rs, rz;
+  uint32_t ldxb, kb, ngrp;
   int tid;
-  u32x4 xa[8], cb[2];
+  u32x4 cb[2];
   uint32_t sb[2], zb[2];
 
-  __device__ __forceinline__ void load(int kt) {
-    // activations: 256 rows x 8 chunks of 8 bf16; chunk (row, c) with c = tid & 7
-    const int c = tid & 7;
-    const int64_t k = (int64_t)kt * kBf16KT + 8 * c;
-    const bool kxok = k < K;
+  __device__ __forceinline__ void init(const uint16_t* x, int64_t ldx, const uint8_t* wc,
+                                       const uint16_t* ws, const uint16_t* wz, int64_t M,
+                                       int64_t N, int64_t K, int64_t m0, int64_t n0, int t) {
+    ldxb = (uint32_t)(ldx * 2); kb = (uint32_t)(K >> 1); ngrp = (uint32_t)(K >> 6);
+    const uint32_t ra = (uint32_t)min<int64_t>(kBf16BM, M - m0), rb = (uint32_t)min<int64_t>(kBf16BN, N - n0);
+    // the last activation row ends at K, not at ldx
+    rx = make_rsrc(x + m0 * ldx, ra > 0 ? (ra - 1) * ldxb + (uint32_t)(K * 2) : 0);
+    rc = make_rsrc(wc + n0 * kb, rb * kb);
+    rs = make_rsrc(ws + n0 * ngrp, rb * ngrp * 2);
+    rz = make_rsrc(wz + n0 * ngrp, rb * ngrp * 2);
+    tid = t;
+  }
+  __device__ __forceinline__ void issue(int kt, uint8_t* la, uint8_t*) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t lr = lane >> 3, lp = lane & 7;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int row = (tid >> 3) + 32 * j;
-      xa[j] = (kxok && m0 + row < M) ? ld16(x + (m0 + row) * ldx + k) : u32x4{0, 0, 0, 0};
+      const uint32_t row = 64 * wave + 8 * j + lr;         // row & 7 == lr
+      const uint32_t off = in_range_or_oob(row * ldxb + (uint32_t)kt * 128 + ((lp ^ lr) << 4), (uint32_t)kt, ngrp);
+      buf_ld16_lds(rx, la + (64 * wave + 8 * j) * kBf16RowBytes, off);
     }
-    // weights: 256 rows x 2 chunks of 32 codes; one group (s, z) per row
-    const int cw = tid & 1;
-    const int64_t kb = K >> 1, ngrp = K >> 6;
-    const bool kwok = kt < ngrp;
+    const uint32_t cw = tid & 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row = (tid >> 1) + 128 * j;
-      const bool ok = kwok && n0 + row < N;
-      cb[j] = ok ? ld16(wc + (n0 + row) * kb + (int64_t)kt * 32 + 16 * cw) : u32x4{0, 0, 0, 0};
-      sb[j] = ok ? ws[(n0 + row) * ngrp + kt] : 0u;
-      zb[j] = ok ? wz[(n0 + row) * ngrp + kt] : 0u;
+      const uint32_t row = (tid >> 1) + 128 * j;
+      cb[j] = buf_ld16(rc, in_range_or_oob(row * kb + (uint32_t)kt * 32 + cw * 16, (uint32_t)kt, ngrp));
+      const uint32_t go = in_range_or_oob((row * ngrp + (uint32_t)kt) * 2, (uint32_t)kt, ngrp);
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
+      zb[j] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)go, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb) {
-    const int c = tid & 7;
+  // half P: the weight chunk of row tid/2 + 128 P
+  template <int P>
+  __device__ __forceinline__ void store(uint8_t*, uint8_t* lb) {
+    const int cw = tid & 1, r = tid >> 1;
+    const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
+    const float sc = __uint_as_float(sb[P] << 16);
+    const float zs = __uint_as_float(zb[P] << 16) * sc;
+    u32x4 o[4];
+    int4_dequant_chunk(cb[P], sc, zs, o);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = (tid >> 3) + 32 * j;
-      st16(la + lds_chunk_off(row, c), xa[j]);
-    }
-    const int cw = tid & 1;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = (tid >> 1) + 128 * j;
-      const float s = __uint_as_float(sb[j] << 16);
-      const float zs = __uint_as_float(zb[j] << 16) * s;
-      u32x4 o[4];
-      int4_dequant_chunk(cb[j], s, zs, o);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) st16(lb + lds_chunk_off(row, 4 * cw + d), o[d]);
-    }
+    for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * cw + d) ^ (r & 7)) << 4), o[d]);
   }
 };
 
@@ -82,20 +88,18 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
-  constexpr int kMainLds = 4 * kBf16BM * kBf16RowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainLds > kEpilogueLdsBytes ? kMainLds : kEpilogueLdsBytes];
+  static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;
+  const int64_t m0 = (int64_t)tm * kBf16BM, n0 = (int64_t)tn * kBf16BN;
   W4A16Loader ld;
-  ld.x = x; ld.ldx = ldx; ld.wc = wc; ld.ws = ws; ld.wz = wz;
-  ld.M = M; ld.N = N; ld.K = K;
-  ld.m0 = (int64_t)tm * kBf16BM; ld.n0 = (int64_t)tn * kBf16BN;
-  ld.tid = tid;
+  ld.init(x, ldx, wc, ws, wz, M, N, K, m0, n0, tid);
   v16f acc[4][4];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
-  const int64_t n_base = ld.n0 + wy * 128, m_base = ld.m0 + wx * 128;
+  const int64_t n_base = n0 + wy * 128, m_base = m0 + wx * 128;
   __syncthreads();                           // all waves are done reading operand tiles
   epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
 }

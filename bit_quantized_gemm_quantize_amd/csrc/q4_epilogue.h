@@ -114,30 +114,15 @@ constexpr int kStageRowBytes = 144;                         // 128 + 16 bytes of
 constexpr int kStageWaveBytes = 128 * kStageRowBytes;       // 18432
 constexpr int kEpilogueLdsBytes = 4 * kStageWaveBytes;      // for 4 waves
 
+// y = scale * acc + bias.  The scale and the bias are applied pass by pass, so
+// only the accumulators being staged are moved out of the matrix registers.
 template <bool OUT_F32, int F>
 __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
                                                int64_t M, int64_t N,
                                                const uint16_t* __restrict__ bias, void* y,
-                                               int64_t ldy, int lane, uint8_t* stage) {
+                                               int64_t ldy, int lane, uint8_t* stage,
+                                               float scale = 1.0f) {
   const int r32 = lane & 31, h = lane >> 5;
-  // bias, per accumulator group of 4 consecutive columns
-#pragma unroll
-  for (int f = 0; f < F; ++f)
-#pragma unroll
-    for (int vq = 0; vq < 4; ++vq) {
-      const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
-      float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (bias) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[f][g][4 * vq + j] += b[j];
-    }
-
   constexpr int kElem = OUT_F32 ? 4 : 2;
   constexpr int kFPerPass = OUT_F32 ? 1 : 2;     // 32-column accumulator blocks per pass
   constexpr int kPasses = F / kFPerPass;
@@ -154,21 +139,32 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
     for (int fp = 0; fp < kFPerPass; ++fp) {
       const int f = pass * kFPerPass + fp;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int vq = 0; vq < 4; ++vq) {
+        // bias of the 4 consecutive columns this lane holds in register group vq
+        const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
+        float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias) {
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq) {
+          for (int j = 0; j < 4; ++j)
+            if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
           uint8_t* dst = stage + (32 * g + r32) * kStageRowBytes + (32 * fp + 8 * vq + 4 * h) * kElem;
-          const v16f& a = acc[f][g];
+          float a[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a[j] = __builtin_fmaf(acc[f][g][4 * vq + j], scale, b[j]);
           if (OUT_F32) {
-            *reinterpret_cast<v4f*>(dst) = v4f{a[4 * vq], a[4 * vq + 1], a[4 * vq + 2], a[4 * vq + 3]};
+            *reinterpret_cast<v4f*>(dst) = v4f{a[0], a[1], a[2], a[3]};
           } else {
-            const v2bf p0 = {(__bf16)a[4 * vq], (__bf16)a[4 * vq + 1]};
-            const v2bf p1 = {(__bf16)a[4 * vq + 2], (__bf16)a[4 * vq + 3]};
+            const v2bf p0 = {(__bf16)a[0], (__bf16)a[1]};
+            const v2bf p1 = {(__bf16)a[2], (__bf16)a[3]};
             typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
             *reinterpret_cast<u32x2*>(dst) =
                 u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
           }
         }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
