@@ -15,6 +15,11 @@
 // products of matching K indices; its scale for the step is byte s of the lane's
 // 4-byte scale word (the op_sel index), one aligned dword load per fragment.
 //
+// Tail: when the tiles do not fill the last round over the CUs (864 tiles on 256
+// CUs leave 96), the leftover tiles are split in two halves of 128 weight rows,
+// each a workgroup whose waves own 128 x 32, so that the last round is half as
+// long.
+//
 // LDS: the two operand tiles (256 rows x 128 bytes each) are stored with 16-byte
 // chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)), so the 16-byte
 // fragment reads are free of bank conflicts.  Tiles go from HBM/L2 straight into
@@ -32,33 +37,33 @@ constexpr int kKTB = kKT / 2;     // bytes per row per K-tile
 constexpr int kThreads = 512;
 constexpr int kGroupM = 4;
 
-template <int R, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
-    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
-    const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
-    const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
-    int64_t ldy, int tiles_m, int tiles_n) {
-  // LDS: two stages x (activation tile, weight tile) of 256 rows x 128 bytes, then
-  // two stages x (activation, weight) of scale rows (256 rows x 16 bytes: the scale
-  // bytes of two consecutive K-tiles); the epilogue reuses the space for the output
-  constexpr int kCodeLds = 2 * 2 * kBM * kKTB;          // 131072
-  constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
-  constexpr int kMainLds = kCodeLds + kScaleLds;
-  static_assert((kThreads / 64) * kStageWaveBytes <= kMainLds, "the epilogue stages each wave's output in the operand LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
+// LDS: two stages x (activation tile, weight tile) of 256 rows x 128 bytes, then
+// two stages x (activation, weight) of scale rows (256 rows x 16 bytes: the scale
+// bytes of two consecutive K-tiles); the epilogue reuses the space for the output
+constexpr int kCodeLds = 2 * 2 * kBM * kKTB;          // 131072
+constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
+constexpr int kMainLds = kCodeLds + kScaleLds;
+static_assert((kThreads / 64) * kStageWaveBytes <= kMainLds, "the epilogue stages each wave's output in the operand LDS");
+
+// One output tile of 256 activation rows x 128 F weight rows starting at (m0, n0):
+// wave (wm, wn) owns m in [128 wm, +128) and n in [32 F wn, +32 F).
+template <int R, bool OUT_F32, int F>
+__device__ __forceinline__ void mx_tile(
+    uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
+    const float* __restrict__ t, const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
+  constexpr int kTN = 128 * F;                   // weight rows of this tile
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
   auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
 
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, kGroupM, &tm, &tn);
-  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wm = wave & 1;       // wave's n quarter, m half
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t kbytes = (uint32_t)(K >> 1), nblk = (uint32_t)(K >> 5);
   const int nkt = (int)((K + kKT - 1) / kKT);
-  const uint32_t rows_a = (uint32_t)min<int64_t>(kBM, M - m0), rows_b = (uint32_t)min<int64_t>(kBN, N - n0);
+  const uint32_t rows_a = (uint32_t)min<int64_t>(kBM, M - m0), rows_b = (uint32_t)min<int64_t>(kTN, N - n0);
 
   // buffer views of this tile's rows: rows past M / N read as zero
   const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
@@ -68,18 +73,20 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
 
   // codes, global -> LDS: each wave moves 8 rows x 128 bytes per instruction straight
   // into LDS (lane i -> row i/8, stored position i%8, which holds global chunk
-  // (i%8) ^ (row & 7), the swizzle).  Wave w covers rows 32 w .. 32 w + 31 of
-  // each operand.
+  // (i%8) ^ (row & 7), the swizzle).  Wave w covers activation rows 32 w .. +31 and
+  // weight rows 16 F w .. +16 F - 1.
   const int lr = lane >> 3, lp = lane & 7;
   auto gload = [&](int kt, int stage, int operand) {
     const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
     const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
     const auto rc = operand == 0 ? rc_a : rc_b;
+    const int per = operand == 0 ? 32 : 16 * F;              // rows per wave
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t row = 32 * wave + 8 * j + lr;
+      if (operand == 1 && j >= 2 * F) break;
+      const uint32_t row = per * wave + 8 * j + lr;
       // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
-      buf_ld16_lds(rc, &lds[stage][operand][(32 * wave + 8 * j) * kKTB], row * kbytes + koff);
+      buf_ld16_lds(rc, &lds[stage][operand][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
     }
   };
   // scales, global -> LDS: waves 0-3 take the activation rows, waves 4-7 the weight
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     buf_ld16_lds(rs_op, &lsc[stage][sop][64 * sw * 16], off);
   };
   // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3
-  uint32_t sa[4], sb[2], sa_n[4], sb_n[2];
+  uint32_t sa[4], sb[F], sa_n[4], sb_n[F];
   auto read_scales = [&](int kt, int stage, uint32_t* xa, uint32_t* xb) {
     const bool kin = (uint32_t)kt * 8 + 4 * h < nblk;      // past K: codes are 0; keep 2**0
 #pragma unroll
@@ -103,14 +110,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
       xa[g] = kin ? v : 0x7F7F7F7Fu;
     }
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 64 + 32 * f + r32) * 16 + 4 * h]);
+    for (int f = 0; f < F; ++f) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 32 * F + 32 * f + r32) * 16 + 4 * h]);
       xb[f] = kin ? v : 0x7F7F7F7Fu;
     }
   };
 
   // fragment registers, double-buffered across MFMA steps
-  u32x4 fa[2][4], fb[2][2];
+  u32x4 fa[2][4], fb[2][F];
   auto read_frags = [&](int buf, int stage, int s) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -118,20 +125,20 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
       fa[buf][g] = ld16(&lds[stage][0][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int row = wn * 64 + 32 * f + r32;
+    for (int f = 0; f < F; ++f) {
+      const int row = wn * 32 * F + 32 * f + r32;
       fb[buf][f] = ld16(&lds[stage][1][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
   };
 
-  v16f acc[2][4];
+  v16f acc[F][4];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
 #define Q4_MX_MMA(S, BUF)                                                                       \
-  _Pragma("unroll") for (int f = 0; f < 2; ++f)                                                 \
+  _Pragma("unroll") for (int f = 0; f < F; ++f)                                                 \
     _Pragma("unroll") for (int g = 0; g < 4; ++g)                                               \
       acc[f][g] = mfma_fp4_32x32x64<S, S>(fb[BUF][f], fa[BUF][g], acc[f][g], (int)sb[f],       \
                                           (int)sa[g]);
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   __builtin_amdgcn_sched_group_barrier(0x100, NREADS, 0); \
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 
-  const int64_t n_base = n0 + wn * 64, m_base = m0 + wm * 128;
+  const int64_t n_base = n0 + wn * 32 * F, m_base = m0 + wm * 128;
   if (nkt > 0) {
     gload(0, 0, 0);
     gload(0, 0, 1);
@@ -158,14 +165,17 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
 #pragma unroll
     for (int j = 0; j < R / 8; ++j)              // kBM * 4R bytes in 1 KB pieces
       buf_ld16_lds(rt, lt + (wave * (R / 8) + j) * 1024, (wave * (R / 8) + j) * 1024 + lane * 16);
+    constexpr int kPieces = kTN * 2 * R / 1024;  // kTN * 2R bytes
 #pragma unroll
-    for (int j = 0; j < R / 16; ++j)             // kBN * 2R bytes
-      buf_ld16_lds(rl, ll + (wave * (R / 16) + j) * 1024, (wave * (R / 16) + j) * 1024 + lane * 16);
+    for (int j = 0; j < (kPieces + 7) / 8; ++j) {
+      const int piece = j * 8 + wave;
+      if (piece < kPieces) buf_ld16_lds(rl, ll + piece * 1024, piece * 1024 + lane * 16);
+    }
   }
   wait_vmem();
   __syncthreads();
   if (R > 0) {
-    lowrank_accumulate_lds<R>(acc, &lds[1][0][0], &lds[1][0][0] + kBM * 4 * R, 128 * wm, 64 * wn, lane);
+    lowrank_accumulate_lds<R>(acc, &lds[1][0][0], &lds[1][0][0] + kBM * 4 * R, 128 * wm, 32 * F * wn, lane);
     lds_barrier();                           // stage 1 is free again for K-tile 1
   }
   if (nkt > 0) {
@@ -225,12 +235,45 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds_raw + wave * kStageWaveBytes);
 }
 
+// Workgroups [0, full) take whole tiles; the rest take halves of the leftover tiles
+// (tile full + q/2, weight rows 128 (q % 2) .. +127).
+template <int R, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
+    const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
+    const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
+    int64_t ldy, int tiles_m, int tiles_n, int full) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (bid < full) {
+    tile_of(bid, tiles_m, tiles_n, kGroupM, &tm, &tn);
+    mx_tile<R, OUT_F32, 2>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,
+                           (int64_t)tn * kBN);
+  } else {
+    const int q = bid - full;
+    tile_of(full + (q >> 1), tiles_m, tiles_n, kGroupM, &tm, &tn);
+    mx_tile<R, OUT_F32, 1>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,
+                           (int64_t)tn * kBN + 128 * (q & 1));
+  }
+}
+
 template <int R, bool F32>
 static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                   int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_mx_kernel<R, F32>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, ac, as,
-                     bc, bs, M, N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+  const int tiles = tiles_m * tiles_n;
+  // leftover tiles of the last round over the CUs run as halves when that fits
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+  }
+  const int rem = tiles % cus;
+  const int full = (tiles > cus && rem > 0 && 2 * rem <= cus) ? tiles - rem : tiles;
+  const int grid = full + 2 * (tiles - full);
+  hipLaunchKernelGGL((gemm_mx_kernel<R, F32>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M, N,
+                     K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
 }
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,

@@ -124,9 +124,12 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
                                                float scale = 1.0f) {
   const int r32 = lane & 31, h = lane >> 5;
   constexpr int kElem = OUT_F32 ? 4 : 2;
-  constexpr int kFPerPass = OUT_F32 ? 1 : 2;     // 32-column accumulator blocks per pass
+  constexpr int kFPerPass = (OUT_F32 || F == 1) ? 1 : 2;   // 32-column blocks per pass
   constexpr int kPasses = F / kFPerPass;
-  constexpr int kColsPerPass = 32 * kFPerPass;   // 128 bytes of output per row
+  constexpr int kColsPerPass = 32 * kFPerPass;
+  constexpr int kRowBytes = kColsPerPass * kElem;  // 128 (or 64: bf16 with F = 1)
+  constexpr int kLanesPerRow = kRowBytes / 16;
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
   constexpr int kPer16 = 16 / kElem;             // elements per 16-byte store
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
@@ -168,12 +171,12 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    // LDS -> global: 8 lanes per row (16 bytes each), 8 rows per instruction
-    const int col_bytes = (lane & 7) * 16;
+    // LDS -> global: kLanesPerRow lanes per row (16 bytes each), whole row segments
+    const int col_bytes = (lane % kLanesPerRow) * 16;
     const int64_t n = n_base + pass * kColsPerPass + col_bytes / kElem;
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int ml = 8 * it + (lane >> 3);
+    for (int it = 0; it < 128 / kRowsPerStore; ++it) {
+      const int ml = kRowsPerStore * it + lane / kLanesPerRow;
       const int64_t m = m_base + ml;
       const u32x4 v = ld16(stage + ml * kStageRowBytes + col_bytes);
       if (m < M) {

@@ -159,6 +159,21 @@ def test_gemm_deterministic():
     assert np.array_equal(y1, y2)
 
 
+def test_gemm_mx_leftover_tiles_as_halves():
+    """More 256 x 256 tiles than one round over the CUs (17 x 16 = 272 on 256 CUs):
+    the leftover tiles run as two halves of 128 weight rows each.  Ragged M and N,
+    rank-32 branch and bias, every element checked."""
+    dev = device()
+    M, N, K = 4335, 4024, 256
+    d = synth.mlp_up_svd(seed=10, M=M, K=K, N=N, rank=32)
+    bias = synth.bias(N, seed=11)
+    for f32 in (True, False):
+        say(f"gemm_w4a4_lowrank mxfp4 leftover tiles M={M} N={N} K={K} f32={f32}")
+        y = run_w4a4("mxfp4", d["x"], d["rt"], dev, bias=bias, f32=f32, l1=d["l1"], l2=d["l2"])
+        y_ref, bound = ref_w4a4("mxfp4", d["x"], d["rt"], bias=bias, l1=d["l1"], l2=d["l2"])
+        _check(y, y_ref, bound, not f32, f"leftover tiles {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------------ full layer sizes
 def test_full_mlp_up_svd_layer_sampled_rows():
     """The benchmarked configuration: M=4608, K=3072, N=12288, rank 32, bf16 output,
