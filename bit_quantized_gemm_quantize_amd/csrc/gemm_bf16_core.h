@@ -1,7 +1,9 @@
 // Main loop of the bf16-MFMA GEMMs (the exact NVFP4 path and the W4A16 path).
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), 128 x 128 per
-// wave as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16.  K advances in tiles of 64
+// wave as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16; or, to fill the CUs when tiles
+// are few, half tiles of 256 x 128 (128 x 64 per wave, F = 2 weight sub-tiles
+// instead of 4).  K advances in tiles of 64
 // elements: each operand tile is 256 rows x 64 bf16 (128 bytes per row) in LDS,
 // 16-byte chunks XOR-swizzled by row, two stages, one barrier per K-tile.
 //
@@ -31,31 +33,32 @@ __device__ __forceinline__ int lds_chunk_off(int row, int chunk) {
   return row * kBf16RowBytes + ((chunk ^ (row & 7)) << 4);
 }
 
+template <int F>
 struct Bf16Frags {
-  u32x4 a[2][4], b[2][4];
+  u32x4 a[2][4], b[2][F];
 };
 
 // fragments of MFMA step s (16 K) of the tile at la / lb into buffer BUF.  Rows
 // 32 g + r32 all have row & 7 == lane & 7, so one swizzled chunk offset per step
 // serves every sub-tile; the sub-tiles are 4 KB apart.
-template <int BUF>
-__device__ __forceinline__ void bf16_read_frags(Bf16Frags& fr, const uint8_t* la, const uint8_t* lb,
+template <int BUF, int F>
+__device__ __forceinline__ void bf16_read_frags(Bf16Frags<F>& fr, const uint8_t* la, const uint8_t* lb,
                                                 int s, int wx, int wy, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
   const int chunk = ((2 * s + h) ^ (lane & 7)) << 4;
   const uint8_t* pa = la + (wx * 128 + r32) * kBf16RowBytes + chunk;
-  const uint8_t* pb = lb + (wy * 128 + r32) * kBf16RowBytes + chunk;
+  const uint8_t* pb = lb + (wy * 32 * F + r32) * kBf16RowBytes + chunk;
 #pragma unroll
   for (int g = 0; g < 4; ++g) fr.a[BUF][g] = ld16(pa + g * 32 * kBf16RowBytes);
 #pragma unroll
-  for (int f = 0; f < 4; ++f) fr.b[BUF][f] = ld16(pb + f * 32 * kBf16RowBytes);
+  for (int f = 0; f < F; ++f) fr.b[BUF][f] = ld16(pb + f * 32 * kBf16RowBytes);
 }
 
 // acc[f][g] holds D[n][m] (A operand = weight rows, B operand = activation rows).
-template <int BUF>
-__device__ __forceinline__ void bf16_mma(v16f (&acc)[4][4], const Bf16Frags& fr) {
+template <int BUF, int F>
+__device__ __forceinline__ void bf16_mma(v16f (&acc)[F][4], const Bf16Frags<F>& fr) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = mfma_bf16_32x32x16(fr.b[BUF][f], fr.a[BUF][g], acc[f][g]);
 }
@@ -69,54 +72,68 @@ template <int ST>
 __device__ __forceinline__ uint8_t* bf16_b(uint8_t* lds) { return lds + (2 + ST) * kBf16TileBytes; }
 
 // One K-tile: multiply stage CUR while tile kt+1 is read and converted into the other.
-template <int CUR, class Loader>
-__device__ __forceinline__ void bf16_ktile(v16f (&acc)[4][4], Bf16Frags& fr, Loader& ld, int kt,
+template <int CUR, int F, class Loader>
+__device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, Loader& ld, int kt,
                                            uint8_t* lds, int wx, int wy, int lane) {
   constexpr int NXT = CUR ^ 1;
   ld.issue(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
-  bf16_read_frags<1>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
-  bf16_mma<0>(acc, fr);
+  bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
+  bf16_mma<0, F>(acc, fr);
   __builtin_amdgcn_sched_barrier(0);
-  bf16_read_frags<0>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
-  bf16_mma<1>(acc, fr);
+  bf16_read_frags<0, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
+  bf16_mma<1, F>(acc, fr);
   __builtin_amdgcn_sched_barrier(0);
-  bf16_read_frags<1>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
+  bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
   ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
-  bf16_mma<0>(acc, fr);
+  bf16_mma<0, F>(acc, fr);
   __builtin_amdgcn_sched_barrier(0);
   ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
-  bf16_mma<1>(acc, fr);
+  bf16_mma<1, F>(acc, fr);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmem();                               // loads straight into LDS have landed
   // every wave has written stage NXT and finished reading stage CUR
   lds_barrier();
-  bf16_read_frags<0>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
+  bf16_read_frags<0, F>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
 }
 
-template <class Loader>
-__device__ __forceinline__ void bf16_mainloop(v16f (&acc)[4][4], Loader& ld, int64_t K, uint8_t* lds,
+template <int F, class Loader>
+__device__ __forceinline__ void bf16_mainloop(v16f (&acc)[F][4], Loader& ld, int64_t K, uint8_t* lds,
                                               int wx, int wy, int lane) {
   const int nkt = (int)((K + kBf16KT - 1) / kBf16KT);
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
   if (nkt == 0) return;
-  Bf16Frags fr;
+  Bf16Frags<F> fr;
   ld.issue(0, bf16_a<0>(lds), bf16_b<0>(lds));
   ld.template store<0>(bf16_a<0>(lds), bf16_b<0>(lds));
   ld.template store<1>(bf16_a<0>(lds), bf16_b<0>(lds));
   wait_vmem();
   lds_barrier();
-  bf16_read_frags<0>(fr, bf16_a<0>(lds), bf16_b<0>(lds), 0, wx, wy, lane);
+  bf16_read_frags<0, F>(fr, bf16_a<0>(lds), bf16_b<0>(lds), 0, wx, wy, lane);
   // two K-tiles per trip so that the stages are static; reads past K return zeros,
   // which are converted into a stage nobody multiplies
   int kt = 0;
   for (; kt + 1 < nkt; kt += 2) {
-    bf16_ktile<0>(acc, fr, ld, kt, lds, wx, wy, lane);
-    bf16_ktile<1>(acc, fr, ld, kt + 1, lds, wx, wy, lane);
+    bf16_ktile<0, F>(acc, fr, ld, kt, lds, wx, wy, lane);
+    bf16_ktile<1, F>(acc, fr, ld, kt + 1, lds, wx, wy, lane);
   }
-  if (kt < nkt) bf16_ktile<0>(acc, fr, ld, kt, lds, wx, wy, lane);
+  if (kt < nkt) bf16_ktile<0, F>(acc, fr, ld, kt, lds, wx, wy, lane);
+}
+
+// Output tiles: the 256 x 256 tiles that do not fill a last round over the CUs
+// (rem of them) run as two halves of 128 weight rows when that fits: workgroups
+// [0, full) take whole tiles, the rest halves (tile full + q/2, half q % 2).
+__host__ inline void bf16_tile_split(int tiles, int* full, int* grid) {
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+  }
+  const int rem = tiles % cus;
+  *full = (rem > 0 && 2 * rem <= cus) ? tiles - rem : tiles;
+  *grid = *full + 2 * (tiles - *full);
 }
 
 // Byte offset `off` when idx < limit, else an offset past any buffer (top bit set),

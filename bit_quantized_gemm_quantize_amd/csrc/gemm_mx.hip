@@ -63,7 +63,7 @@ __device__ __forceinline__ void mx_tile(
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t kbytes = (uint32_t)(K >> 1), nblk = (uint32_t)(K >> 5);
   const int nkt = (int)((K + kKT - 1) / kKT);
-  const uint32_t rows_a = (uint32_t)min<int64_t>(kBM, M - m0), rows_b = (uint32_t)min<int64_t>(kTN, N - n0);
+  const uint32_t rows_a = rows_in(kBM, M, m0), rows_b = rows_in(kTN, N, n0);
 
   // buffer views of this tile's rows: rows past M / N read as zero
   const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
@@ -253,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   } else {
     const int q = bid - full;
     tile_of(full + (q >> 1), tiles_m, tiles_n, kGroupM, &tm, &tn);
+    if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
     mx_tile<R, OUT_F32, 1>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,
                            (int64_t)tn * kBN + 128 * (q & 1));
   }

@@ -29,9 +29,11 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
   }
 }
 
-// Per K-tile (64 K) and operand: 256 rows x 2 chunks of 32 codes; thread tid owns
-// chunk c = tid & 1 of rows tid/2 and tid/2 + 128, with the two E4M3 scale bytes of
-// each chunk.  Reads past M / N / K return zeros (buffer range checks).
+// Per K-tile (64 K) and operand: 256 (weights: TN) rows x 2 chunks of 32 codes;
+// thread tid owns chunk c = tid & 1 of rows tid/2 and tid/2 + 128, with the two
+// E4M3 scale bytes of each chunk.  Reads past M / N / K return zeros (buffer range
+// checks).
+template <int TN>
 struct NvLoader {
   __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
   uint32_t kb, sbytes, nchunk;
@@ -43,7 +45,7 @@ struct NvLoader {
                                        const uint8_t* bs, int64_t M, int64_t N, int64_t K,
                                        int64_t m0, int64_t n0, int t) {
     kb = (uint32_t)(K >> 1); sbytes = (uint32_t)(K >> 4); nchunk = (uint32_t)(K >> 5);
-    const uint32_t ra = (uint32_t)min<int64_t>(kBf16BM, M - m0), rb = (uint32_t)min<int64_t>(kBf16BN, N - n0);
+    const uint32_t ra = rows_in(kBf16BM, M, m0), rb = rows_in(TN, N, n0);
     rca = make_rsrc(ac + m0 * kb, ra * kb);
     rcb = make_rsrc(bc + n0 * kb, rb * kb);
     rsa = make_rsrc(as + m0 * sbytes, ra * sbytes);
@@ -58,9 +60,11 @@ struct NvLoader {
       const uint32_t co = in_range_or_oob(row * kb + chunk * 16, chunk, nchunk);
       const uint32_t so = in_range_or_oob(row * sbytes + chunk * 2, chunk, nchunk);
       ca[j] = buf_ld16(rca, co);
-      cb[j] = buf_ld16(rcb, co);
       sa[j] = __builtin_amdgcn_raw_buffer_load_b16(rsa, (int)so, 0, 0);
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rsb, (int)so, 0, 0);
+      if (j < TN / 128) {
+        cb[j] = buf_ld16(rcb, co);
+        sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rsb, (int)so, 0, 0);
+      }
     }
   }
   // half P: both operands' chunks of row group P
@@ -73,36 +77,35 @@ struct NvLoader {
     nv_dequant_chunk(ca[P], sa[P], o);
 #pragma unroll
     for (int d = 0; d < 4; ++d) st16(la + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
-    nv_dequant_chunk(cb[P], sb[P], o);
+    if (P < TN / 128) {
+      nv_dequant_chunk(cb[P], sb[P], o);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
+      for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
+    }
   }
 };
 
-template <int R, bool OUT_F32>
-__global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
-    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
-    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
-    int64_t M, int64_t N, int64_t K, const float* __restrict__ t, const uint16_t* __restrict__ l2t,
-    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
-  static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+// One output tile of 256 activation rows x 64 F weight rows at (m0, n0).
+template <int R, bool OUT_F32, int F>
+__device__ __forceinline__ void nv_tile(
+    uint8_t* lds, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    const float* __restrict__ ats, const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs,
+    const float* __restrict__ bts, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
+    const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
+    int64_t ldy, int64_t m0, int64_t n0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;
-  const int64_t m0 = (int64_t)tm * kBf16BM, n0 = (int64_t)tn * kBf16BN;
-  NvLoader ld;
+  NvLoader<64 * F> ld;
   ld.init(ac, as, bc, bs, M, N, K, m0, n0, tid);
-  v16f acc[4][4];
+  v16f acc[F][4];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
 
   // the tensor scales multiply the 4-bit product only, before the low-rank term
   const float scale = ats[0] * bts[0];
-  const int64_t n_base = n0 + wy * 128, m_base = m0 + wx * 128;
+  const int64_t n_base = n0 + wy * 32 * F, m_base = m0 + wx * 128;
   if (R > 0) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < F; ++f)
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[f][g] = acc[f][g] * scale;
     lowrank_accumulate<R>(acc, n_base, m_base, M, N, t, l2t, lane);
@@ -112,14 +115,41 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
                           R > 0 ? 1.0f : scale);
 }
 
+// Workgroups [0, full) take whole 256 x 256 tiles, the rest halves of the leftover
+// tiles (256 x 128).
+template <int R, bool OUT_F32>
+__global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ t, const uint16_t* __restrict__ l2t,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
+    int full) {
+  static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (bid < full) {
+    tile_of(bid, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+    nv_tile<R, OUT_F32, 4>(lds, ac, as, ats, bc, bs, bts, M, N, K, t, l2t, bias, y, ldy,
+                           (int64_t)tm * kBf16BM, (int64_t)tn * kBf16BN);
+  } else {
+    const int q = bid - full;
+    tile_of(full + (q >> 1), tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+    if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
+    nv_tile<R, OUT_F32, 2>(lds, ac, as, ats, bc, bs, bts, M, N, K, t, l2t, bias, y, ldy,
+                           (int64_t)tm * kBf16BM, (int64_t)tn * kBf16BN + 128 * (q & 1));
+  }
+}
+
 template <int R, bool F32>
 static void queue(const uint8_t* ac, const uint8_t* as, const float* ats, const uint8_t* bc,
                   const uint8_t* bs, const float* bts, int64_t M, int64_t N, int64_t K,
                   const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kBf16BM - 1) / kBf16BM), tiles_n = (int)((N + kBf16BN - 1) / kBf16BN);
-  hipLaunchKernelGGL((gemm_nv_kernel<R, F32>), dim3(tiles_m * tiles_n), dim3(kBf16Threads), 0, s,
-                     ac, as, ats, bc, bs, bts, M, N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m,
-                     tiles_n);
+  int full, grid;
+  bf16_tile_split(tiles_m * tiles_n, &full, &grid);
+  hipLaunchKernelGGL((gemm_nv_kernel<R, F32>), dim3(grid), dim3(kBf16Threads), 0, s, ac, as, ats, bc,
+                     bs, bts, M, N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
 }
 
 hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats,

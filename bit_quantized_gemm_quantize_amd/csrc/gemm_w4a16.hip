@@ -28,9 +28,10 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
 // Per K-tile (one quantization group of 64 K): the activation tile (256 rows x 128
 // bytes of bf16) goes straight into LDS, each wave moving rows 64 w .. 64 w + 63 as
 // 8 rows x 128 bytes per instruction (lane i -> row i/8, stored position i%8, which
-// holds global chunk (i%8) ^ (row & 7)); the weight tile is 256 rows x 2 chunks of
-// 32 codes, thread tid owning chunk tid & 1 of rows tid/2 and tid/2 + 128, with each
-// row's (s, z).  Reads past M / N / K return zeros.
+// holds global chunk (i%8) ^ (row & 7)); the weight tile is TN rows x 2 chunks of
+// 32 codes, thread tid owning chunk tid & 1 of rows tid/2 (and tid/2 + 128), with
+// each row's (s, z).  Reads past M / N / K return zeros.
+template <int TN>
 struct W4A16Loader {
   __amdgpu_buffer_rsrc_t rx, rc, rs, rz;
   uint32_t ldxb, kb, ngrp;
@@ -42,7 +43,7 @@ struct W4A16Loader {
                                        const uint16_t* ws, const uint16_t* wz, int64_t M,
                                        int64_t N, int64_t K, int64_t m0, int64_t n0, int t) {
     ldxb = (uint32_t)(ldx * 2); kb = (uint32_t)(K >> 1); ngrp = (uint32_t)(K >> 6);
-    const uint32_t ra = (uint32_t)min<int64_t>(kBf16BM, M - m0), rb = (uint32_t)min<int64_t>(kBf16BN, N - n0);
+    const uint32_t ra = rows_in(kBf16BM, M, m0), rb = rows_in(TN, N, n0);
     // the last activation row ends at K, not at ldx
     rx = make_rsrc(x + m0 * ldx, ra > 0 ? (ra - 1) * ldxb + (uint32_t)(K * 2) : 0);
     rc = make_rsrc(wc + n0 * kb, rb * kb);
@@ -61,7 +62,7 @@ struct W4A16Loader {
     }
     const uint32_t cw = tid & 1;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TN / 128; ++j) {
       const uint32_t row = (tid >> 1) + 128 * j;
       cb[j] = buf_ld16(rc, in_range_or_oob(row * kb + (uint32_t)kt * 32 + cw * 16, (uint32_t)kt, ngrp));
       const uint32_t go = in_range_or_oob((row * ngrp + (uint32_t)kt) * 2, (uint32_t)kt, ngrp);
@@ -72,6 +73,7 @@ struct W4A16Loader {
   // half P: the weight chunk of row tid/2 + 128 P
   template <int P>
   __device__ __forceinline__ void store(uint8_t*, uint8_t* lb) {
+    if (P >= TN / 128) return;
     const int cw = tid & 1, r = tid >> 1;
     const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
     const float sc = __uint_as_float(sb[P] << 16);
@@ -83,37 +85,60 @@ struct W4A16Loader {
   }
 };
 
+// One output tile of 256 activation rows x 64 F weight rows at (m0, n0).
+template <bool OUT_F32, int F>
+__device__ __forceinline__ void w4a16_tile(
+    uint8_t* lds, const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
+    const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
+  W4A16Loader<64 * F> ld;
+  ld.init(x, ldx, wc, ws, wz, M, N, K, m0, n0, tid);
+  v16f acc[F][4];
+  bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
+  const int64_t n_base = n0 + wy * 32 * F, m_base = m0 + wx * 128;
+  __syncthreads();                           // all waves are done reading operand tiles
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
+}
+
+// Workgroups [0, full) take whole 256 x 256 tiles, the rest halves of the leftover
+// tiles (256 x 128).
 template <bool OUT_F32>
 __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
-    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
+    int full) {
   static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
+  const int bid = blockIdx.x;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wy = wave >> 1, wx = wave & 1;
-  const int64_t m0 = (int64_t)tm * kBf16BM, n0 = (int64_t)tn * kBf16BN;
-  W4A16Loader ld;
-  ld.init(x, ldx, wc, ws, wz, M, N, K, m0, n0, tid);
-  v16f acc[4][4];
-  bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
-  const int64_t n_base = n0 + wy * 128, m_base = m0 + wx * 128;
-  __syncthreads();                           // all waves are done reading operand tiles
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
+  if (bid < full) {
+    tile_of(bid, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+    w4a16_tile<OUT_F32, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
+                           (int64_t)tn * kBf16BN);
+  } else {
+    const int q = bid - full;
+    tile_of(full + (q >> 1), tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+    if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
+    w4a16_tile<OUT_F32, 2>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
+                           (int64_t)tn * kBf16BN + 128 * (q & 1));
+  }
 }
 
 hipError_t launch_gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* wc,
                              const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                              int64_t K, const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kBf16BM - 1) / kBf16BM), tiles_n = (int)((N + kBf16BN - 1) / kBf16BN);
+  int full, grid;
+  bf16_tile_split(tiles_m * tiles_n, &full, &grid);
   if (ep.out_f32)
-    hipLaunchKernelGGL(gemm_w4a16_kernel<true>, dim3(tiles_m * tiles_n), dim3(kBf16Threads), 0, s, x,
-                       ldx, wc, ws, wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+    hipLaunchKernelGGL(gemm_w4a16_kernel<true>, dim3(grid), dim3(kBf16Threads), 0, s, x, ldx, wc, ws,
+                       wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
   else
-    hipLaunchKernelGGL(gemm_w4a16_kernel<false>, dim3(tiles_m * tiles_n), dim3(kBf16Threads), 0, s, x,
-                       ldx, wc, ws, wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+    hipLaunchKernelGGL(gemm_w4a16_kernel<false>, dim3(grid), dim3(kBf16Threads), 0, s, x, ldx, wc, ws,
+                       wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
   return hipGetLastError();
 }
 

@@ -134,6 +134,13 @@ namespace q4 {
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3
 
+// Rows of a tile that lie inside the matrix: total - start clamped to [0, limit]
+// (a half tile can start past the last row of a ragged matrix).
+__device__ __forceinline__ uint32_t rows_in(int64_t limit, int64_t total, int64_t start) {
+  const int64_t r = total - start;
+  return (uint32_t)(r < 0 ? 0 : (r > limit ? limit : r));
+}
+
 // base and bytes must be the same in every lane; they are moved to scalar registers
 // explicitly, since a descriptor the compiler keeps in vector registers turns every
 // access through it into a loop over lanes.
