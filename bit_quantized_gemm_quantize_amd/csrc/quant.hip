@@ -318,18 +318,13 @@ __global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restric
 }
 
 // Asymmetric int4, group 64: s = bf16(fp32(hi - lo) / 15) (1 if 0),
-// z = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).
-__global__ __launch_bounds__(256) void pack_int4_kernel(const uint16_t* __restrict__ w, int64_t K,
-                                                        int64_t N, int64_t sk, int64_t sn,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint16_t* __restrict__ scales,
-                                                        uint16_t* __restrict__ zeros) {
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// z = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15).  v holds the
+// 64 bf16 values of group g of column n (element 2j in the low half of v[j]).
+__device__ __forceinline__ void int4_encode_group(const uint32_t* v, int64_t n, int64_t g, int64_t K,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint16_t* __restrict__ scales,
+                                                  uint16_t* __restrict__ zeros) {
   const int64_t ngrp = K >> 6;
-  if (q >= N * ngrp) return;
-  const int64_t n = q % N, g = q / N;
-  uint32_t v[32];
-  load_strided(w, g * 64, n, sk, sn, 64, v);
   float lo = 0.0f, hi = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
@@ -362,9 +357,58 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const uint16_t* __restri
   zeros[n * ngrp + g] = (uint16_t)f32_to_bf16_rne(z + 0.0f);   // never -0
 }
 
+// Any strides: one thread per (column n, group); consecutive threads take
+// consecutive n, so a [K, N] row-major weight is read coalesced.
+__global__ __launch_bounds__(256) void pack_int4_kernel(const uint16_t* __restrict__ w, int64_t K,
+                                                        int64_t N, int64_t sk, int64_t sn,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint16_t* __restrict__ scales,
+                                                        uint16_t* __restrict__ zeros) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t ngrp = K >> 6;
+  if (q >= N * ngrp) return;
+  const int64_t n = q % N, g = q / N;
+  uint32_t v[32];
+  load_strided(w, g * 64, n, sk, sn, 64, v);
+  int4_encode_group(v, n, g, K, codes, scales, zeros);
+}
+
+// K-contiguous weight ([N, K], nn.Linear layout): one thread per (n, group),
+// consecutive threads along K, 128 contiguous bytes per thread in 16-byte loads.
+__global__ __launch_bounds__(256) void pack_int4_rows_kernel(const uint16_t* __restrict__ w,
+                                                             int64_t K, int64_t N, int64_t sn,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint16_t* __restrict__ scales,
+                                                             uint16_t* __restrict__ zeros) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t ngrp = K >> 6;
+  if (q >= N * ngrp) return;
+  const int64_t n = q / ngrp, g = q % ngrp;
+  const uint16_t* src = w + n * sn + g * 64;
+  uint32_t v[32];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 x = ld16(src + 8 * j);
+    v[4 * j] = x[0]; v[4 * j + 1] = x[1]; v[4 * j + 2] = x[2]; v[4 * j + 3] = x[3];
+  }
+  int4_encode_group(v, n, g, K, codes, scales, zeros);
+}
+
 hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N, int64_t sk,
                                int64_t sn, uint8_t* codes, void* scales, uint16_t* zeros,
                                float* tensor_scale, hipStream_t s) {
+  // K-contiguous rows with 16-byte alignment: the rows of W^T are quantized exactly
+  // like activation rows (same blocks along K, same encoders), with vector loads
+  const bool rows = sk == 1 && sn % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+  if (rows && fmt != 2)
+    return launch_quantize_act(fmt, w, N, K, sn, codes, static_cast<uint8_t*>(scales), tensor_scale,
+                               nullptr, 0, nullptr, s);
+  if (rows) {
+    const int64_t work = N * (K >> 6);
+    hipLaunchKernelGGL(pack_int4_rows_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, w,
+                       K, N, sn, codes, static_cast<uint16_t*>(scales), zeros);
+    return hipGetLastError();
+  }
   if (fmt == 2) {
     const int64_t work = N * (K >> 6);
     hipLaunchKernelGGL(pack_int4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, w, K,
