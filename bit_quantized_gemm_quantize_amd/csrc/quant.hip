@@ -3,7 +3,7 @@
 //
 // Activation pass (one read of X):
 //   * a workgroup owns up to 32 rows (as many as spread M evenly over the CUs) and
-//     all of K; its 8 waves stride over K in pairs of 32-element blocks, so a lane
+//     all of K; its 16 waves stride over K in pairs of 32-element blocks, so a lane
 //     (row l%32, half l/32) owns one whole block per step: 64 contiguous bytes of X
 //     in, 16 bytes of codes and its scale out.  The block maximum therefore needs
 //     no cross-lane exchange.
@@ -19,7 +19,7 @@
 
 namespace q4 {
 
-constexpr int kQWaves = 8;
+constexpr int kQWaves = 16;
 constexpr int kQRows = 32;
 constexpr float kNvTensorDiv = 2688.0f;   // 6 (largest E2M1) * 448 (largest E4M3)
 
@@ -95,11 +95,11 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
 }
 
 // A workgroup owns `rows` (<= 32) consecutive rows and all of K; rows is chosen
-// so the workgroups spread evenly over the CUs (lanes past it idle).  Each of the 8
-// waves takes every 8th pair of blocks, keeping the X bytes of three pairs in
+// so the workgroups spread evenly over the CUs (lanes past it idle).  Each of the 16
+// waves takes every 16th pair of blocks, keeping the X bytes of three pairs in
 // flight per lane.
 template <int FMT, int R>
-__global__ __launch_bounds__(512) void quant_act_kernel(
+__global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int rows,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax_t,
     const uint16_t* __restrict__ l1t, float* __restrict__ t) {
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(512) void quant_act_kernel(
     for (int v = 0; v < 16; ++v) red[wave * 1024 + acc_row(v, lane) * 32 + i] = acc[v];
     __syncthreads();
     constexpr int kR = R > 0 ? R : 1;
-    for (int idx = threadIdx.x; idx < 32 * R; idx += 512) {
+    for (int idx = threadIdx.x; idx < 32 * R; idx += kQWaves * 64) {
       const int rr = idx / kR, cc = idx % kR;
       float sum = 0.0f;
 #pragma unroll
@@ -239,8 +239,8 @@ template <int FMT, int R>
 static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
                         uint8_t* scales, const float* amax, const uint16_t* l1t, float* t,
                         hipStream_t s) {
-  // rows per workgroup: the fewest whole waves of workgroups over the CUs, at most
-  // 32 rows each (M = 4608 on 256 CUs: 18 rows, one workgroup per CU)
+  // rows per workgroup: the fewest rounds of workgroups over the CUs with at most 32
+  // rows each (M = 4608 on 256 CUs: 18 rows, one workgroup per CU)
   int cus = 256;
   int dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -251,7 +251,7 @@ static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   while ((M + cus * waves - 1) / (cus * waves) > kQRows) ++waves;
   const int rows = (int)std::max<int64_t>(1, (M + cus * waves - 1) / (cus * waves));
   const unsigned grid = (unsigned)((M + rows - 1) / rows);
-  hipLaunchKernelGGL((quant_act_kernel<FMT, R>), dim3(grid), dim3(512), 0, s, x, M, K, ldx, rows,
+  hipLaunchKernelGGL((quant_act_kernel<FMT, R>), dim3(grid), dim3(kQWaves * 64), 0, s, x, M, K, ldx, rows,
                      codes, scales, amax, l1t, t);
 }
 
