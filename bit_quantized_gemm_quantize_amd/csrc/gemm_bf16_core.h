@@ -72,23 +72,47 @@ template <int ST>
 __device__ __forceinline__ uint8_t* bf16_b(uint8_t* lds) { return lds + (2 + ST) * kBf16TileBytes; }
 
 // One K-tile: multiply stage CUR while tile kt+1 is read and converted into the other.
+// The sched group barriers interleave the loads of the first step and the
+// conversion arithmetic of the last two with single MFMAs, so that the in-order
+// wave keeps the matrix pipe fed (Loader::kValuPerStore: VALU ops of one store part).
 template <int CUR, int F, class Loader>
 __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, Loader& ld, int kt,
                                            uint8_t* lds, int wx, int wy, int lane) {
   constexpr int NXT = CUR ^ 1;
+  constexpr int kMma = 4 * F;                                  // MFMAs per step
+  constexpr int kValu = (Loader::kValuPerStore + kMma - 1) / kMma;
   ld.issue(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
   bf16_mma<0, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);       // fragment reads first
+  for (int i = 0; i < kMma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // global read
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);         // its address arithmetic
+  }
   __builtin_amdgcn_sched_barrier(0);
   bf16_read_frags<0, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
   bf16_mma<1, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, kMma, 0);
   __builtin_amdgcn_sched_barrier(0);
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
   ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_mma<0, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+  for (int i = 0; i < kMma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);           // LDS writes of the part
   __builtin_amdgcn_sched_barrier(0);
   ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_mma<1, F>(acc, fr);
+  for (int i = 0; i < kMma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmem();                               // loads straight into LDS have landed
   // every wave has written stage NXT and finished reading stage CUR

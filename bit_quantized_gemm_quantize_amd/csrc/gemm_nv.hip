@@ -35,6 +35,7 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
 // checks).
 template <int TN>
 struct NvLoader {
+  static constexpr int kValuPerStore = 192;   // VALU ops of one store part (about)
   __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
   uint32_t kb, sbytes, nchunk;
   int tid;

@@ -33,6 +33,7 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
 // each row's (s, z).  Reads past M / N / K return zeros.
 template <int TN>
 struct W4A16Loader {
+  static constexpr int kValuPerStore = 96;   // VALU ops of one store part (about)
   __amdgpu_buffer_rsrc_t rx, rc, rs, rz;
   uint32_t ldxb, kb, ngrp;
   int tid;
