@@ -27,6 +27,8 @@
 // K blocks past the matrix read as zero).  Two LDS stages: tile kt+1 is in
 // flight while tile kt is multiplied, one barrier per K-tile, and the fragments
 // of the next MFMA step are read from LDS while the current step's MFMAs run.
+#include <type_traits>
+
 #include "q4_epilogue.h"
 
 namespace q4 {
@@ -37,9 +39,11 @@ constexpr int kKTB = kKT / 2;     // bytes per row per K-tile
 constexpr int kThreads = 512;
 constexpr int kGroupM = 4;
 
-// LDS: two stages x (activation tile, weight tile) of 256 rows x 128 bytes, then
-// two stages x (activation, weight) of scale rows (256 rows x 16 bytes: the scale
-// bytes of two consecutive K-tiles); the epilogue reuses the space for the output
+// LDS: (activation, weight) x two stages of tiles of 256 rows x 128 bytes (so the
+// stage offset of an operand, 32 KB, folds into the LDS instructions' immediate
+// offsets), then two stages x (activation, weight) of scale rows (256 rows x 16
+// bytes: the scale bytes of two consecutive K-tiles); the epilogue reuses the space
+// for the output
 constexpr int kCodeLds = 2 * 2 * kBM * kKTB;          // 131072
 constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
 constexpr int kMainLds = kCodeLds + kScaleLds;
@@ -54,7 +58,7 @@ __device__ __forceinline__ void mx_tile(
     const float* __restrict__ t, const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias,
     void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
   constexpr int kTN = 128 * F;                   // weight rows of this tile
-  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
+  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
   auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -86,7 +90,7 @@ __device__ __forceinline__ void mx_tile(
       if (operand == 1 && j >= 2 * F) break;
       const uint32_t row = per * wave + 8 * j + lr;
       // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
-      buf_ld16_lds(rc, &lds[stage][operand][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
+      buf_ld16_lds(rc, &lds[operand][stage][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
     }
   };
   // scales, global -> LDS: waves 0-3 take the activation rows, waves 4-7 the weight
@@ -122,12 +126,12 @@ __device__ __forceinline__ void mx_tile(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int row = wm * 128 + 32 * g + r32;
-      fa[buf][g] = ld16(&lds[stage][0][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+      fa[buf][g] = ld16(&lds[0][stage][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int row = wn * 32 * F + 32 * f + r32;
-      fb[buf][f] = ld16(&lds[stage][1][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+      fb[buf][f] = ld16(&lds[1][stage][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
     }
   };
 
@@ -155,13 +159,13 @@ __device__ __forceinline__ void mx_tile(
   }
   // The low-rank term t L2 goes into the accumulators first.  The tile's t rows
   // and L2^T rows (contiguous in memory) are loaded into the second, still unused
-  // operand stage together with the first K-tile, so the epilogue is left with the
-  // bias and the store.
+  // stage of the activation and weight tiles together with the first K-tile, so the
+  // epilogue is left with the bias and the store.
   if (R > 0) {
     const auto rt = make_rsrc(t + m0 * R, rows_a * (uint32_t)(4 * R));
     const auto rl = make_rsrc(l2t + n0 * R, rows_b * (uint32_t)(2 * R));
-    uint8_t* lt = &lds[1][0][0];
-    uint8_t* ll = lt + kBM * 4 * R;
+    uint8_t* lt = &lds[0][1][0];                 // kBM * 4R <= 32 KB
+    uint8_t* ll = &lds[1][1][0];                 // kTN * 2R <= 16 KB
 #pragma unroll
     for (int j = 0; j < R / 8; ++j)              // kBM * 4R bytes in 1 KB pieces
       buf_ld16_lds(rt, lt + (wave * (R / 8) + j) * 1024, (wave * (R / 8) + j) * 1024 + lane * 16);
@@ -175,7 +179,7 @@ __device__ __forceinline__ void mx_tile(
   wait_vmem();
   __syncthreads();
   if (R > 0) {
-    lowrank_accumulate_lds<R>(acc, &lds[1][0][0], &lds[1][0][0] + kBM * 4 * R, 128 * wm, 32 * F * wn, lane);
+    lowrank_accumulate_lds<R>(acc, &lds[0][1][0], &lds[1][1][0], 128 * wm, 32 * F * wn, lane);
     lds_barrier();                           // stage 1 is free again for K-tile 1
   }
   if (nkt > 0) {
@@ -188,8 +192,8 @@ __device__ __forceinline__ void mx_tile(
   // the loads of tile kt+1 are slotted between the MFMAs of steps 0 and 1 (issuing
   // them in a burst would hold the in-order MFMA stream behind them).  On the last
   // tile the "next" loads fall past K and read zeros, harmlessly.
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & 1;
+  auto ktile = [&](auto stage_c, int kt) {
+    constexpr int st = decltype(stage_c)::value;
     read_frags(1, st, 1);
     gload(kt + 1, st ^ 1, 0);
     sload(kt + 1, st ^ 1);
@@ -226,8 +230,15 @@ __device__ __forceinline__ void mx_tile(
 #pragma unroll
     for (int g = 0; g < 4; ++g) sa[g] = sa_n[g];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) sb[f] = sb_n[f];
+    for (int f = 0; f < F; ++f) sb[f] = sb_n[f];
+  };
+  // two K-tiles per trip, so that the stages (and the LDS addresses) are static
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    ktile(std::integral_constant<int, 0>{}, kt);
+    ktile(std::integral_constant<int, 1>{}, kt + 1);
   }
+  if (kt < nkt) ktile(std::integral_constant<int, 0>{}, kt);
 #undef Q4_MX_MMA
 #undef Q4_READS_THEN_MMA
 
