@@ -273,6 +273,22 @@ def bench_rows(reps=20):
              note="comparison: hipBLASLt via torch, unquantized bf16 weight")
 
 
+def summarize_rows_profile(stats_csv, command):
+    """rocprofv3 --kernel-trace --stats of `bench.py --rows` -> a text table of every
+    kernel's average duration (the per-row numbers' own kernels)."""
+    lines = ["# rocprofv3 summary: every kernel of `bench.py --rows` (one MI355X)", "",
+             "command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    lines += ["    " + c for c in command]
+    lines += ["", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in _csv_rows(stats_csv):
+        short = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| `{short[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "Kernels named `Cijk_*` are hipBLASLt's bf16 GEMMs behind the torch comparison rows;",
+              "`__amd_rocclr_*` are runtime copies and fills of the input setup."]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +299,8 @@ def main():
                     help="time every other step of the path, one JSON line per row")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the rocprofv3 summary under profiles/ (no GPU needed)")
+    ap.add_argument("--summarize-rows", metavar="STATS_CSV",
+                    help="write the rocprofv3 summary of `bench.py --rows` under profiles/")
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize: a command line that produced the inputs")
     a = ap.parse_args()
@@ -292,6 +310,12 @@ def main():
             f.write(text)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(rec, f, indent=1)
+        print(text)
+        return
+    if a.summarize_rows:
+        text = summarize_rows_profile(a.summarize_rows, a.command)
+        with open(os.path.join(ROOT, "profiles", "rows_kernels.md"), "w") as f:
+            f.write(text)
         print(text)
         return
     if a.rows:
