@@ -93,9 +93,10 @@ __device__ __forceinline__ void mx_tile(
       buf_ld16_lds(rc, &lds[operand][stage][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
     }
   };
-  // scales, global -> LDS: waves 0-3 take the activation rows, waves 4-7 the weight
-  // rows; lane i of wave w takes row 64 (w % 4) + i, 16 bytes = the scale bytes of
-  // K-tiles kt and kt+1 (the second half is unused when kt+1 is past K)
+  // scales, global -> LDS, once per pair of K-tiles: waves 0-3 take the activation
+  // rows, waves 4-7 the weight rows; lane i of wave w takes row 64 (w % 4) + i, 16
+  // bytes = the scale bytes of K-tiles kt and kt+1 (kt even), into scale stage
+  // (kt / 2) % 2
   const int sop = wave >> 2, sw = wave & 3;
   const auto rs_op = sop == 0 ? rs_a : rs_b;
   auto sload = [&](int kt, int stage) {
@@ -104,19 +105,21 @@ __device__ __forceinline__ void mx_tile(
     const uint32_t off = (64 * sw + lane) * nblk + koff;
     buf_ld16_lds(rs_op, &lsc[stage][sop][64 * sw * 16], off);
   };
-  // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3
+  // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3,
+  // at byte 8 (kt % 2) + 4h of the row's 16 bytes in scale stage (kt / 2) % 2
   uint32_t sa[4], sb[F], sa_n[4], sb_n[F];
-  auto read_scales = [&](int kt, int stage, uint32_t* xa, uint32_t* xb) {
+  auto read_scales = [&](int kt) {
     const bool kin = (uint32_t)kt * 8 + 4 * h < nblk;      // past K: codes are 0; keep 2**0
+    const int stage = (kt >> 1) & 1, byte = 8 * (kt & 1) + 4 * h;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wm * 128 + 32 * g + r32) * 16 + 4 * h]);
-      xa[g] = kin ? v : 0x7F7F7F7Fu;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wm * 128 + 32 * g + r32) * 16 + byte]);
+      sa_n[g] = kin ? v : 0x7F7F7F7Fu;
     }
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 32 * F + 32 * f + r32) * 16 + 4 * h]);
-      xb[f] = kin ? v : 0x7F7F7F7Fu;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 32 * F + 32 * f + r32) * 16 + byte]);
+      sb_n[f] = kin ? v : 0x7F7F7F7Fu;
     }
   };
 
@@ -184,7 +187,11 @@ __device__ __forceinline__ void mx_tile(
   }
   if (nkt > 0) {
     read_frags(0, 0, 0);
-    read_scales(0, 0, sa, sb);
+    read_scales(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sa[g] = sa_n[g];
+#pragma unroll
+    for (int f = 0; f < F; ++f) sb[f] = sb_n[f];
   }
 
   // The loop body is one basic block (no branches), so the sched barriers pin the
@@ -196,7 +203,7 @@ __device__ __forceinline__ void mx_tile(
     constexpr int st = decltype(stage_c)::value;
     read_frags(1, st, 1);
     gload(kt + 1, st ^ 1, 0);
-    sload(kt + 1, st ^ 1);
+    if (st == 1) sload(kt + 1, ((kt + 1) >> 1) & 1);   // kt + 1 even: a new pair
     Q4_MX_MMA(0, 0)
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
     for (int i = 0; i < 5; ++i) {
@@ -223,7 +230,7 @@ __device__ __forceinline__ void mx_tile(
     // every wave's tile kt+1 has landed, and every read of tile kt has completed
     __syncthreads();
     read_frags(0, st ^ 1, 0);
-    read_scales(kt + 1, st ^ 1, sa_n, sb_n);
+    read_scales(kt + 1);
     Q4_MX_MMA(3, 1)
     Q4_READS_THEN_MMA(12)
     __builtin_amdgcn_sched_barrier(0);
