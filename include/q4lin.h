@@ -96,6 +96,7 @@ typedef enum q4_out {
  *   M, K          M >= 0; K >= 0 and a multiple of 32.
  *   codes  (out)  uint8 [M, K/2].  16-byte aligned.
  *   scales (out)  MXFP4: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16].
+ *                 4-byte aligned.
  *   tensor_scale  NVFP4: float[1], written with s_t (also used as the amax
  *                 accumulator while the call runs).  MXFP4: ignored, may be NULL.
  *   l1t           r > 0: bf16 L1^T [r, K] (the down-projection stored
@@ -119,10 +120,12 @@ Q4_API q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64
  *   w                 bf16, logical [K, N]: element (k, n) at w[k*stride_k + n*stride_n]
  *                     (stride_k = 1, stride_n = K for nn.Linear's [out, in] storage;
  *                     stride_k = N, stride_n = 1 for row-major [K, N]).  Strides >= 1.
+ *                     w 2-byte aligned; with stride_k = 1, stride_n a multiple of 8
+ *                     and w 16-byte aligned the rows are read 16 bytes at a time.
  *   K, N              K a multiple of 32 (MXFP4, NVFP4) or 64 (INT4_G64).
- *   codes  (out)      uint8 [N, K/2].
+ *   codes  (out)      uint8 [N, K/2], 16-byte aligned.
  *   scales (out)      MXFP4: uint8 [N, K/32]; NVFP4: uint8 E4M3 [N, K/16];
- *                     INT4_G64: bf16 [N, K/64].
+ *                     INT4_G64: bf16 [N, K/64].  4-byte aligned.
  *   zeros  (out)      INT4_G64: bf16 [N, K/64] (integers 0..15); else ignored.
  *   tensor_scale(out) NVFP4: float[1] (s_t of the weight); else ignored.
  */
@@ -141,7 +144,9 @@ Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64
  *   a_*       activation codes [M, K/2] and scales (layout as quantize_act);
  *             a_tscale: NVFP4 float[1], else ignored.
  *   b_*       weight codes [N, K/2] and scales (layout as pack_weights).
- *   K         a multiple of 128.
+ *             Codes 16-byte aligned, scales and tensor scales 4-byte aligned.
+ *   K         a multiple of 128 (and 256 K/2 < 2^31: a tile's rows are addressed
+ *             with 32-bit offsets).
  *   bias      bf16 [N] or NULL.
  *   y   (out) [M, N] with row stride ldy >= N elements; bf16 or fp32 per `out`.
  *             16-byte aligned, ldy a multiple of 8.
@@ -157,7 +162,7 @@ Q4_API q4_status gemm_w4a4(q4_format fmt,
 
 /*
  * gemm_w4a4_lowrank -- gemm_w4a4 plus the low-rank up-projection t L2 fused into
- * the epilogue (SVDQuant Guide, "3. The Nunchaku Fused Kernel Engine": the 4-bit
+ * the same kernel (SVDQuant Guide, "3. The Nunchaku Fused Kernel Engine": the 4-bit
  * GEMM and the 16-bit low-rank GEMM in one kernel).  t comes from quantize_act.
  *
  *   t     fp32 [M, r], 16-byte aligned.  It enters the bf16 MFMA as a pair of
