@@ -13,6 +13,10 @@ q4_status launched(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_LAUNC
 
 bool rank_ok(int32_t r) { return r == 0 || r == 16 || r == 32; }
 
+// Size limits of the kernels' 32-bit tile addressing and grid sizes.
+constexpr int64_t kMaxRows = int64_t(1) << 30;   // M, N
+constexpr int64_t kMaxK = int64_t(1) << 22;      // K, and ldx of the W4A16 activations
+
 // Checks shared by the two W4A4 entry points.
 q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales,
                      const float* a_tscale, const uint8_t* b_codes, const uint8_t* b_scales,
@@ -21,6 +25,7 @@ q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_sca
   if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4) return Q4_ERR_FORMAT;
   if (out != Q4_OUT_BF16 && out != Q4_OUT_F32) return Q4_ERR_FORMAT;
   if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || ldy < N) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || K > kMaxK) return Q4_ERR_SHAPE;
   if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return Q4_ERR_NULL;
   if (fmt == Q4_NVFP4 && (!a_tscale || !b_tscale)) return Q4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
@@ -51,6 +56,7 @@ q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, i
                        const uint16_t* l1t, int32_t r, float* t, void* stream) {
   if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4) return Q4_ERR_FORMAT;
   if (M < 0 || K < 0 || (K % 32) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows) return Q4_ERR_SHAPE;
   if (!x || !codes || !scales) return Q4_ERR_NULL;
   if (fmt == Q4_NVFP4 && !tensor_scale) return Q4_ERR_NULL;
   if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
@@ -120,6 +126,7 @@ q4_status gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* w_codes,
   if (out != Q4_OUT_BF16 && out != Q4_OUT_F32) return Q4_ERR_FORMAT;
   if (group != 64) return Q4_ERR_SHAPE;
   if (M < 0 || N < 0 || K < 0 || (K % 64) != 0 || ldx < K || ldy < N) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || K > kMaxK || ldx > kMaxK) return Q4_ERR_SHAPE;
   if (!x || !w_codes || !w_scales || !w_zeros || !y) return Q4_ERR_NULL;
   if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(w_codes, 16) || !aligned(w_scales, 2) ||
       !aligned(w_zeros, 2) || !aligned(y, 16) || (ldy % 8) != 0)

@@ -93,7 +93,7 @@ typedef enum q4_out {
  *   fmt           Q4_MXFP4 or Q4_NVFP4 (else Q4_ERR_FORMAT).
  *   x             bf16 [M, K], row stride ldx elements.  16-byte aligned, ldx a
  *                 multiple of 8, ldx >= K.
- *   M, K          M >= 0; K >= 0 and a multiple of 32.
+ *   M, K          0 <= M <= 2^30; K >= 0 and a multiple of 32.
  *   codes  (out)  uint8 [M, K/2].  16-byte aligned.
  *   scales (out)  MXFP4: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16].
  *                 4-byte aligned.
@@ -145,8 +145,9 @@ Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64
  *             a_tscale: NVFP4 float[1], else ignored.
  *   b_*       weight codes [N, K/2] and scales (layout as pack_weights).
  *             Codes 16-byte aligned, scales and tensor scales 4-byte aligned.
- *   K         a multiple of 128 (and 256 K/2 < 2^31: a tile's rows are addressed
- *             with 32-bit offsets).
+ *   M, N      0 .. 2^30.
+ *   K         a multiple of 128, at most 2^22 (a tile's rows are addressed with
+ *             32-bit offsets).
  *   bias      bf16 [N] or NULL.
  *   y   (out) [M, N] with row stride ldy >= N elements; bf16 or fp32 per `out`.
  *             16-byte aligned, ldy a multiple of 8.
@@ -189,7 +190,7 @@ Q4_API q4_status gemm_w4a4_lowrank(q4_format fmt,
  *   x         bf16 [M, K], row stride ldx (multiple of 8), 16-byte aligned.
  *   w_codes   uint8 [N, K/2]; w_scales, w_zeros bf16 [N, K/group] from pack_weights.
  *   group     64.
- *   K         a multiple of 64.
+ *   K, ldx    K a multiple of 64; K and ldx at most 2^22.
  * Other arguments as gemm_w4a4.
  */
 Q4_API q4_status gemm_w4a16(const uint16_t* x, int64_t ldx,

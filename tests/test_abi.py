@@ -98,6 +98,8 @@ def test_gemm_w4a4_rejections():
     assert gw(K=96) == B.Q4_ERR_SHAPE                    # K not a multiple of 128
     assert gw(N=-2) == B.Q4_ERR_SHAPE
     assert gw(ldy=100) == B.Q4_ERR_SHAPE
+    assert gw(K=(1 << 22) + 128) == B.Q4_ERR_SHAPE        # past the 32-bit tile offsets
+    assert gw(M=(1 << 30) + 1) == B.Q4_ERR_SHAPE
     assert gw(ldy=260) == B.Q4_ERR_ALIGN
     assert gw(y=ODD) == B.Q4_ERR_ALIGN
     assert gw(bc=ODD) == B.Q4_ERR_ALIGN
@@ -128,6 +130,7 @@ def test_gemm_w4a16_and_pack_rejections():
 
     assert w16(group=32) == B.Q4_ERR_SHAPE
     assert w16(K=96, ldx=96) == B.Q4_ERR_SHAPE
+    assert w16(ldx=(1 << 22) + 8) == B.Q4_ERR_SHAPE
     assert w16(x=None) == B.Q4_ERR_NULL
     assert w16(ldx=260) == B.Q4_ERR_ALIGN
     assert w16(out=2) == B.Q4_ERR_FORMAT
