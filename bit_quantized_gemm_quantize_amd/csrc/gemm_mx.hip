@@ -95,32 +95,37 @@ __device__ __forceinline__ void mx_tile(
   };
   // scales, global -> LDS, once per pair of K-tiles: waves 0-3 take the activation
   // rows, waves 4-7 the weight rows; lane i of wave w takes row 64 (w % 4) + i, 16
-  // bytes = the scale bytes of K-tiles kt and kt+1 (kt even), into scale stage
-  // (kt / 2) % 2
+  // bytes = the scale bytes of K-tiles 2p and 2p+1 of pair p, into scale stage p % 2.
+  // Pair p+1 is loaded while K-tile 2p is multiplied, so the scales of every K-tile
+  // are in LDS one barrier before they are read.
   const int sop = wave >> 2, sw = wave & 3;
   const auto rs_op = sop == 0 ? rs_a : rs_b;
-  auto sload = [&](int kt, int stage) {
-    const uint32_t b0 = (uint32_t)kt * 8;
+  auto sload = [&](int p) {
+    const uint32_t b0 = (uint32_t)p * 16;
     const uint32_t koff = b0 < nblk ? b0 : kOOB;
     const uint32_t off = (64 * sw + lane) * nblk + koff;
-    buf_ld16_lds(rs_op, &lsc[stage][sop][64 * sw * 16], off);
+    buf_ld16_lds(rs_op, &lsc[p & 1][sop][64 * sw * 16], off);
   };
   // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3,
-  // at byte 8 (kt % 2) + 4h of the row's 16 bytes in scale stage (kt / 2) % 2
+  // at byte 8 (kt % 2) + 4h of the row's 16 bytes in scale stage (kt / 2) % 2.
+  // Read raw; valid_scales() replaces the words of blocks past K (whose codes are
+  // zero) by 2**0, so that bytes beyond the row's last block never reach the MFMA.
   uint32_t sa[4], sb[F], sa_n[4], sb_n[F];
   auto read_scales = [&](int kt) {
-    const bool kin = (uint32_t)kt * 8 + 4 * h < nblk;      // past K: codes are 0; keep 2**0
     const int stage = (kt >> 1) & 1, byte = 8 * (kt & 1) + 4 * h;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wm * 128 + 32 * g + r32) * 16 + byte]);
-      sa_n[g] = kin ? v : 0x7F7F7F7Fu;
-    }
+    for (int g = 0; g < 4; ++g)
+      sa_n[g] = *reinterpret_cast<const uint32_t*>(&lsc[stage][0][(wm * 128 + 32 * g + r32) * 16 + byte]);
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 32 * F + 32 * f + r32) * 16 + byte]);
-      sb_n[f] = kin ? v : 0x7F7F7F7Fu;
-    }
+    for (int f = 0; f < F; ++f)
+      sb_n[f] = *reinterpret_cast<const uint32_t*>(&lsc[stage][1][(wn * 32 * F + 32 * f + r32) * 16 + byte]);
+  };
+  auto valid_scales = [&](int kt) {
+    const bool kin = (uint32_t)kt * 8 + 4 * h < nblk;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sa[g] = kin ? sa_n[g] : 0x7F7F7F7Fu;
+#pragma unroll
+    for (int f = 0; f < F; ++f) sb[f] = kin ? sb_n[f] : 0x7F7F7F7Fu;
   };
 
   // fragment registers, double-buffered across MFMA steps
@@ -158,7 +163,7 @@ __device__ __forceinline__ void mx_tile(
   if (nkt > 0) {
     gload(0, 0, 0);
     gload(0, 0, 1);
-    sload(0, 0);
+    sload(0);
   }
   // The low-rank term t L2 goes into the accumulators first.  The tile's t rows
   // and L2^T rows (contiguous in memory) are loaded into the second, still unused
@@ -188,22 +193,22 @@ __device__ __forceinline__ void mx_tile(
   if (nkt > 0) {
     read_frags(0, 0, 0);
     read_scales(0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) sa[g] = sa_n[g];
-#pragma unroll
-    for (int f = 0; f < F; ++f) sb[f] = sb_n[f];
+    valid_scales(0);
   }
 
   // The loop body is one basic block (no branches), so the sched barriers pin the
   // order: each MFMA step runs with the next step's fragment reads in flight, and
   // the loads of tile kt+1 are slotted between the MFMAs of steps 0 and 1 (issuing
-  // them in a burst would hold the in-order MFMA stream behind them).  On the last
-  // tile the "next" loads fall past K and read zeros, harmlessly.
+  // them in a burst would hold the in-order MFMA stream behind them).  The scales
+  // of tile kt+1 are read in step 1, from a stage that an earlier barrier made
+  // visible, so that after this tile's barrier only the fragment reads of the next
+  // step are outstanding.  On the last tile the "next" loads fall past K and read
+  // zeros, harmlessly.
   auto ktile = [&](auto stage_c, int kt) {
     constexpr int st = decltype(stage_c)::value;
     read_frags(1, st, 1);
     gload(kt + 1, st ^ 1, 0);
-    if (st == 1) sload(kt + 1, ((kt + 1) >> 1) & 1);   // kt + 1 even: a new pair
+    if (st == 0) sload((kt >> 1) + 1);                 // kt even: the next pair
     Q4_MX_MMA(0, 0)
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
     for (int i = 0; i < 5; ++i) {
@@ -212,10 +217,11 @@ __device__ __forceinline__ void mx_tile(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
+    read_scales(kt + 1);
     read_frags(0, st, 2);
     gload(kt + 1, st ^ 1, 1);
     Q4_MX_MMA(1, 1)
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 10 + F, 0);
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -230,14 +236,10 @@ __device__ __forceinline__ void mx_tile(
     // every wave's tile kt+1 has landed, and every read of tile kt has completed
     __syncthreads();
     read_frags(0, st ^ 1, 0);
-    read_scales(kt + 1);
     Q4_MX_MMA(3, 1)
-    Q4_READS_THEN_MMA(12)
+    Q4_READS_THEN_MMA(6)
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) sa[g] = sa_n[g];
-#pragma unroll
-    for (int f = 0; f < F; ++f) sb[f] = sb_n[f];
+    valid_scales(kt + 1);
   };
   // two K-tiles per trip, so that the stages (and the LDS addresses) are static
   int kt = 0;
