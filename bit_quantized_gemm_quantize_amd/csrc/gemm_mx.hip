@@ -17,8 +17,8 @@
 //
 // Tail: when the tiles do not fill the last round over the CUs (864 tiles on 256
 // CUs leave 96), the leftover tiles are split in two halves of 128 weight rows,
-// each a workgroup whose waves own 128 x 32, so that the last round is half as
-// long.
+// each a workgroup whose waves own 128 x 32, so that the extra round is half as
+// long.  The halves are dispatched first (see gemm_mx_kernel).
 //
 // LDS: the two operand tiles (256 rows x 128 bytes each) are stored with 16-byte
 // chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)), so the 16-byte
@@ -255,8 +255,10 @@ __device__ __forceinline__ void mx_tile(
   epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds_raw + wave * kStageWaveBytes);
 }
 
-// Workgroups [0, full) take whole tiles; the rest take halves of the leftover tiles
-// (tile full + q/2, weight rows 128 (q % 2) .. +127).
+// Workgroups [0, halves) take halves of the leftover tiles (tile full + q/2, weight
+// rows 128 (q % 2) .. +127), the rest whole tiles.  Running the halves first puts
+// the CUs that took one half tile a half tile out of step with the others, so the
+// output stores of the two sets fall at different times instead of all at once.
 template <int R, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
@@ -264,14 +266,15 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int tiles_m, int tiles_n, int full) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
+  const int halves = 2 * (tiles_m * tiles_n - full);
   const int bid = blockIdx.x;
   int tm, tn;
-  if (bid < full) {
-    tile_of(bid, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  if (bid >= halves) {
+    tile_of(bid - halves, tiles_m, tiles_n, kGroupM, &tm, &tn);
     mx_tile<R, OUT_F32, 2>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,
                            (int64_t)tn * kBN);
   } else {
-    const int q = bid - full;
+    const int q = bid;
     tile_of(full + (q >> 1), tiles_m, tiles_n, kGroupM, &tm, &tn);
     if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
     mx_tile<R, OUT_F32, 1>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,

@@ -14,6 +14,16 @@
 
 namespace q4 {
 
+// t = hi + lo for a pair of fp32 values, hi and lo bf16 pairs (packed, element 0
+// in the low half).  The hardware conversion rounds to nearest even; v - hi is
+// exact in fp32, so hi + lo carries 16 significant bits of t.
+__device__ __forceinline__ void split_bf16_pair(float v0, float v1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, v2bf{(__bf16)v0, (__bf16)v1});
+  const float r0 = v0 - __uint_as_float(hi << 16);
+  const float r1 = v1 - __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(uint32_t, v2bf{(__bf16)r0, (__bf16)r1});
+}
+
 // acc[f][g]: f = weight (n) sub-tile, g = activation (m) sub-tile, 32 x 32 each.
 // n_base / m_base: first n / m of the wave's (32 F) x 128 region.
 template <int R, int F>
@@ -33,17 +43,12 @@ __device__ __forceinline__ void lowrank_accumulate(v16f (&acc)[F][4], int64_t n_
         const float* src = t + m * R + 16 * ks + 8 * h;
         const u32x4 a = ld16(src), b = ld16(src + 4);
         const uint32_t tv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = __uint_as_float(tv[j]);
-          hi[j] = f32_to_bf16_rne(v);
-          lo[j] = f32_to_bf16_rne(v - __uint_as_float(hi[j] << 16));
-        }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          thi[g][d] = hi[2 * d] | (hi[2 * d + 1] << 16);
-          tlo[g][d] = lo[2 * d] | (lo[2 * d + 1] << 16);
+          uint32_t hi, lo;
+          split_bf16_pair(__uint_as_float(tv[2 * d]), __uint_as_float(tv[2 * d + 1]), hi, lo);
+          thi[g][d] = hi;
+          tlo[g][d] = lo;
         }
       }
     }
@@ -79,17 +84,12 @@ __device__ __forceinline__ void lowrank_accumulate_lds(v16f (&acc)[F][4], const 
       const uint8_t* src = lds_t + (m_loc + 32 * g + r32) * (4 * R) + (16 * ks + 8 * h) * 4;
       const u32x4 a = ld16(src), b = ld16(src + 16);
       const uint32_t tv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = __uint_as_float(tv[j]);
-        hi[j] = f32_to_bf16_rne(v);
-        lo[j] = f32_to_bf16_rne(v - __uint_as_float(hi[j] << 16));
-      }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        thi[g][d] = hi[2 * d] | (hi[2 * d + 1] << 16);
-        tlo[g][d] = lo[2 * d] | (lo[2 * d + 1] << 16);
+        uint32_t hi, lo;
+        split_bf16_pair(__uint_as_float(tv[2 * d]), __uint_as_float(tv[2 * d + 1]), hi, lo);
+        thi[g][d] = hi;
+        tlo[g][d] = lo;
       }
     }
 #pragma unroll
@@ -103,6 +103,12 @@ __device__ __forceinline__ void lowrank_accumulate_lds(v16f (&acc)[F][4], const 
         acc[f][g] = mfma_bf16_32x32x16(l2f[f], tlo[g], acc[f][g]);
       }
   }
+}
+
+// A 16-byte store marked non-temporal: the output is not read again by this
+// kernel, so it should not displace the operands in the caches.
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 // Output staging through LDS: each wave writes a 128-row x 128-byte slab of its
@@ -182,7 +188,7 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
       if (m < M) {
         uint8_t* dst = static_cast<uint8_t*>(y) + (m * ldy + n) * kElem;
         if (n + kPer16 <= N) {
-          st16(dst, v);
+          st16_stream(dst, v);
         } else if (n < N) {
           const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
           for (int j = 0; j < kPer16 && n + j < N; ++j) {
