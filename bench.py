@@ -260,6 +260,25 @@ def bench_rows(reps=20):
         emit(f"gemm_w4a4 mxfp4 {Mq}x{Kq}x{n} bf16 out", ms, flops=2.0 * Mq * n * Kq,
              peak=MXFP4_PEAK_TFLOPS, note="inputs warm in L2/MALL")
 
+    # ---- comparison: the vendor MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on
+    # the same codes and E8M0 scales, row-major scale layout
+    y = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)
+    B.gemm_w4a4("mxfp4", ac, asc, None, bc, bsc, None, Mq, Np, Kq, y, stream=stream)
+    try:
+        a4, b4 = ac.view(torch.float4_e2m1fn_x2), bc.view(torch.float4_e2m1fn_x2)
+        sa8, sb8 = asc.view(torch.float8_e8m0fnu), bsc.view(torch.float8_e8m0fnu)
+        y_lib = torch._scaled_mm(a4, b4.t(), sa8, sb8, out_dtype=torch.bfloat16)
+        diff = (y_lib.float() - y.float()).abs().max().item() / max(y.float().abs().max().item(), 1e-30)
+        ms = timed(lambda i: torch._scaled_mm(a4, b4.t(), sa8, sb8, out_dtype=torch.bfloat16), 1)
+        emit(f"torch._scaled_mm mxfp4 {Mq}x{Kq}x{Np} bf16 out", ms, flops=2.0 * Mq * Np * Kq,
+             peak=MXFP4_PEAK_TFLOPS,
+             note=f"comparison: hipBLASLt MXFP4 on the same codes and scales; max |diff| / max |y| "
+                  f"vs gemm_w4a4 = {diff:.2e}")
+    except (RuntimeError, TypeError, AttributeError) as e:
+        print(json.dumps({"row": "torch._scaled_mm mxfp4", "note": f"unavailable: {str(e)[:200]}"}),
+              flush=True)
+    del y
+
     # ---- a8: W4A16 against a plain bf16 GEMM of the same shape
     wbf = wt
     for m in (512, 4608):

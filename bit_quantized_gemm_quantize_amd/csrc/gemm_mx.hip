@@ -2,12 +2,14 @@
 // fused in (its bf16 MFMAs seed the accumulators before the K loop) and the bias
 // and store in the epilogue.
 //
-// Tiling: 256 x 256 output tile per workgroup of 8 waves, two per SIMD, so that
-// one wave's MFMAs run while the other waits on an LDS read or a load issue.  Wave
-// (wm, wn) owns m in [128 wm, +128) and n in [64 wn, +64) as 2 x 4 tiles of
+// Tiling: 256 x 256 output tile per workgroup of 4 waves, one per SIMD.  Wave
+// (wm, wn) owns m in [128 wm, +128) and n in [128 wn, +128) as 4 x 4 tiles of
 // v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4, one E8M0 scale per 32 K elements
-// per row, applied by the MFMA itself); 128 accumulators per lane.  K advances in
-// tiles of 256 elements (128 bytes per row; 8 scale bytes per row).
+// per row, applied by the MFMA itself); its 256 accumulators per lane live in the
+// matrix registers (AGPRs).  A 128 x 128 wave tile reads 0.5 KB of LDS fragments
+// per MFMA, against 0.75 KB for 128 x 64.  K advances in tiles of 256 elements
+// (128 bytes per row; 8 scale bytes per row).  The wave count is one constant
+// (kWaves = 4 or 8; with 8, two per SIMD, a wave owns 128 x 64).
 //
 // K order inside a K-tile: lane half h (= lane/32) of every fragment owns the
 // contiguous blocks 4h .. 4h+3 of the tile, and MFMA step s (0..3) consumes block
@@ -17,16 +19,16 @@
 //
 // Tail: when the tiles do not fill the last round over the CUs (864 tiles on 256
 // CUs leave 96), the leftover tiles are split in two halves of 128 weight rows,
-// each a workgroup whose waves own 128 x 32, so that the extra round is half as
-// long.  The halves are dispatched first (see gemm_mx_kernel).
+// so that the extra round is half as long.  The halves are dispatched first (see
+// gemm_mx_kernel).
 //
 // LDS: the two operand tiles (256 rows x 128 bytes each) are stored with 16-byte
 // chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)), so the 16-byte
 // fragment reads are free of bank conflicts.  Tiles go from HBM/L2 straight into
 // LDS (buffer loads with the LDS destination, no staging registers; rows and
-// K blocks past the matrix read as zero).  Two LDS stages: tile kt+1 is in
-// flight while tile kt is multiplied, one barrier per K-tile, and the fragments
-// of the next MFMA step are read from LDS while the current step's MFMAs run.
+// K blocks past the matrix read as zero).  Two LDS stages, one barrier per K-tile;
+// the fragments of the next MFMA step are read from LDS while the current step's
+// MFMAs run.
 #include <type_traits>
 
 #include "q4_epilogue.h"
@@ -36,8 +38,11 @@ namespace q4 {
 constexpr int kBM = 256, kBN = 256;
 constexpr int kKT = 256;          // K elements per K-tile
 constexpr int kKTB = kKT / 2;     // bytes per row per K-tile
-constexpr int kThreads = 512;
+constexpr int kWaves = 4;         // one per SIMD
+constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupM = 4;
+// weight sub-tiles (32 rows each) per wave: whole tiles and half tiles
+constexpr int kFFull = 512 / (32 * kWaves), kFHalf = kFFull / 2;
 
 // LDS: (activation, weight) x two stages of tiles of 256 rows x 128 bytes (so the
 // stage offset of an operand, 32 KB, folds into the LDS instructions' immediate
@@ -49,7 +54,7 @@ constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
 constexpr int kMainLds = kCodeLds + kScaleLds;
 static_assert((kThreads / 64) * kStageWaveBytes <= kMainLds, "the epilogue stages each wave's output in the operand LDS");
 
-// One output tile of 256 activation rows x 128 F weight rows starting at (m0, n0):
+// One output tile of 256 activation rows x kTN weight rows starting at (m0, n0):
 // wave (wm, wn) owns m in [128 wm, +128) and n in [32 F wn, +32 F).
 template <int R, bool OUT_F32, int F>
 __device__ __forceinline__ void mx_tile(
@@ -57,7 +62,9 @@ __device__ __forceinline__ void mx_tile(
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
     const float* __restrict__ t, const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias,
     void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
-  constexpr int kTN = 128 * F;                   // weight rows of this tile
+  constexpr int kTN = 16 * F * kWaves;           // weight rows of this tile
+  constexpr int kRowsA = kBM / kWaves, kRowsB = kTN / kWaves;   // rows each wave loads
+  constexpr int kMma = 4 * F;                    // MFMAs per wave per step
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
   auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
 
@@ -77,34 +84,46 @@ __device__ __forceinline__ void mx_tile(
 
   // codes, global -> LDS: each wave moves 8 rows x 128 bytes per instruction straight
   // into LDS (lane i -> row i/8, stored position i%8, which holds global chunk
-  // (i%8) ^ (row & 7), the swizzle).  Wave w covers activation rows 32 w .. +31 and
-  // weight rows 16 F w .. +16 F - 1.
+  // (i%8) ^ (row & 7), the swizzle).  Wave w covers activation rows kRowsA w .. +kRowsA-1
+  // and weight rows kRowsB w .. +kRowsB-1: kNL instructions per K-tile, issued in
+  // three parts (instructions [kPartBegin[p], kPartBegin[p+1])).
+  constexpr int kNA = kRowsA / 8, kNL = kNA + kRowsB / 8;
+  constexpr int kPart0 = kNL / 3, kPart1 = (kNL - kPart0) / 2;
+  constexpr int kPartBegin[4] = {0, kPart0, kPart0 + kPart1, kNL};
   const int lr = lane >> 3, lp = lane & 7;
-  auto gload = [&](int kt, int stage, int operand) {
+  auto gload_part = [&](auto part_c, int kt, int stage) {
+    constexpr int part = decltype(part_c)::value;
     const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
     const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
-    const auto rc = operand == 0 ? rc_a : rc_b;
-    const int per = operand == 0 ? 32 : 16 * F;              // rows per wave
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (operand == 1 && j >= 2 * F) break;
+    for (int idx = kPartBegin[part]; idx < kPartBegin[part + 1]; ++idx) {
+      const int op = idx < kNA ? 0 : 1;
+      const int per = op == 0 ? kRowsA : kRowsB;
+      const int j = op == 0 ? idx : idx - kNA;
       const uint32_t row = per * wave + 8 * j + lr;
       // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
-      buf_ld16_lds(rc, &lds[operand][stage][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
+      buf_ld16_lds(op == 0 ? rc_a : rc_b, &lds[op][stage][(per * wave + 8 * j) * kKTB],
+                   row * kbytes + koff);
     }
   };
-  // scales, global -> LDS, once per pair of K-tiles: waves 0-3 take the activation
-  // rows, waves 4-7 the weight rows; lane i of wave w takes row 64 (w % 4) + i, 16
-  // bytes = the scale bytes of K-tiles 2p and 2p+1 of pair p, into scale stage p % 2.
-  // Pair p+1 is loaded while K-tile 2p is multiplied, so the scales of every K-tile
-  // are in LDS one barrier before they are read.
-  const int sop = wave >> 2, sw = wave & 3;
-  const auto rs_op = sop == 0 ? rs_a : rs_b;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  // scales, global -> LDS, once per pair of K-tiles: 64 rows per instruction (lane i
+  // takes row 64 sw + i, 16 bytes = the scale bytes of K-tiles 2p and 2p+1 of pair
+  // p) into scale stage p % 2.  With 8 waves, waves 0-3 take the activation rows
+  // and waves 4-7 the weight rows; with 4, every wave takes both.
+  constexpr int kScaleOps = kWaves == 8 ? 1 : 2;        // scale loads per wave per pair
+  const int sw = wave & 3;
   auto sload = [&](int p) {
     const uint32_t b0 = (uint32_t)p * 16;
     const uint32_t koff = b0 < nblk ? b0 : kOOB;
     const uint32_t off = (64 * sw + lane) * nblk + koff;
-    buf_ld16_lds(rs_op, &lsc[p & 1][sop][64 * sw * 16], off);
+#pragma unroll
+    for (int k = 0; k < kScaleOps; ++k) {
+      const int op = kWaves == 8 ? (wave >> 2) : k;
+      buf_ld16_lds(op == 0 ? rs_a : rs_b, &lsc[p & 1][op][64 * sw * 16], off);
+    }
   };
   // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3,
   // at byte 8 (kt % 2) + 4h of the row's 16 bytes in scale stage (kt / 2) % 2.
@@ -149,21 +168,29 @@ __device__ __forceinline__ void mx_tile(
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
-#define Q4_MX_MMA(S, BUF)                                                                       \
-  _Pragma("unroll") for (int f = 0; f < F; ++f)                                                 \
+#define Q4_MX_MMA(S, BUF) Q4_MX_MMA_F(S, BUF, 0, F)
+#define Q4_MX_MMA_F(S, BUF, F0, F1)                                                             \
+  _Pragma("unroll") for (int f = F0; f < F1; ++f)                                               \
     _Pragma("unroll") for (int g = 0; g < 4; ++g)                                               \
       acc[f][g] = mfma_fp4_32x32x64<S, S>(fb[BUF][f], fa[BUF][g], acc[f][g], (int)sb[f],       \
                                           (int)sa[g]);
 // within a region: the LDS reads for the next step go out first, then the MFMAs
 #define Q4_READS_THEN_MMA(NREADS)                          \
   __builtin_amdgcn_sched_group_barrier(0x100, NREADS, 0); \
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, kMma, 0);
 
   const int64_t n_base = n0 + wn * 32 * F, m_base = m0 + wm * 128;
+  // Pipeline: the loads of K-tile kt+1 go out from the barrier of K-tile kt-1 (part
+  // 0, once that barrier has freed the stage) through steps 0 and 1 of K-tile kt
+  // (parts 1 and 2), and are waited for at the barrier inside step 3 of K-tile kt:
+  // nearly a whole K-tile of latency cover.  Scale pair q is loaded with part 0 of
+  // K-tile 2q-1, and read (for K-tile 2q) in step 1 of K-tile 2q-1.
   if (nkt > 0) {
-    gload(0, 0, 0);
-    gload(0, 0, 1);
+    gload_part(P0{}, 0, 0);
+    gload_part(P1{}, 0, 0);
+    gload_part(P2{}, 0, 0);
     sload(0);
+    sload(1);
   }
   // The low-rank term t L2 goes into the accumulators first.  The tile's t rows
   // and L2^T rows (contiguous in memory) are loaded into the second, still unused
@@ -174,13 +201,16 @@ __device__ __forceinline__ void mx_tile(
     const auto rl = make_rsrc(l2t + n0 * R, rows_b * (uint32_t)(2 * R));
     uint8_t* lt = &lds[0][1][0];                 // kBM * 4R <= 32 KB
     uint8_t* ll = &lds[1][1][0];                 // kTN * 2R <= 16 KB
+    constexpr int kPiecesT = kBM * 4 * R / 1024;  // kBM * 4R bytes in 1 KB pieces
 #pragma unroll
-    for (int j = 0; j < R / 8; ++j)              // kBM * 4R bytes in 1 KB pieces
-      buf_ld16_lds(rt, lt + (wave * (R / 8) + j) * 1024, (wave * (R / 8) + j) * 1024 + lane * 16);
+    for (int j = 0; j < kPiecesT / kWaves; ++j) {
+      const int piece = wave * (kPiecesT / kWaves) + j;
+      buf_ld16_lds(rt, lt + piece * 1024, piece * 1024 + lane * 16);
+    }
     constexpr int kPieces = kTN * 2 * R / 1024;  // kTN * 2R bytes
 #pragma unroll
-    for (int j = 0; j < (kPieces + 7) / 8; ++j) {
-      const int piece = j * 8 + wave;
+    for (int j = 0; j < (kPieces + kWaves - 1) / kWaves; ++j) {
+      const int piece = j * kWaves + wave;
       if (piece < kPieces) buf_ld16_lds(rl, ll + piece * 1024, piece * 1024 + lane * 16);
     }
   }
@@ -191,6 +221,7 @@ __device__ __forceinline__ void mx_tile(
     lds_barrier();                           // stage 1 is free again for K-tile 1
   }
   if (nkt > 0) {
+    gload_part(P0{}, 1, 1);
     read_frags(0, 0, 0);
     read_scales(0);
     valid_scales(0);
@@ -198,46 +229,55 @@ __device__ __forceinline__ void mx_tile(
 
   // The loop body is one basic block (no branches), so the sched barriers pin the
   // order: each MFMA step runs with the next step's fragment reads in flight, and
-  // the loads of tile kt+1 are slotted between the MFMAs of steps 0 and 1 (issuing
-  // them in a burst would hold the in-order MFMA stream behind them).  The scales
-  // of tile kt+1 are read in step 1, from a stage that an earlier barrier made
-  // visible, so that after this tile's barrier only the fragment reads of the next
-  // step are outstanding.  On the last tile the "next" loads fall past K and read
-  // zeros, harmlessly.
+  // the loads are slotted between MFMAs (issuing them in a burst would hold the
+  // in-order MFMA stream behind them).  The scales of tile kt+1 are read in step 1,
+  // from a stage that an earlier barrier made visible.  The barrier sits in the
+  // middle of step 3, whose MFMAs need no LDS: the first half covers the wait, the
+  // second the fragment reads of the next tile.  Loads past K read zeros.
+  constexpr int kF3 = F / 2;                 // weight sub-tiles of step 3 before the barrier
   auto ktile = [&](auto stage_c, int kt) {
     constexpr int st = decltype(stage_c)::value;
+    constexpr int vm0 = kPartBegin[2] - kPartBegin[1], vm1 = kPartBegin[3] - kPartBegin[2];
+    constexpr int vm3 = kPartBegin[1] + (st == 1 ? kScaleOps : 0);
     read_frags(1, st, 1);
-    gload(kt + 1, st ^ 1, 0);
-    if (st == 0) sload((kt >> 1) + 1);                 // kt even: the next pair
+    gload_part(P1{}, kt + 1, st ^ 1);
     Q4_MX_MMA(0, 0)
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    for (int i = 0; i < 5; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+    for (int i = 0; i < kMma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < vm0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_scales(kt + 1);
     read_frags(0, st, 2);
-    gload(kt + 1, st ^ 1, 1);
+    gload_part(P2{}, kt + 1, st ^ 1);
     Q4_MX_MMA(1, 1)
-    __builtin_amdgcn_sched_group_barrier(0x100, 10 + F, 0);
-    for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * F, 0);
+    for (int i = 0; i < kMma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < vm1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(1, st, 3);
     Q4_MX_MMA(2, 0)
-    Q4_READS_THEN_MMA(6)
+    Q4_READS_THEN_MMA(4 + F)
+    __builtin_amdgcn_sched_barrier(0);
+    Q4_MX_MMA_F(3, 1, 0, kF3)
+    if (kF3 > 0) __builtin_amdgcn_sched_group_barrier(0x008, 4 * kF3, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem();
-    // every wave's tile kt+1 has landed, and every read of tile kt has completed
+    // every wave's tile kt+1 has landed, and every read of tile kt has completed:
+    // stage st is free for tile kt+2
     __syncthreads();
     read_frags(0, st ^ 1, 0);
-    Q4_MX_MMA(3, 1)
-    Q4_READS_THEN_MMA(6)
+    gload_part(P0{}, kt + 2, st);
+    if (st == 1) sload((kt + 3) >> 1);                 // kt odd: pair (kt+3)/2
+    Q4_MX_MMA_F(3, 1, kF3, F)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+    for (int i = 0; i < 4 * (F - kF3); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < vm3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     valid_scales(kt + 1);
   };
@@ -249,9 +289,11 @@ __device__ __forceinline__ void mx_tile(
   }
   if (kt < nkt) ktile(std::integral_constant<int, 0>{}, kt);
 #undef Q4_MX_MMA
+#undef Q4_MX_MMA_F
 #undef Q4_READS_THEN_MMA
 
-  __syncthreads();                           // all waves are done reading operand tiles
+  wait_vmem();                               // the loads past K have landed
+  __syncthreads();                           // all waves are done with the operand LDS
   epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds_raw + wave * kStageWaveBytes);
 }
 
@@ -271,14 +313,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   int tm, tn;
   if (bid >= halves) {
     tile_of(bid - halves, tiles_m, tiles_n, kGroupM, &tm, &tn);
-    mx_tile<R, OUT_F32, 2>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,
-                           (int64_t)tn * kBN);
+    mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
+                                (int64_t)tm * kBM, (int64_t)tn * kBN);
   } else {
     const int q = bid;
     tile_of(full + (q >> 1), tiles_m, tiles_n, kGroupM, &tm, &tn);
     if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
-    mx_tile<R, OUT_F32, 1>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy, (int64_t)tm * kBM,
-                           (int64_t)tn * kBN + 128 * (q & 1));
+    mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
+                                (int64_t)tm * kBM, (int64_t)tn * kBN + 128 * (q & 1));
   }
 }
 
