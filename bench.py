@@ -102,7 +102,17 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize_profiles(stats_csv, fetch_csv, write_csv, command):
+def timed_region_avg_ns(trace_csv, steps):
+    """Average duration of the GEMM over its last `steps` dispatches in a rocprofv3
+    kernel trace: the launches of the timed region (the warmup launches come first)."""
+    rows = [r for r in _csv_rows(trace_csv) if r["Kernel_Name"].startswith(GEMM_KERNEL_PREFIX)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[-steps:]]
+    return float(np.mean(d)) if d else None
+
+
+def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None, steps=None,
+                       bench_log=None):
     """Turns the rocprofv3 outputs of a bench run (one --kernel-trace --stats run,
     one --pmc FETCH_SIZE run, one --pmc WRITE_SIZE run) into the committed text
     summary and the traffic record read by measured_traffic().  HBM bytes of the
@@ -148,6 +158,23 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, command):
               f"algorithmic bytes per launch: read {alg_in / 1e6:.2f} MB (A, B codes + scales, t, L2^T), "
               f"write {alg_out / 1e6:.2f} MB (Y bf16); measured / algorithmic = "
               f"{(fetch_b + write_b) / (alg_in + alg_out):.3f}"]
+    if trace_csv and steps:
+        timed_ns = timed_region_avg_ns(trace_csv, steps)
+        if timed_ns:
+            lines += ["", f"GEMM average over the timed region (last {steps} dispatches of the kernel trace, "
+                          f"the launches bench.py times with HIP events): {timed_ns / 1e3:.2f} us -> "
+                          f"{2.0 * M * N * K / (timed_ns * 1e-9) / 1e12:.1f} TFLOP/s "
+                          f"({100 * 2.0 * M * N * K / (timed_ns * 1e-9) / 1e12 / MXFP4_PEAK_TFLOPS:.1f}% "
+                          f"of {MXFP4_PEAK_TFLOPS:.0f}); the stats average above also covers the warmup "
+                          f"launches, run while the clocks ramp up"]
+    if bench_log:
+        with open(bench_log) as f:
+            recs = [json.loads(l) for l in f if l.startswith("{")]
+        if recs and "roofline" in recs[-1]:
+            ev_ms = recs[-1]["roofline"]["avg_launch_ms"]
+            lines += ["", f"bench.py's own line from the same profiled run: GEMM {ev_ms * 1e3:.2f} us by HIP "
+                          f"events around each launch (the events add the gap between the event and "
+                          f"the dispatch to the kernel's own duration)"]
     if gemm_avg_ns:
         lines += ["", f"GEMM average duration {gemm_avg_ns / 1e3:.2f} us -> "
                       f"{2.0 * M * N * K / (gemm_avg_ns * 1e-9) / 1e12:.1f} TFLOP/s "
@@ -311,8 +338,11 @@ def summarize_rows_profile(stats_csv, command):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU's clocks ramp up over the first ~40 ms of sustained load (after an idle
+    # gap the GEMM runs ~25% slower for ~250 steps), so the default warmup is 400 steps
+    # (~65 ms) and the timed region 200 steps (~32 ms), both well inside a second.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true",
                     help="time every other step of the path, one JSON line per row")
@@ -322,9 +352,15 @@ def main():
                     help="write the rocprofv3 summary of `bench.py --rows` under profiles/")
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize: a command line that produced the inputs")
+    ap.add_argument("--bench-log", metavar="LOG",
+                    help="with --summarize: the output of the profiled bench.py run")
+    ap.add_argument("--trace", metavar="TRACE_CSV",
+                    help="with --summarize: the kernel trace of the stats run; the GEMM average "
+                         "over its last --steps dispatches is added")
     a = ap.parse_args()
     if a.summarize:
-        text, rec = summarize_profiles(*a.summarize, a.command)
+        text, rec = summarize_profiles(*a.summarize, a.command, trace_csv=a.trace, steps=a.steps,
+                                       bench_log=a.bench_log)
         with open(os.path.join(ROOT, "profiles", "gemm_mx_mlp_up_4608x3072x12288.md"), "w") as f:
             f.write(text)
         with open(TRAFFIC_FILE, "w") as f:
