@@ -52,7 +52,17 @@ constexpr int kFFull = 512 / (32 * kWaves), kFHalf = kFFull / 2;
 constexpr int kCodeLds = 2 * 2 * kBM * kKTB;          // 131072
 constexpr int kScaleLds = 2 * 2 * kBM * 16;           // 16384
 constexpr int kMainLds = kCodeLds + kScaleLds;
-static_assert((kThreads / 64) * kStageWaveBytes <= kMainLds, "the epilogue stages each wave's output in the operand LDS");
+// epilogue staging rows: 256 bytes wide (one pass for a bf16 tile) with 4 waves and
+// bf16 output, else 128
+template <bool OUT_F32>
+constexpr int mx_stage_row_max() { return kWaves == 4 && !OUT_F32 ? 256 : 128; }
+template <bool OUT_F32, int F>
+constexpr int mx_stage_wave_bytes() {
+  return EpilogueShape<OUT_F32, F, mx_stage_row_max<OUT_F32>()>::kStageWaveBytes;
+}
+static_assert(kWaves * mx_stage_wave_bytes<true, kFFull>() <= kMainLds &&
+                  kWaves * mx_stage_wave_bytes<false, kFFull>() <= kMainLds,
+              "the epilogue stages each wave's output in the operand LDS");
 
 // One output tile of 256 activation rows x kTN weight rows starting at (m0, n0):
 // wave (wm, wn) owns m in [128 wm, +128) and n in [32 F wn, +32 F).
@@ -294,7 +304,8 @@ __device__ __forceinline__ void mx_tile(
 
   wait_vmem();                               // the loads past K have landed
   __syncthreads();                           // all waves are done with the operand LDS
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds_raw + wave * kStageWaveBytes);
+  epilogue_store<OUT_F32, F, mx_stage_row_max<OUT_F32>()>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                                           lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>());
 }
 
 // Workgroups [0, halves) take halves of the leftover tiles (tile full + q/2, weight

@@ -112,8 +112,9 @@ __device__ __forceinline__ void nv_tile(
     lowrank_accumulate<R>(acc, n_base, m_base, M, N, t, l2t, lane);
   }
   __syncthreads();                           // all waves are done reading operand tiles
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes,
-                          R > 0 ? 1.0f : scale);
+  epilogue_store<OUT_F32, F, 128, true>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                                        lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes,
+                                        R > 0 ? 1.0f : scale);
 }
 
 // Workgroups [0, full) take whole 256 x 256 tiles, the rest halves of the leftover

@@ -100,7 +100,8 @@ __device__ __forceinline__ void w4a16_tile(
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
   const int64_t n_base = n0 + wy * 32 * F, m_base = m0 + wx * 128;
   __syncthreads();                           // all waves are done reading operand tiles
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane, lds + wave * kStageWaveBytes);
+  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                          lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
 }
 
 // Workgroups [0, full) take whole 256 x 256 tiles, the rest halves of the leftover

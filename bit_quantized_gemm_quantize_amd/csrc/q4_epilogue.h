@@ -9,6 +9,8 @@
 // the bias and writes bf16 or fp32.
 #pragma once
 
+#include <type_traits>
+
 #include "q4_device.h"
 #include "q4_internal.h"
 
@@ -111,38 +113,46 @@ __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// Output staging through LDS: each wave writes a 128-row x 128-byte slab of its
-// 128 x (32 F) output region into LDS (rows padded to 144 bytes), then reads it
-// back so that every store instruction writes 8 full 128-byte row segments; a pass
-// covers 64 bf16 or 32 fp32 columns.  Direct stores from the MFMA layout would
+// Output staging through LDS: each wave writes a 128-row slab of its 128 x (32 F)
+// output region into LDS, ROW_BYTES wide at most (rows padded by 16 bytes), then
+// reads it back so that every store instruction writes whole 128-byte row segments
+// (8 rows of 128 bytes, or 4 of 256).  Direct stores from the MFMA layout would
 // write 8- or 16-byte pieces of 32 different rows per instruction.
-constexpr int kStageRowBytes = 144;                         // 128 + 16 bytes of padding
-constexpr int kStageWaveBytes = 128 * kStageRowBytes;       // 18432
-constexpr int kEpilogueLdsBytes = 4 * kStageWaveBytes;      // for 4 waves
+template <bool OUT_F32, int F, int ROW_BYTES>
+struct EpilogueShape {
+  static constexpr int kElem = OUT_F32 ? 4 : 2;
+  static constexpr int kFPerPassMax = ROW_BYTES / (32 * kElem);          // 32-column blocks
+  static constexpr int kFPerPass = F < kFPerPassMax ? F : kFPerPassMax;
+  static constexpr int kPasses = F / kFPerPass;
+  static constexpr int kRowBytes = 32 * kFPerPass * kElem;
+  static constexpr int kStageRowBytes = kRowBytes + 16;
+  static constexpr int kStageWaveBytes = 128 * kStageRowBytes;
+};
+// the 4-wave bf16 GEMMs' staging (128-byte rows): what their operand LDS must hold
+constexpr int kStageWaveBytes = EpilogueShape<false, 4, 128>::kStageWaveBytes;   // 18432
+constexpr int kEpilogueLdsBytes = 4 * EpilogueShape<true, 4, 128>::kStageWaveBytes;
 
-// y = scale * acc + bias.  The scale and the bias are applied pass by pass, so
-// only the accumulators being staged are moved out of the matrix registers.
-template <bool OUT_F32, int F>
+// y = scale * acc + bias (SCALED), or acc + bias.  The bias is added, and the
+// scale applied, pass by pass, so only the accumulators being staged are moved out
+// of the matrix registers; without a bias the add is skipped.
+template <bool OUT_F32, int F, int ROW_BYTES = 128, bool SCALED = false>
 __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
                                                int64_t M, int64_t N,
                                                const uint16_t* __restrict__ bias, void* y,
                                                int64_t ldy, int lane, uint8_t* stage,
                                                float scale = 1.0f) {
+  using S = EpilogueShape<OUT_F32, F, ROW_BYTES>;
   const int r32 = lane & 31, h = lane >> 5;
-  constexpr int kElem = OUT_F32 ? 4 : 2;
-  constexpr int kFPerPass = (OUT_F32 || F == 1) ? 1 : 2;   // 32-column blocks per pass
-  constexpr int kPasses = F / kFPerPass;
+  constexpr int kElem = S::kElem;
+  constexpr int kFPerPass = S::kFPerPass;
   constexpr int kColsPerPass = 32 * kFPerPass;
-  constexpr int kRowBytes = kColsPerPass * kElem;  // 128 (or 64: bf16 with F = 1)
+  constexpr int kRowBytes = S::kRowBytes;
+  constexpr int kStageRow = S::kStageRowBytes;
   constexpr int kLanesPerRow = kRowBytes / 16;
   constexpr int kRowsPerStore = 64 / kLanesPerRow;
   constexpr int kPer16 = 16 / kElem;             // elements per 16-byte store
-#pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass) {
-    if (pass > 0) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): previous pass read back
-      __builtin_amdgcn_wave_barrier();
-    }
+  auto pass_body = [&](auto has_bias_c, int pass) {
+    constexpr bool kBias = decltype(has_bias_c)::value;
     // registers -> LDS: row m_local = 32 g + lane%32, columns 32 f' + 8 vq + 4 h .. +3
 #pragma unroll
     for (int fp = 0; fp < kFPerPass; ++fp) {
@@ -152,17 +162,21 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
         // bias of the 4 consecutive columns this lane holds in register group vq
         const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
         float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (bias) {
+        if (kBias && bias != nullptr) {        // the fp32 path adds zeros without a bias
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint8_t* dst = stage + (32 * g + r32) * kStageRowBytes + (32 * fp + 8 * vq + 4 * h) * kElem;
+          uint8_t* dst = stage + (32 * g + r32) * kStageRow + (32 * fp + 8 * vq + 4 * h) * kElem;
           float a[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) a[j] = __builtin_fmaf(acc[f][g][4 * vq + j], scale, b[j]);
+          for (int j = 0; j < 4; ++j) {
+            a[j] = acc[f][g][4 * vq + j];
+            if (SCALED) a[j] = kBias ? __builtin_fmaf(a[j], scale, b[j]) : a[j] * scale;
+            else if (kBias) a[j] += b[j];
+          }
           if (OUT_F32) {
             *reinterpret_cast<v4f*>(dst) = v4f{a[0], a[1], a[2], a[3]};
           } else {
@@ -175,6 +189,17 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
         }
       }
     }
+  };
+#pragma unroll
+  for (int pass = 0; pass < S::kPasses; ++pass) {
+    if (pass > 0) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): previous pass read back
+      __builtin_amdgcn_wave_barrier();
+    }
+    // fp32 output keeps one path (a second copy of the pass made the compiler spill);
+    // it reads the bias only when there is one
+    if (OUT_F32 || bias) pass_body(std::true_type{}, pass);
+    else pass_body(std::false_type{}, pass);
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     // LDS -> global: kLanesPerRow lanes per row (16 bytes each), whole row segments
@@ -184,7 +209,7 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
     for (int it = 0; it < 128 / kRowsPerStore; ++it) {
       const int ml = kRowsPerStore * it + lane / kLanesPerRow;
       const int64_t m = m_base + ml;
-      const u32x4 v = ld16(stage + ml * kStageRowBytes + col_bytes);
+      const u32x4 v = ld16(stage + ml * kStageRow + col_bytes);
       if (m < M) {
         uint8_t* dst = static_cast<uint8_t*>(y) + (m * ldy + n) * kElem;
         if (n + kPer16 <= N) {
