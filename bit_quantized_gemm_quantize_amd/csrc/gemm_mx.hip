@@ -327,11 +327,24 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
                                 (int64_t)tm * kBM, (int64_t)tn * kBN);
   } else {
+    // Workgroup q runs on XCD q % 8.  When the leftover tiles split evenly over the
+    // XCDs, each XCD takes both halves of the leftover tiles that tile_of assigns to
+    // it, so the two halves of a tile share its activation rows in one L2; else
+    // halves q and q+1 are the two halves of tile full + q/2.
     const int q = bid;
-    tile_of(full + (q >> 1), tiles_m, tiles_n, kGroupM, &tm, &tn);
-    if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
+    int vt, half;
+    if ((full & 7) == 0 && ((tiles_m * tiles_n - full) & 7) == 0) {
+      const int j = q >> 3;
+      vt = full + (q & 7) + 8 * (j >> 1);
+      half = j & 1;
+    } else {
+      vt = full + (q >> 1);
+      half = q & 1;
+    }
+    tile_of(vt, tiles_m, tiles_n, kGroupM, &tm, &tn);
+    if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
     mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
-                                (int64_t)tm * kBM, (int64_t)tn * kBN + 128 * (q & 1));
+                                (int64_t)tm * kBM, (int64_t)tn * kBN + 128 * half);
   }
 }
 
