@@ -8,13 +8,17 @@
 // 16-byte chunks XOR-swizzled by row, two stages, one barrier per K-tile.
 //
 // A loader policy turns global data into bf16 LDS rows:
-//   Loader::issue(kt, lds_a, lds_b)   issue the global reads of K-tile kt (into
-//                                    registers, or straight into LDS)
+//   Loader::issue_regs(kt)            issue the global reads of K-tile kt that land
+//                                    in registers (Loader::kRegLoads instructions)
+//   Loader::issue_lds(kt, lds_a, lds_b)  issue those that go straight into LDS
 //   Loader::store<P>(lds_a, lds_b)    convert half P (0, 1) of the registers and
 //                                    write it
-// Pipeline: the reads of tile kt+1 go out before tile kt is multiplied; its
-// conversion is spread over the last two MFMA steps of tile kt; the fragments of
-// the next MFMA step are read while the current step's MFMAs run.
+// Pipeline of K-tile kt: the fragments of the next MFMA step are read while the
+// current step's MFMAs run; the registers of K-tile kt+1 are converted into the
+// other stage during steps 1 and 2 and then reloaded with K-tile kt+2; the barrier
+// sits in the middle of step 3, whose MFMAs need no LDS, so the first half covers
+// the wait and the second the fragment reads of K-tile kt+1 and the issue of
+// K-tile kt+2's direct-to-LDS loads into the stage just freed.
 #pragma once
 
 #include "q4_epilogue.h"
@@ -54,16 +58,16 @@ __device__ __forceinline__ void bf16_read_frags(Bf16Frags<F>& fr, const uint8_t*
   for (int f = 0; f < F; ++f) fr.b[BUF][f] = ld16(pb + f * 32 * kBf16RowBytes);
 }
 
-// acc[f][g] holds D[n][m] (A operand = weight rows, B operand = activation rows).
-template <int BUF, int F>
+// acc[f][g] holds D[n][m] (A operand = weight rows, B operand = activation rows);
+// weight sub-tiles f in [F0, F1).
+template <int BUF, int F, int F0 = 0, int F1 = F>
 __device__ __forceinline__ void bf16_mma(v16f (&acc)[F][4], const Bf16Frags<F>& fr) {
 #pragma unroll
-  for (int f = 0; f < F; ++f)
+  for (int f = F0; f < F1; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = mfma_bf16_32x32x16(fr.b[BUF][f], fr.a[BUF][g], acc[f][g]);
 }
 
-// One K-tile: multiply stage `cur` while tile kt+1 is read and converted into `nxt`.
 // Stage st of the operand tiles: A at lds + st * tile, B at lds + (2 + st) * tile,
 // so the stage offsets fold into the LDS instructions' immediate offsets.
 template <int ST>
@@ -71,24 +75,81 @@ __device__ __forceinline__ uint8_t* bf16_a(uint8_t* lds) { return lds + ST * kBf
 template <int ST>
 __device__ __forceinline__ uint8_t* bf16_b(uint8_t* lds) { return lds + (2 + ST) * kBf16TileBytes; }
 
-// One K-tile: multiply stage CUR while tile kt+1 is read and converted into the other.
-// The sched group barriers interleave the loads of the first step and the
-// conversion arithmetic of the last two with single MFMAs, so that the in-order
-// wave keeps the matrix pipe fed (Loader::kValuPerStore: VALU ops of one store part).
+// One K-tile: multiply stage CUR while K-tile kt+1 is converted into the other.
+// The sched group barriers interleave the conversion arithmetic and the loads with
+// single MFMAs, so that the in-order wave keeps the matrix pipe fed
+// (Loader::kValuPerStore: VALU ops of one store part).
 template <int CUR, int F, class Loader>
 __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, Loader& ld, int kt,
                                            uint8_t* lds, int wx, int wy, int lane) {
   constexpr int NXT = CUR ^ 1;
   constexpr int kMma = 4 * F;                                  // MFMAs per step
   constexpr int kValu = (Loader::kValuPerStore + kMma - 1) / kMma;
-  ld.issue(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  constexpr int kH = F / 2;                                    // sub-tiles of step 3 before the barrier
+  // step 0
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
   bf16_mma<0, F>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);       // fragment reads first
+  __builtin_amdgcn_sched_group_barrier(0x008, kMma, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // step 1: half 0 of K-tile kt+1 into the other stage
+  bf16_read_frags<0, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
+  ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  bf16_mma<1, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // global read
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);         // its address arithmetic
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);     // conversion arithmetic
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);           // LDS writes of the part
+  __builtin_amdgcn_sched_barrier(0);
+  // step 2: half 1, then the register loads of K-tile kt+2
+  bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
+  ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  ld.issue_regs(kt + 2);
+  bf16_mma<0, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+  for (int i = 0; i < kMma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x020, Loader::kRegLoads, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // step 3
+  bf16_mma<1, F, 0, kH>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4 * kH, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<Loader::kRegLoads>();           // K-tile kt+1's loads into LDS have landed
+  // every wave has written stage NXT and finished reading stage CUR
+  lds_barrier();
+  bf16_read_frags<0, F>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
+  ld.issue_lds(kt + 2, bf16_a<CUR>(lds), bf16_b<CUR>(lds));
+  bf16_mma<1, F, kH, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4 * (F - kH), 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same K-tile for loaders whose conversion is heavy (Loader::kLateStores): the
+// register loads of K-tile kt+1 go out in step 0, its conversion fills steps 2 and
+// 3, and the barrier closes the K-tile.  Converting in steps 1 and 2 instead would
+// leave the heavy arithmetic less latency cover for the loads it waits on.
+template <int CUR, int F, class Loader>
+__device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][4], Bf16Frags<F>& fr, Loader& ld,
+                                                int kt, uint8_t* lds, int wx, int wy, int lane) {
+  constexpr int NXT = CUR ^ 1;
+  constexpr int kMma = 4 * F;
+  constexpr int kValu = (Loader::kValuPerStore + kMma - 1) / kMma;
+  ld.issue_regs(kt + 1);
+  ld.issue_lds(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
+  bf16_mma<0, F>(acc, fr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
+  for (int i = 0; i < kMma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   bf16_read_frags<0, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
@@ -104,7 +165,7 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, 
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);           // LDS writes of the part
+  __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
   ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_mma<1, F>(acc, fr);
@@ -114,8 +175,7 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, 
   }
   __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmem();                               // loads straight into LDS have landed
-  // every wave has written stage NXT and finished reading stage CUR
+  wait_vmem();
   lds_barrier();
   bf16_read_frags<0, F>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
 }
@@ -130,11 +190,30 @@ __device__ __forceinline__ void bf16_mainloop(v16f (&acc)[F][4], Loader& ld, int
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
   if (nkt == 0) return;
   Bf16Frags<F> fr;
-  ld.issue(0, bf16_a<0>(lds), bf16_b<0>(lds));
-  ld.template store<0>(bf16_a<0>(lds), bf16_b<0>(lds));
+  if constexpr (Loader::kLateStores) {
+    ld.issue_lds(0, bf16_a<0>(lds), bf16_b<0>(lds));
+    ld.issue_regs(0);
+    ld.template store<0>(bf16_a<0>(lds), bf16_b<0>(lds));
+    ld.template store<1>(bf16_a<0>(lds), bf16_b<0>(lds));
+    wait_vmem();
+    lds_barrier();
+    bf16_read_frags<0, F>(fr, bf16_a<0>(lds), bf16_b<0>(lds), 0, wx, wy, lane);
+    int kt = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+      bf16_ktile_late<0, F>(acc, fr, ld, kt, lds, wx, wy, lane);
+      bf16_ktile_late<1, F>(acc, fr, ld, kt + 1, lds, wx, wy, lane);
+    }
+    if (kt < nkt) bf16_ktile_late<0, F>(acc, fr, ld, kt, lds, wx, wy, lane);
+    return;
+  }
+  ld.issue_lds(0, bf16_a<0>(lds), bf16_b<0>(lds));
+  ld.issue_regs(0);
+  ld.template store<0>(bf16_a<0>(lds), bf16_b<0>(lds));   // waits for the loads issued so far
   ld.template store<1>(bf16_a<0>(lds), bf16_b<0>(lds));
-  wait_vmem();
+  ld.issue_regs(1);
+  wait_vmcnt<Loader::kRegLoads>();
   lds_barrier();
+  ld.issue_lds(1, bf16_a<1>(lds), bf16_b<1>(lds));
   bf16_read_frags<0, F>(fr, bf16_a<0>(lds), bf16_b<0>(lds), 0, wx, wy, lane);
   // two K-tiles per trip so that the stages are static; reads past K return zeros,
   // which are converted into a stage nobody multiplies
@@ -144,6 +223,7 @@ __device__ __forceinline__ void bf16_mainloop(v16f (&acc)[F][4], Loader& ld, int
     bf16_ktile<1, F>(acc, fr, ld, kt + 1, lds, wx, wy, lane);
   }
   if (kt < nkt) bf16_ktile<0, F>(acc, fr, ld, kt, lds, wx, wy, lane);
+  wait_vmem();                               // the loads past K have landed before LDS is reused
 }
 
 // Output tiles: the 256 x 256 tiles that do not fill a last round over the CUs

@@ -36,6 +36,8 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
 template <int TN>
 struct NvLoader {
   static constexpr int kValuPerStore = 192;   // VALU ops of one store part (about)
+  static constexpr int kRegLoads = 4 + 2 * (TN / 128);   // VMEM instructions of issue_regs
+  static constexpr bool kLateStores = true;   // heavy conversion: see bf16_ktile_late
   __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
   uint32_t kb, sbytes, nchunk;
   int tid;
@@ -53,7 +55,8 @@ struct NvLoader {
     rsb = make_rsrc(bs + n0 * sbytes, rb * sbytes);
     tid = t;
   }
-  __device__ __forceinline__ void issue(int kt, uint8_t*, uint8_t*) {
+  __device__ __forceinline__ void issue_lds(int, uint8_t*, uint8_t*) {}   // all through registers
+  __device__ __forceinline__ void issue_regs(int kt) {
     const uint32_t chunk = (uint32_t)kt * 2 + (tid & 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

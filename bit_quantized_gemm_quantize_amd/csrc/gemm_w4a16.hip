@@ -34,6 +34,8 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
 template <int TN>
 struct W4A16Loader {
   static constexpr int kValuPerStore = 96;   // VALU ops of one store part (about)
+  static constexpr int kRegLoads = 3 * (TN / 128);   // VMEM instructions of issue_regs
+  static constexpr bool kLateStores = false;
   __amdgpu_buffer_rsrc_t rx, rc, rs, rz;
   uint32_t ldxb, kb, ngrp;
   int tid;
@@ -52,7 +54,7 @@ struct W4A16Loader {
     rz = make_rsrc(wz + n0 * ngrp, rb * ngrp * 2);
     tid = t;
   }
-  __device__ __forceinline__ void issue(int kt, uint8_t* la, uint8_t*) {
+  __device__ __forceinline__ void issue_lds(int kt, uint8_t* la, uint8_t*) {
     const int lane = tid & 63, wave = tid >> 6;
     const uint32_t lr = lane >> 3, lp = lane & 7;
 #pragma unroll
@@ -61,6 +63,8 @@ struct W4A16Loader {
       const uint32_t off = in_range_or_oob(row * ldxb + (uint32_t)kt * 128 + ((lp ^ lr) << 4), (uint32_t)kt, ngrp);
       buf_ld16_lds(rx, la + (64 * wave + 8 * j) * kBf16RowBytes, off);
     }
+  }
+  __device__ __forceinline__ void issue_regs(int kt) {
     const uint32_t cw = tid & 1;
 #pragma unroll
     for (int j = 0; j < TN / 128; ++j) {
