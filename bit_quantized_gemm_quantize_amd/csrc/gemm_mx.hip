@@ -308,10 +308,8 @@ __device__ __forceinline__ void mx_tile(
                                            lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>());
 }
 
-// Workgroups [0, halves) take halves of the leftover tiles (tile full + q/2, weight
-// rows 128 (q % 2) .. +127), the rest whole tiles.  Running the halves first puts
-// the CUs that took one half tile a half tile out of step with the others, so the
-// output stores of the two sets fall at different times instead of all at once.
+// Whole tiles and halves of the leftover ones (weight rows 128 h .. +127): see
+// tile_unit.
 template <int R, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
@@ -319,29 +317,13 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int tiles_m, int tiles_n, int full) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
-  const int halves = 2 * (tiles_m * tiles_n - full);
-  const int bid = blockIdx.x;
-  int tm, tn;
-  if (bid >= halves) {
-    tile_of(bid - halves, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  int vt, half, tm, tn;
+  const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
+  tile_of(vt, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  if (!is_half) {
     mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
                                 (int64_t)tm * kBM, (int64_t)tn * kBN);
   } else {
-    // Workgroup q runs on XCD q % 8.  When the leftover tiles split evenly over the
-    // XCDs, each XCD takes both halves of the leftover tiles that tile_of assigns to
-    // it, so the two halves of a tile share its activation rows in one L2; else
-    // halves q and q+1 are the two halves of tile full + q/2.
-    const int q = bid;
-    int vt, half;
-    if ((full & 7) == 0 && ((tiles_m * tiles_n - full) & 7) == 0) {
-      const int j = q >> 3;
-      vt = full + (q & 7) + 8 * (j >> 1);
-      half = j & 1;
-    } else {
-      vt = full + (q >> 1);
-      half = q & 1;
-    }
-    tile_of(vt, tiles_m, tiles_n, kGroupM, &tm, &tn);
     if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
     mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
                                 (int64_t)tm * kBM, (int64_t)tn * kBN + 128 * half);

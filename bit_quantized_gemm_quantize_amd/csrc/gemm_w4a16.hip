@@ -108,8 +108,7 @@ __device__ __forceinline__ void w4a16_tile(
                           lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
 }
 
-// Workgroups [0, full) take whole 256 x 256 tiles, the rest halves of the leftover
-// tiles (256 x 128).
+// Whole 256 x 256 tiles and halves (256 x 128) of the leftover ones: see tile_unit.
 template <bool OUT_F32>
 __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
@@ -118,18 +117,16 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
     int full) {
   static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
-  const int bid = blockIdx.x;
-  int tm, tn;
-  if (bid < full) {
-    tile_of(bid, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+  int vt, half, tm, tn;
+  const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
+  tile_of(vt, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+  if (!is_half) {
     w4a16_tile<OUT_F32, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
                            (int64_t)tn * kBf16BN);
   } else {
-    const int q = bid - full;
-    tile_of(full + (q >> 1), tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
-    if ((int64_t)tn * 256 + 128 * (q & 1) >= N) return;   // half past the last weight row
+    if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
     w4a16_tile<OUT_F32, 2>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
-                           (int64_t)tn * kBf16BN + 128 * (q & 1));
+                           (int64_t)tn * kBf16BN + 128 * half);
   }
 }
 

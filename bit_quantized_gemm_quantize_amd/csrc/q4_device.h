@@ -125,6 +125,34 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
   *tn = in / gm;
 }
 
+// Work units of a GEMM launch whose leftover tiles (those that do not fill a last
+// round over the CUs) run as two halves each: workgroups [0, 2 (tiles - full)) take
+// half tiles, the rest whole ones.  Running the halves first puts the CUs that took
+// one half a half tile out of step with the others, so the output stores of the two
+// sets do not all fall at once.  A whole tile gets the virtual index bid - halves
+// for tile_of (whose XCD assignment holds when halves is a multiple of 8).  Half q
+// runs on XCD q % 8: when the leftover tiles split evenly over the XCDs, it takes
+// one half of a leftover tile that tile_of gives that XCD, so both halves of a tile
+// share their activation rows in one L2; else halves q and q+1 split tile full + q/2.
+// Returns whether the unit is a half tile (*half: which half).
+__device__ __forceinline__ bool tile_unit(int bid, int tiles, int full, int* vt, int* half) {
+  const int halves = 2 * (tiles - full);
+  if (bid >= halves) {
+    *vt = bid - halves;
+    *half = 0;
+    return false;
+  }
+  if ((full & 7) == 0 && ((tiles - full) & 7) == 0) {
+    const int j = bid >> 3;
+    *vt = full + (bid & 7) + 8 * (j >> 1);
+    *half = j & 1;
+  } else {
+    *vt = full + (bid >> 1);
+    *half = bid & 1;
+  }
+  return true;
+}
+
 }  // namespace q4
 
 namespace q4 {
