@@ -186,7 +186,7 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None,
     return "\n".join(lines) + "\n", rec
 
 
-def bench_rows(reps=20):
+def bench_rows(reps=50):
     """Times every other step of the path on its own workload and prints one JSON
     line per row: the quantizers and packers against the HBM peak (algorithmic
     bytes: X read once, codes and scales written once), the GEMMs against their MFMA
@@ -207,10 +207,20 @@ def bench_rows(reps=20):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     def timed(fn, n_sets):
-        for i in range(3):
-            fn(i % n_sets)
+        # The clocks need about 40 ms of sustained load to settle after an idle gap
+        # (the host work between rows is one): run about 80 ms of this launch back to
+        # back, sized from one cold launch, before the timed launches.
+        fn(0)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(1 % n_sets)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n_warm = max(3, min(20000, int(80.0 / max(e0.elapsed_time(e1), 1e-3))))
+        for i in range(n_warm):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
         e0.record(stream)
         for i in range(reps):
             fn(i % n_sets)
