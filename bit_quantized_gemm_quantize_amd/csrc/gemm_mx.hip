@@ -64,49 +64,54 @@ static_assert(kWaves * mx_stage_wave_bytes<true, kFFull>() <= kMainLds &&
                   kWaves * mx_stage_wave_bytes<false, kFFull>() <= kMainLds,
               "the epilogue stages each wave's output in the operand LDS");
 
-// One output tile of 256 activation rows x kTN weight rows starting at (m0, n0):
-// wave (wm, wn) owns m in [128 wm, +128) and n in [32 F wn, +32 F).
-template <int R, bool OUT_F32, int F>
-__device__ __forceinline__ void mx_tile(
-    uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
-    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
-    const float* __restrict__ t, const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias,
-    void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
-  constexpr int kTN = 16 * F * kWaves;           // weight rows of this tile
-  constexpr int kRowsA = kBM / kWaves, kRowsB = kTN / kWaves;   // rows each wave loads
-  constexpr int kMma = 4 * F;                    // MFMAs per wave per step
-  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
-  auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave >> 1, wm = wave & 1;       // wave's n quarter, m half
-  const int r32 = lane & 31, h = lane >> 5;
-  const uint32_t kbytes = (uint32_t)(K >> 1), nblk = (uint32_t)(K >> 5);
-  const int nkt = (int)((K + kKT - 1) / kKT);
-  const uint32_t rows_a = rows_in(kBM, M, m0), rows_b = rows_in(kTN, N, n0);
-
-  // buffer views of this tile's rows: rows past M / N read as zero
-  const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
-  const auto rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
-  const auto rs_a = make_rsrc(as + m0 * nblk, rows_a * nblk);
-  const auto rs_b = make_rsrc(bs + n0 * nblk, rows_b * nblk);
-
+// The operand views of one output tile of 256 activation rows x kTN weight rows
+// starting at (m0, n0), and the loads into LDS that feed its K loop.
+template <int F>
+struct MxLoads {
+  static constexpr int kTN = 16 * F * kWaves;                   // weight rows of the tile
+  static constexpr int kRowsA = kBM / kWaves, kRowsB = kTN / kWaves;   // rows each wave loads
   // codes, global -> LDS: each wave moves 8 rows x 128 bytes per instruction straight
   // into LDS (lane i -> row i/8, stored position i%8, which holds global chunk
-  // (i%8) ^ (row & 7), the swizzle).  Wave w covers activation rows kRowsA w .. +kRowsA-1
-  // and weight rows kRowsB w .. +kRowsB-1: kNL instructions per K-tile, issued in
-  // three parts (instructions [kPartBegin[p], kPartBegin[p+1])).
-  constexpr int kNA = kRowsA / 8, kNL = kNA + kRowsB / 8;
-  constexpr int kPart0 = kNL / 3, kPart1 = (kNL - kPart0) / 2;
-  constexpr int kPartBegin[4] = {0, kPart0, kPart0 + kPart1, kNL};
-  const int lr = lane >> 3, lp = lane & 7;
-  auto gload_part = [&](auto part_c, int kt, int stage) {
-    constexpr int part = decltype(part_c)::value;
+  // (i%8) ^ (row & 7), the swizzle).  Wave w covers activation rows kRowsA w ..
+  // +kRowsA-1 and weight rows kRowsB w .. +kRowsB-1: kNL instructions per K-tile,
+  // issued in three parts (instructions [begin(p), begin(p+1))).
+  static constexpr int kNA = kRowsA / 8, kNL = kNA + kRowsB / 8;
+  static constexpr int kPart0 = kNL / 3, kPart1 = (kNL - kPart0) / 2;
+  static constexpr int begin(int p) { return p == 0 ? 0 : p == 1 ? kPart0 : p == 2 ? kPart0 + kPart1 : kNL; }
+  static constexpr int kScaleOps = kWaves == 8 ? 1 : 2;        // scale loads per wave per pair
+
+  uint8_t* lds_raw;
+  __amdgpu_buffer_rsrc_t rc_a, rc_b, rs_a, rs_b;
+  uint32_t kbytes, nblk, rows_a, rows_b;
+  int wave, lane;
+
+  __device__ __forceinline__ MxLoads(uint8_t* lds, const uint8_t* ac, const uint8_t* as,
+                                     const uint8_t* bc, const uint8_t* bs, int64_t M, int64_t N,
+                                     int64_t K, int64_t m0, int64_t n0)
+      : lds_raw(lds) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // opaque: keeps per-tile address math inside the tile loop
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    kbytes = (uint32_t)(K >> 1);
+    nblk = (uint32_t)(K >> 5);
+    rows_a = rows_in(kBM, M, m0);
+    rows_b = rows_in(kTN, N, n0);
+    // buffer views of this tile's rows: rows past M / N read as zero
+    rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
+    rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
+    rs_a = make_rsrc(as + m0 * nblk, rows_a * nblk);
+    rs_b = make_rsrc(bs + n0 * nblk, rows_b * nblk);
+  }
+
+  template <int PART>
+  __device__ __forceinline__ void gload_part(int kt, int stage) const {
+    auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
+    const int lr = lane >> 3, lp = lane & 7;
     const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
     const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
 #pragma unroll
-    for (int idx = kPartBegin[part]; idx < kPartBegin[part + 1]; ++idx) {
+    for (int idx = begin(PART); idx < begin(PART + 1); ++idx) {
       const int op = idx < kNA ? 0 : 1;
       const int per = op == 0 ? kRowsA : kRowsB;
       const int j = op == 0 ? idx : idx - kNA;
@@ -115,17 +120,15 @@ __device__ __forceinline__ void mx_tile(
       buf_ld16_lds(op == 0 ? rc_a : rc_b, &lds[op][stage][(per * wave + 8 * j) * kKTB],
                    row * kbytes + koff);
     }
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
+  }
+
   // scales, global -> LDS, once per pair of K-tiles: 64 rows per instruction (lane i
   // takes row 64 sw + i, 16 bytes = the scale bytes of K-tiles 2p and 2p+1 of pair
   // p) into scale stage p % 2.  With 8 waves, waves 0-3 take the activation rows
   // and waves 4-7 the weight rows; with 4, every wave takes both.
-  constexpr int kScaleOps = kWaves == 8 ? 1 : 2;        // scale loads per wave per pair
-  const int sw = wave & 3;
-  auto sload = [&](int p) {
+  __device__ __forceinline__ void sload(int p) const {
+    auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
+    const int sw = wave & 3;
     const uint32_t b0 = (uint32_t)p * 16;
     const uint32_t koff = b0 < nblk ? b0 : kOOB;
     const uint32_t off = (64 * sw + lane) * nblk + koff;
@@ -134,7 +137,82 @@ __device__ __forceinline__ void mx_tile(
       const int op = kWaves == 8 ? (wave >> 2) : k;
       buf_ld16_lds(op == 0 ? rs_a : rs_b, &lsc[p & 1][op][64 * sw * 16], off);
     }
+  }
+
+  // What the tile's K loop needs in LDS before it starts: K-tile 0 (stage 0), the
+  // first two scale pairs, and for the low-rank term the tile's t rows and L2^T rows
+  // (contiguous in memory), in the second, still unused stage of the activation and
+  // weight tiles.
+  template <int R>
+  __device__ __forceinline__ void prologue(int nkt, const float* __restrict__ t,
+                                           const uint16_t* __restrict__ l2t, int64_t m0,
+                                           int64_t n0) const {
+    if (nkt > 0) {
+      gload_part<0>(0, 0);
+      gload_part<1>(0, 0);
+      gload_part<2>(0, 0);
+      sload(0);
+      sload(1);
+    }
+    if (R > 0) {
+      auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
+      const auto rt = make_rsrc(t + m0 * R, rows_a * (uint32_t)(4 * R));
+      const auto rl = make_rsrc(l2t + n0 * R, rows_b * (uint32_t)(2 * R));
+      uint8_t* lt = &lds[0][1][0];                 // kBM * 4R <= 32 KB
+      uint8_t* ll = &lds[1][1][0];                 // kTN * 2R <= 16 KB
+      constexpr int kPiecesT = kBM * 4 * R / 1024;  // kBM * 4R bytes in 1 KB pieces
+#pragma unroll
+      for (int j = 0; j < kPiecesT / kWaves; ++j) {
+        const int piece = wave * (kPiecesT / kWaves) + j;
+        buf_ld16_lds(rt, lt + piece * 1024, piece * 1024 + lane * 16);
+      }
+      constexpr int kPieces = kTN * 2 * R / 1024;  // kTN * 2R bytes
+#pragma unroll
+      for (int j = 0; j < (kPieces + kWaves - 1) / kWaves; ++j) {
+        const int piece = j * kWaves + wave;
+        if (piece < kPieces) buf_ld16_lds(rl, ll + piece * 1024, piece * 1024 + lane * 16);
+      }
+    }
+  }
+};
+
+// One output tile of 256 activation rows x kTN weight rows starting at (m0, n0),
+// whose prologue loads (MxLoads::prologue) are already issued: wave (wm, wn) owns m
+// in [128 wm, +128) and n in [32 F wn, +32 F).  `pending` is the number of this
+// wave's stores from the previous tile still queued behind those loads.  Once the
+// tile's LDS is free again, issue_next() queues the next tile's prologue loads; the
+// return value is the number of stores queued after them.
+template <int R, bool OUT_F32, int F, class Next>
+__device__ __forceinline__ int mx_tile(
+    uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0,
+    int pending, Next&& issue_next) {
+  using L = MxLoads<F>;
+  constexpr int kMma = 4 * F;                    // MFMAs per wave per step
+  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
+  auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
+  const L ld(lds_raw, ac, as, bc, bs, M, N, K, m0, n0);
+
+  // opaque thread index: the compiler would otherwise hoist the tile's address math
+  // out of the persistent loop, for both tile shapes, and run out of registers
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 1, wm = wave & 1;       // wave's n quarter, m half
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t nblk = (uint32_t)(K >> 5);
+  const int nkt = (int)((K + kKT - 1) / kKT);
+  constexpr int kPartBegin[4] = {L::begin(0), L::begin(1), L::begin(2), L::begin(3)};
+  constexpr int kScaleOps = L::kScaleOps;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  auto gload_part = [&](auto part_c, int kt, int stage) {
+    ld.template gload_part<decltype(part_c)::value>(kt, stage);
   };
+  auto sload = [&](int p) { ld.sload(p); };
   // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3,
   // at byte 8 (kt % 2) + 4h of the row's 16 bytes in scale stage (kt / 2) % 2.
   // Read raw; valid_scales() replaces the words of blocks past K (whose codes are
@@ -195,37 +273,16 @@ __device__ __forceinline__ void mx_tile(
   // (parts 1 and 2), and are waited for at the barrier inside step 3 of K-tile kt:
   // nearly a whole K-tile of latency cover.  Scale pair q is loaded with part 0 of
   // K-tile 2q-1, and read (for K-tile 2q) in step 1 of K-tile 2q-1.
-  if (nkt > 0) {
-    gload_part(P0{}, 0, 0);
-    gload_part(P1{}, 0, 0);
-    gload_part(P2{}, 0, 0);
-    sload(0);
-    sload(1);
-  }
-  // The low-rank term t L2 goes into the accumulators first.  The tile's t rows
-  // and L2^T rows (contiguous in memory) are loaded into the second, still unused
-  // stage of the activation and weight tiles together with the first K-tile, so the
-  // epilogue is left with the bias and the store.
-  if (R > 0) {
-    const auto rt = make_rsrc(t + m0 * R, rows_a * (uint32_t)(4 * R));
-    const auto rl = make_rsrc(l2t + n0 * R, rows_b * (uint32_t)(2 * R));
-    uint8_t* lt = &lds[0][1][0];                 // kBM * 4R <= 32 KB
-    uint8_t* ll = &lds[1][1][0];                 // kTN * 2R <= 16 KB
-    constexpr int kPiecesT = kBM * 4 * R / 1024;  // kBM * 4R bytes in 1 KB pieces
-#pragma unroll
-    for (int j = 0; j < kPiecesT / kWaves; ++j) {
-      const int piece = wave * (kPiecesT / kWaves) + j;
-      buf_ld16_lds(rt, lt + piece * 1024, piece * 1024 + lane * 16);
-    }
-    constexpr int kPieces = kTN * 2 * R / 1024;  // kTN * 2R bytes
-#pragma unroll
-    for (int j = 0; j < (kPieces + kWaves - 1) / kWaves; ++j) {
-      const int piece = j * kWaves + wave;
-      if (piece < kPieces) buf_ld16_lds(rl, ll + piece * 1024, piece * 1024 + lane * 16);
-    }
-  }
-  wait_vmem();
-  __syncthreads();
+  //
+  // The prologue loads were queued before the previous tile's stores, and vector
+  // memory operations complete in order: waiting until only those stores are
+  // outstanding waits for the loads alone.
+  if (pending == RegEpilogue<kFFull>::kStores) wait_vmcnt<RegEpilogue<kFFull>::kStores>();
+  else if (pending == RegEpilogue<kFHalf>::kStores) wait_vmcnt<RegEpilogue<kFHalf>::kStores>();
+  else wait_vmem();
+  barrier_after_wait();
+  // The low-rank term t L2 goes into the accumulators first (its operands came
+  // with the prologue), so the epilogue is left with the bias and the store.
   if (R > 0) {
     lowrank_accumulate_lds<R>(acc, &lds[0][1][0], &lds[1][1][0], 128 * wm, 32 * F * wn, lane);
     lds_barrier();                           // stage 1 is free again for K-tile 1
@@ -304,29 +361,75 @@ __device__ __forceinline__ void mx_tile(
 
   wait_vmem();                               // the loads past K have landed
   __syncthreads();                           // all waves are done with the operand LDS
-  epilogue_store<OUT_F32, F, mx_stage_row_max<OUT_F32>()>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
-                                           lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>());
+  uint8_t* stage = lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>();
+  // A wave region inside the output, bf16: staged into registers, so that the LDS is
+  // free for the next tile's loads before the stores go out.  Otherwise (edges, fp32)
+  // staged and stored pass by pass.
+  const bool regs = !OUT_F32 && m_base + 128 <= M && n_base + 32 * F <= N;
+  u32x4 out[RegEpilogue<F>::kStores];
+  if (regs) epilogue_stage_to_regs<F>(acc, n_base, N, bias, lane, stage, out);
+  else epilogue_store<OUT_F32, F, mx_stage_row_max<OUT_F32>()>(acc, n_base, m_base, M, N, bias, y, ldy,
+                                                               lane, stage);
+  lds_barrier();
+  issue_next();
+  if (!regs) return 0;
+  epilogue_store_regs<F>(out, n_base, m_base, y, ldy, lane);
+  return RegEpilogue<F>::kStores;
 }
 
-// Whole tiles and halves of the leftover ones (weight rows 128 h .. +127): see
-// tile_unit.
+// Work unit u -> its tile: whole tiles, and halves (weight rows 128 h .. +127) of
+// the leftover ones (see tile_unit).  False for a half past the last weight row.
+__device__ __forceinline__ bool mx_unit(int u, int tiles_m, int tiles_n, int full, int64_t N,
+                                        bool* is_half, int64_t* m0, int64_t* n0) {
+  int vt, half, tm, tn;
+  *is_half = tile_unit(u, tiles_m * tiles_n, full, &vt, &half);
+  tile_of(vt, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  *m0 = (int64_t)tm * kBM;
+  *n0 = (int64_t)tn * kBN + (*is_half ? 128 * half : 0);
+  return *n0 < N;
+}
+
+// Persistent: workgroup b runs units b, b + G, b + 2G, ... (G = the grid), so unit u
+// still runs on XCD u % 8 when G is a multiple of 8.  Each tile queues the next
+// one's first loads as soon as its output is staged, ahead of its own stores, so
+// the stores drain while the next tile starts.
 template <int R, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
     const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
-    int64_t ldy, int tiles_m, int tiles_n, int full) {
+    int64_t ldy, int tiles_m, int tiles_n, int full, int units) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
-  int vt, half, tm, tn;
-  const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
-  tile_of(vt, tiles_m, tiles_n, kGroupM, &tm, &tn);
-  if (!is_half) {
-    mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
-                                (int64_t)tm * kBM, (int64_t)tn * kBN);
-  } else {
-    if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
-    mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, t, l2t, bias, y, ldy,
-                                (int64_t)tm * kBM, (int64_t)tn * kBN + 128 * half);
+  const int nkt = (int)((K + kKT - 1) / kKT);
+  const int step = gridDim.x;
+  auto find = [&](int v, bool* h, int64_t* mm, int64_t* nn) {
+    while (v < units && !mx_unit(v, tiles_m, tiles_n, full, N, h, mm, nn)) v += step;
+    return v;
+  };
+  auto prologue = [&](bool h, int64_t mm, int64_t nn) {
+    if (h) MxLoads<kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, mm, nn).template prologue<R>(nkt, t, l2t, mm, nn);
+    else MxLoads<kFFull>(lds_raw, ac, as, bc, bs, M, N, K, mm, nn).template prologue<R>(nkt, t, l2t, mm, nn);
+  };
+  bool half;
+  int64_t m0, n0;
+  int u = find(blockIdx.x, &half, &m0, &n0);
+  if (u >= units) return;
+  prologue(half, m0, n0);
+  int pending = 0;
+  while (u < units) {
+    // the next unit is looked up again after the tile rather than kept live across it
+    auto issue_next = [&]() {
+      bool nh;
+      int64_t nm, nn;
+      if (find(u + step, &nh, &nm, &nn) < units) prologue(nh, nm, nn);
+    };
+    if (half)
+      pending = mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0,
+                                           pending, issue_next);
+    else
+      pending = mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0,
+                                           pending, issue_next);
+    u = find(u + step, &half, &m0, &n0);
   }
 }
 
@@ -343,9 +446,11 @@ static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const
   }
   const int rem = tiles % cus;
   const int full = (tiles > cus && rem > 0 && 2 * rem <= cus) ? tiles - rem : tiles;
-  const int grid = full + 2 * (tiles - full);
+  const int units = full + 2 * (tiles - full);
+  // one workgroup per CU (the LDS allows no more), each looping over its units
+  const int grid = units < cus ? units : cus;
   hipLaunchKernelGGL((gemm_mx_kernel<R, F32>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M, N,
-                     K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
+                     K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full, units);
 }
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,

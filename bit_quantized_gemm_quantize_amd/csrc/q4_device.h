@@ -233,6 +233,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier after an explicit wait for loads into LDS.  The compiler counts
+// those loads as LDS writes, so lds_barrier() would make it wait for every vector
+// memory operation in flight (vmcnt(0)), global stores included.  This one waits
+// only for the wave's own LDS accesses; the memory clobber keeps the compiler from
+// moving accesses across it.
+__device__ __forceinline__ void barrier_after_wait() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace q4
 
 namespace q4 {

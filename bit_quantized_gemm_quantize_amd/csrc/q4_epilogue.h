@@ -132,6 +132,53 @@ struct EpilogueShape {
 constexpr int kStageWaveBytes = EpilogueShape<false, 4, 128>::kStageWaveBytes;   // 18432
 constexpr int kEpilogueLdsBytes = 4 * EpilogueShape<true, 4, 128>::kStageWaveBytes;
 
+// One staging pass: the accumulators of weight sub-tiles pass * kFPerPass ..
+// + kFPerPass - 1, scaled (SCALED) and with the bias added (BIAS), into this wave's
+// LDS rows: row m_local = 32 g + lane%32, columns 32 f' + 8 vq + 4 h .. +3.
+template <bool OUT_F32, int F, int ROW_BYTES, bool SCALED, bool BIAS>
+__device__ __forceinline__ void epilogue_stage_pass(v16f (&acc)[F][4], int pass, int64_t n_base,
+                                                    int64_t N, const uint16_t* __restrict__ bias,
+                                                    int lane, uint8_t* stage, float scale) {
+  using S = EpilogueShape<OUT_F32, F, ROW_BYTES>;
+  const int r32 = lane & 31, h = lane >> 5;
+  constexpr int kElem = S::kElem;
+#pragma unroll
+  for (int fp = 0; fp < S::kFPerPass; ++fp) {
+    const int f = pass * S::kFPerPass + fp;
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      // bias of the 4 consecutive columns this lane holds in register group vq
+      const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
+      float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (BIAS && bias != nullptr) {           // the fp32 path adds zeros without a bias
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint8_t* dst = stage + (32 * g + r32) * S::kStageRowBytes + (32 * fp + 8 * vq + 4 * h) * kElem;
+        float a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a[j] = acc[f][g][4 * vq + j];
+          if (SCALED) a[j] = BIAS ? __builtin_fmaf(a[j], scale, b[j]) : a[j] * scale;
+          else if (BIAS) a[j] += b[j];
+        }
+        if (OUT_F32) {
+          *reinterpret_cast<v4f*>(dst) = v4f{a[0], a[1], a[2], a[3]};
+        } else {
+          const v2bf p0 = {(__bf16)a[0], (__bf16)a[1]};
+          const v2bf p1 = {(__bf16)a[2], (__bf16)a[3]};
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        }
+      }
+    }
+  }
+}
+
 // y = scale * acc + bias (SCALED), or acc + bias.  The bias is added, and the
 // scale applied, pass by pass, so only the accumulators being staged are moved out
 // of the matrix registers; without a bias the add is skipped.
@@ -142,54 +189,12 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
                                                int64_t ldy, int lane, uint8_t* stage,
                                                float scale = 1.0f) {
   using S = EpilogueShape<OUT_F32, F, ROW_BYTES>;
-  const int r32 = lane & 31, h = lane >> 5;
   constexpr int kElem = S::kElem;
-  constexpr int kFPerPass = S::kFPerPass;
-  constexpr int kColsPerPass = 32 * kFPerPass;
-  constexpr int kRowBytes = S::kRowBytes;
+  constexpr int kColsPerPass = 32 * S::kFPerPass;
   constexpr int kStageRow = S::kStageRowBytes;
-  constexpr int kLanesPerRow = kRowBytes / 16;
+  constexpr int kLanesPerRow = S::kRowBytes / 16;
   constexpr int kRowsPerStore = 64 / kLanesPerRow;
   constexpr int kPer16 = 16 / kElem;             // elements per 16-byte store
-  auto pass_body = [&](auto has_bias_c, int pass) {
-    constexpr bool kBias = decltype(has_bias_c)::value;
-    // registers -> LDS: row m_local = 32 g + lane%32, columns 32 f' + 8 vq + 4 h .. +3
-#pragma unroll
-    for (int fp = 0; fp < kFPerPass; ++fp) {
-      const int f = pass * kFPerPass + fp;
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        // bias of the 4 consecutive columns this lane holds in register group vq
-        const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
-        float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (kBias && bias != nullptr) {        // the fp32 path adds zeros without a bias
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint8_t* dst = stage + (32 * g + r32) * kStageRow + (32 * fp + 8 * vq + 4 * h) * kElem;
-          float a[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a[j] = acc[f][g][4 * vq + j];
-            if (SCALED) a[j] = kBias ? __builtin_fmaf(a[j], scale, b[j]) : a[j] * scale;
-            else if (kBias) a[j] += b[j];
-          }
-          if (OUT_F32) {
-            *reinterpret_cast<v4f*>(dst) = v4f{a[0], a[1], a[2], a[3]};
-          } else {
-            const v2bf p0 = {(__bf16)a[0], (__bf16)a[1]};
-            const v2bf p1 = {(__bf16)a[2], (__bf16)a[3]};
-            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2*>(dst) =
-                u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-          }
-        }
-      }
-    }
-  };
 #pragma unroll
   for (int pass = 0; pass < S::kPasses; ++pass) {
     if (pass > 0) {
@@ -198,8 +203,10 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
     }
     // fp32 output keeps one path (a second copy of the pass made the compiler spill);
     // it reads the bias only when there is one
-    if (OUT_F32 || bias) pass_body(std::true_type{}, pass);
-    else pass_body(std::false_type{}, pass);
+    if (OUT_F32 || bias)
+      epilogue_stage_pass<OUT_F32, F, ROW_BYTES, SCALED, true>(acc, pass, n_base, N, bias, lane, stage, scale);
+    else
+      epilogue_stage_pass<OUT_F32, F, ROW_BYTES, SCALED, false>(acc, pass, n_base, N, bias, lane, stage, scale);
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     // LDS -> global: kLanesPerRow lanes per row (16 bytes each), whole row segments
@@ -224,6 +231,51 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
       }
     }
   }
+}
+
+// bf16 output of a wave's 128 x 32F region staged in one pass and held in
+// registers until it is stored: out[i] holds the 16 bytes of store i (row
+// kRowsPerStore i + lane / kLanesPerRow, bytes 16 (lane % kLanesPerRow) ..).  This
+// lets a kernel free its LDS (and queue other loads) before the stores go out.
+template <int F>
+struct RegEpilogue {
+  using S = EpilogueShape<false, F, 64 * F>;
+  static_assert(S::kPasses == 1, "one staging pass");
+  static constexpr int kLanesPerRow = S::kRowBytes / 16;
+  static constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  static constexpr int kStores = 128 / kRowsPerStore;
+};
+
+template <int F>
+__device__ __forceinline__ void epilogue_stage_to_regs(v16f (&acc)[F][4], int64_t n_base, int64_t N,
+                                                       const uint16_t* __restrict__ bias, int lane,
+                                                       uint8_t* stage,
+                                                       u32x4 (&out)[RegEpilogue<F>::kStores]) {
+  using E = RegEpilogue<F>;
+  if (bias)
+    epilogue_stage_pass<false, F, 64 * F, false, true>(acc, 0, n_base, N, bias, lane, stage, 1.0f);
+  else
+    epilogue_stage_pass<false, F, 64 * F, false, false>(acc, 0, n_base, N, bias, lane, stage, 1.0f);
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
+  const int col_bytes = (lane % E::kLanesPerRow) * 16;
+#pragma unroll
+  for (int it = 0; it < E::kStores; ++it)
+    out[it] = ld16(stage + (E::kRowsPerStore * it + lane / E::kLanesPerRow) * E::S::kStageRowBytes + col_bytes);
+}
+
+// The stores of epilogue_stage_to_regs' registers, for a region wholly inside the
+// output (no masks).
+template <int F>
+__device__ __forceinline__ void epilogue_store_regs(const u32x4 (&out)[RegEpilogue<F>::kStores],
+                                                    int64_t n_base, int64_t m_base, void* y,
+                                                    int64_t ldy, int lane) {
+  using E = RegEpilogue<F>;
+  const int64_t n = n_base + (lane % E::kLanesPerRow) * 8;
+  uint16_t* base = static_cast<uint16_t*>(y) + (m_base + lane / E::kLanesPerRow) * ldy + n;
+#pragma unroll
+  for (int it = 0; it < E::kStores; ++it)
+    st16_stream(base + (int64_t)E::kRowsPerStore * it * ldy, out[it]);
 }
 
 }  // namespace q4

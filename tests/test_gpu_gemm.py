@@ -174,6 +174,22 @@ def test_gemm_mx_leftover_tiles_as_halves():
         _check(y, y_ref, bound, not f32, f"leftover tiles {M}x{N}x{K}")
 
 
+def test_gemm_mx_several_tiles_per_workgroup():
+    """About four work units per workgroup (864 tiles of 256 x 256, the leftover 96
+    as halves): each tile queues the next one's first loads before its own stores.
+    Ragged M and N put masked edge tiles among the interior ones; rank-16 branch and
+    bias, bf16 and fp32 output, every element checked."""
+    dev = device()
+    M, N, K = 4600, 12280, 256
+    d = synth.mlp_up_svd(seed=12, M=M, K=K, N=N, rank=16)
+    bias = synth.bias(N, seed=13)
+    y_ref, bound = ref_w4a4("mxfp4", d["x"], d["rt"], bias=bias, l1=d["l1"], l2=d["l2"])
+    for f32 in (False, True):
+        say(f"gemm_w4a4_lowrank mxfp4 several tiles per workgroup M={M} N={N} K={K} f32={f32}")
+        y = run_w4a4("mxfp4", d["x"], d["rt"], dev, bias=bias, f32=f32, l1=d["l1"], l2=d["l2"])
+        _check(y, y_ref, bound, not f32, f"several tiles per workgroup {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------------ full layer sizes
 def test_full_mlp_up_svd_layer_sampled_rows():
     """The benchmarked configuration: M=4608, K=3072, N=12288, rank 32, bf16 output,
