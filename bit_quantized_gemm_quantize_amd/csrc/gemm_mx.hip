@@ -81,6 +81,7 @@ struct MxLoads {
   static constexpr int kScaleOps = kWaves == 8 ? 1 : 2;        // scale loads per wave per pair
 
   uint8_t* lds_raw;
+  // buffer views of this tile's rows of codes and scales: rows past M / N read as zero
   __amdgpu_buffer_rsrc_t rc_a, rc_b, rs_a, rs_b;
   uint32_t kbytes, nblk, rows_a, rows_b;
   int wave, lane;
@@ -97,7 +98,6 @@ struct MxLoads {
     nblk = (uint32_t)(K >> 5);
     rows_a = rows_in(kBM, M, m0);
     rows_b = rows_in(kTN, N, n0);
-    // buffer views of this tile's rows: rows past M / N read as zero
     rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
     rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
     rs_a = make_rsrc(as + m0 * nblk, rows_a * nblk);
@@ -105,7 +105,8 @@ struct MxLoads {
   }
 
   template <int PART>
-  __device__ __forceinline__ void gload_part(int kt, int stage) const {
+  __device__ __forceinline__ void gload(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int kt,
+                                        int stage) const {
     auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
     const int lr = lane >> 3, lp = lane & 7;
     const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
@@ -117,16 +118,27 @@ struct MxLoads {
       const int j = op == 0 ? idx : idx - kNA;
       const uint32_t row = per * wave + 8 * j + lr;
       // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
-      buf_ld16_lds(op == 0 ? rc_a : rc_b, &lds[op][stage][(per * wave + 8 * j) * kKTB],
-                   row * kbytes + koff);
+      buf_ld16_lds(op == 0 ? ra : rb, &lds[op][stage][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
     }
+  }
+  template <int PART>
+  __device__ __forceinline__ void gload_part(int kt, int stage) const {
+    gload<PART>(rc_a, rc_b, kt, stage);
+  }
+  // Part PART of K-tile kt of this tile, or of K-tile 0 of tile nx when use_next: the
+  // tiles have the same shape, so only the buffer views differ (scalar selects).
+  template <int PART>
+  __device__ __forceinline__ void gload_part_or(const MxLoads& nx, bool use_next, int kt,
+                                                int stage) const {
+    gload<PART>(use_next ? nx.rc_a : rc_a, use_next ? nx.rc_b : rc_b, use_next ? 0 : kt, stage);
   }
 
   // scales, global -> LDS, once per pair of K-tiles: 64 rows per instruction (lane i
   // takes row 64 sw + i, 16 bytes = the scale bytes of K-tiles 2p and 2p+1 of pair
   // p) into scale stage p % 2.  With 8 waves, waves 0-3 take the activation rows
   // and waves 4-7 the weight rows; with 4, every wave takes both.
-  __device__ __forceinline__ void sload(int p) const {
+  __device__ __forceinline__ void sload_from(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                             int p) const {
     auto& lsc = *reinterpret_cast<uint8_t(*)[2][2][kBM * 16]>(lds_raw + kCodeLds);
     const int sw = wave & 3;
     const uint32_t b0 = (uint32_t)p * 16;
@@ -135,25 +147,21 @@ struct MxLoads {
 #pragma unroll
     for (int k = 0; k < kScaleOps; ++k) {
       const int op = kWaves == 8 ? (wave >> 2) : k;
-      buf_ld16_lds(op == 0 ? rs_a : rs_b, &lsc[p & 1][op][64 * sw * 16], off);
+      buf_ld16_lds(op == 0 ? ra : rb, &lsc[p & 1][op][64 * sw * 16], off);
     }
   }
+  __device__ __forceinline__ void sload(int p) const { sload_from(rs_a, rs_b, p); }
+  // scale pair p of this tile, or pair p - pairs of tile nx when use_next
+  __device__ __forceinline__ void sload_or(const MxLoads& nx, bool use_next, int p, int pairs) const {
+    sload_from(use_next ? nx.rs_a : rs_a, use_next ? nx.rs_b : rs_b, use_next ? p - pairs : p);
+  }
 
-  // What the tile's K loop needs in LDS before it starts: K-tile 0 (stage 0), the
-  // first two scale pairs, and for the low-rank term the tile's t rows and L2^T rows
-  // (contiguous in memory), in the second, still unused stage of the activation and
-  // weight tiles.
+  // The low-rank operands: the tile's t rows and L2^T rows (contiguous in memory), in
+  // the second stage of the activation and weight tiles.
   template <int R>
-  __device__ __forceinline__ void prologue(int nkt, const float* __restrict__ t,
-                                           const uint16_t* __restrict__ l2t, int64_t m0,
-                                           int64_t n0) const {
-    if (nkt > 0) {
-      gload_part<0>(0, 0);
-      gload_part<1>(0, 0);
-      gload_part<2>(0, 0);
-      sload(0);
-      sload(1);
-    }
+  __device__ __forceinline__ void lowrank_loads(const float* __restrict__ t,
+                                                const uint16_t* __restrict__ l2t, int64_t m0,
+                                                int64_t n0) const {
     if (R > 0) {
       auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
       const auto rt = make_rsrc(t + m0 * R, rows_a * (uint32_t)(4 * R));
@@ -174,20 +182,103 @@ struct MxLoads {
       }
     }
   }
+
+  // What the tile's K loop needs in LDS before it starts: K-tile 0 (stage 0), the
+  // first two scale pairs, and the low-rank operands (stage 1).
+  template <int R>
+  __device__ __forceinline__ void prologue(int nkt, const float* __restrict__ t,
+                                           const uint16_t* __restrict__ l2t, int64_t m0,
+                                           int64_t n0) const {
+    if (nkt > 0) {
+      gload_part<0>(0, 0);
+      gload_part<1>(0, 0);
+      gload_part<2>(0, 0);
+      sload(0);
+      sload(1);
+    }
+    lowrank_loads<R>(t, l2t, m0, n0);
+  }
 };
+
+// Output staging for a tile whose successor's first K-tile already fills stage 0:
+// each wave stages 128 rows x 128 bytes at a time in 16 KB of stage 1 (wave w: the
+// stage-1 tile of operand w / 2, offset 16 KB (w % 2)), its 16-byte chunks
+// XOR-swizzled by row pair (chunk c of row r at c ^ ((r / 2) % 8)): with the 256
+// bytes of a bank row holding two 128-byte rows, 16 consecutive rows then cover
+// every bank, so neither the transposing writes nor the row reads conflict.  bf16:
+// two passes of 64 columns; fp32: four of 32.
+template <bool OUT_F32>
+struct MxStage1 {
+  static constexpr int kElem = OUT_F32 ? 4 : 2;
+  static constexpr int kFPerPass = OUT_F32 ? 1 : 2;
+  static constexpr int kPasses = kFFull / kFPerPass;
+  static constexpr int kCols = 32 * kFPerPass;         // columns per pass
+  static constexpr int kReads = 16;                    // 16-byte reads per lane per pass
+};
+__device__ __forceinline__ uint8_t* mx_stage1_base(uint8_t* lds_raw, int wave) {
+  return lds_raw + (2 * (wave >> 1) + 1) * (kBM * kKTB) + (wave & 1) * 16384;
+}
+template <bool OUT_F32, bool BIAS>
+__device__ __forceinline__ void mx_stage1_write(v16f (&acc)[kFFull][4], int pass, int64_t n_base,
+                                                int64_t N, const uint16_t* __restrict__ bias,
+                                                int lane, uint8_t* stage) {
+  using S = MxStage1<OUT_F32>;
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int fp = 0; fp < S::kFPerPass; ++fp) {
+    const int f = pass * S::kFPerPass + fp;
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      const int64_t n = n_base + 32 * f + 8 * vq + 4 * h;
+      float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (BIAS && bias != nullptr) {           // the edge path adds zeros without a bias
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
+      }
+      const int col_byte = (32 * fp + 8 * vq + 4 * h) * S::kElem;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = 32 * g + r32;
+        uint8_t* dst = stage + row * 128 + ((((col_byte >> 4) ^ (row >> 1)) & 7) << 4) + (col_byte & 15);
+        float a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = BIAS ? acc[f][g][4 * vq + j] + b[j] : acc[f][g][4 * vq + j];
+        if (OUT_F32) {
+          *reinterpret_cast<v4f*>(dst) = v4f{a[0], a[1], a[2], a[3]};
+        } else {
+          const v2bf p0 = {(__bf16)a[0], (__bf16)a[1]};
+          const v2bf p1 = {(__bf16)a[2], (__bf16)a[3]};
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        }
+      }
+    }
+  }
+}
+// read i of a pass: row 8 i + lane / 8, logical chunk lane % 8
+__device__ __forceinline__ u32x4 mx_stage1_read(const uint8_t* stage, int i, int lane) {
+  const int row = 8 * i + (lane >> 3), c = lane & 7;
+  return ld16(stage + row * 128 + (((c ^ (row >> 1)) & 7) << 4));
+}
 
 // One output tile of 256 activation rows x kTN weight rows starting at (m0, n0),
 // whose prologue loads (MxLoads::prologue) are already issued: wave (wm, wn) owns m
 // in [128 wm, +128) and n in [32 F wn, +32 F).  `pending` is the number of this
-// wave's stores from the previous tile still queued behind those loads.  Once the
-// tile's LDS is free again, issue_next() queues the next tile's prologue loads; the
-// return value is the number of stores queued after them.
+// wave's stores from the previous tile still queued behind those loads.  next_kind
+// says what follows (0 nothing, 1 a whole tile at (nm0, nn0), 2 a half tile).  A
+// whole tile followed by a whole tile is chained when K is a multiple of 4 K-tiles:
+// its last K-tiles load the next tile's first K-tile and scale pairs in place of
+// the loads past K, so only the low-rank operands remain for the next prologue.
+// Once the tile's LDS is free again, issue_next(chained) queues what remains of the
+// next tile's prologue; the return value is the number of stores queued after it.
 template <int R, bool OUT_F32, int F, class Next>
 __device__ __forceinline__ int mx_tile(
     uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0,
-    int pending, Next&& issue_next) {
+    int pending, int next_kind, int64_t nm0, int64_t nn0, Next&& issue_next) {
   using L = MxLoads<F>;
   constexpr int kMma = 4 * F;                    // MFMAs per wave per step
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
@@ -209,10 +300,18 @@ __device__ __forceinline__ int mx_tile(
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
+  const bool chain = F == kFFull && next_kind == 1 && (nkt & 3) == 0 && nkt >= 4;
+  const L nx(lds_raw, ac, as, bc, bs, M, N, K, chain ? nm0 : m0, chain ? nn0 : n0);
+  const int pairs = nkt >> 1;
   auto gload_part = [&](auto part_c, int kt, int stage) {
     ld.template gload_part<decltype(part_c)::value>(kt, stage);
   };
-  auto sload = [&](int p) { ld.sload(p); };
+  // in a chained tile, K-tile nkt is the next tile's K-tile 0 and scale pairs
+  // pairs, pairs + 1 are the next tile's pairs 0 and 1
+  auto gload_part_or_next = [&](auto part_c, int kt, int stage) {
+    ld.template gload_part_or<decltype(part_c)::value>(nx, chain && kt == nkt, kt, stage);
+  };
+  auto sload_or_next = [&](int p) { ld.sload_or(nx, chain && p >= pairs, p, pairs); };
   // the lane's scale word for K-tile kt: bytes for blocks 8kt + 4h .. 8kt + 4h + 3,
   // at byte 8 (kt % 2) + 4h of the row's 16 bytes in scale stage (kt / 2) % 2.
   // Read raw; valid_scales() replaces the words of blocks past K (whose codes are
@@ -285,7 +384,9 @@ __device__ __forceinline__ int mx_tile(
   // with the prologue), so the epilogue is left with the bias and the store.
   if (R > 0) {
     lowrank_accumulate_lds<R>(acc, &lds[0][1][0], &lds[1][1][0], 128 * wm, 32 * F * wn, lane);
-    lds_barrier();                           // stage 1 is free again for K-tile 1
+    // stage 1 is free again for K-tile 1.  The prologue loads were waited for above;
+    // a fenced barrier would also wait for the previous tile's stores.
+    barrier_after_wait();
   }
   if (nkt > 0) {
     gload_part(P0{}, 1, 1);
@@ -307,7 +408,7 @@ __device__ __forceinline__ int mx_tile(
     constexpr int vm0 = kPartBegin[2] - kPartBegin[1], vm1 = kPartBegin[3] - kPartBegin[2];
     constexpr int vm3 = kPartBegin[1] + (st == 1 ? kScaleOps : 0);
     read_frags(1, st, 1);
-    gload_part(P1{}, kt + 1, st ^ 1);
+    gload_part_or_next(P1{}, kt + 1, st ^ 1);
     Q4_MX_MMA(0, 0)
     __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
     for (int i = 0; i < kMma; ++i) {
@@ -317,7 +418,7 @@ __device__ __forceinline__ int mx_tile(
     __builtin_amdgcn_sched_barrier(0);
     read_scales(kt + 1);
     read_frags(0, st, 2);
-    gload_part(P2{}, kt + 1, st ^ 1);
+    gload_part_or_next(P2{}, kt + 1, st ^ 1);
     Q4_MX_MMA(1, 1)
     __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * F, 0);
     for (int i = 0; i < kMma; ++i) {
@@ -337,8 +438,8 @@ __device__ __forceinline__ int mx_tile(
     // stage st is free for tile kt+2
     __syncthreads();
     read_frags(0, st ^ 1, 0);
-    gload_part(P0{}, kt + 2, st);
-    if (st == 1) sload((kt + 3) >> 1);                 // kt odd: pair (kt+3)/2
+    gload_part_or_next(P0{}, kt + 2, st);
+    if (st == 1) sload_or_next((kt + 3) >> 1);         // kt odd: pair (kt+3)/2
     Q4_MX_MMA_F(3, 1, kF3, F)
     __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
     for (int i = 0; i < 4 * (F - kF3); ++i) {
@@ -359,6 +460,79 @@ __device__ __forceinline__ int mx_tile(
 #undef Q4_MX_MMA_F
 #undef Q4_READS_THEN_MMA
 
+  if constexpr (F == kFFull) {
+   if (chain) {
+    // The last loads of the K loop are the next tile's scale pair 1 (into a scale
+    // stage): wait for everything before them (the zero loads past K into stage 1)
+    // but not for them.
+    wait_vmcnt<L::kScaleOps>();
+    barrier_after_wait();                    // all waves are done with the operand LDS
+    // stage 0 and the scale stages hold the next tile's first K-tile and scale pairs:
+    // stage in stage 1 only
+    using S = MxStage1<OUT_F32>;
+    uint8_t* stage = mx_stage1_base(lds_raw, wave);
+    auto& accf = acc;
+    if (!OUT_F32 && m_base + 128 <= M && n_base + 128 <= N) {
+      // inside the output, bf16: both passes into registers, then the next tile's
+      // low-rank loads, then the stores
+      u32x4 out[S::kPasses * S::kReads];
+#pragma unroll
+      for (int pass = 0; pass < S::kPasses; ++pass) {
+        // a wave's LDS accesses take effect in order: no wait between the writes, the
+        // reads and the next pass's writes
+        if (bias) mx_stage1_write<OUT_F32, true>(accf, pass, n_base, N, bias, lane, stage);
+        else mx_stage1_write<OUT_F32, false>(accf, pass, n_base, N, bias, lane, stage);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < S::kReads; ++i) out[pass * S::kReads + i] = mx_stage1_read(stage, i, lane);
+        __builtin_amdgcn_wave_barrier();
+      }
+      // the next tile's scale pair 1 may still be landing in a scale stage: a
+      // fenced barrier would wait for it
+      barrier_after_wait();
+      issue_next(true);
+      uint16_t* dst = static_cast<uint16_t*>(y) + (m_base + (lane >> 3)) * ldy + n_base + (lane & 7) * 8;
+#pragma unroll
+      for (int pass = 0; pass < S::kPasses; ++pass)
+#pragma unroll
+        for (int i = 0; i < S::kReads; ++i)
+          st16_stream(dst + (int64_t)8 * i * ldy + pass * S::kCols, out[pass * S::kReads + i]);
+      return S::kPasses * S::kReads;
+    }
+    // edges or fp32: each pass stored as it is read back, with the M and N masks
+    constexpr int kPer16 = 16 / S::kElem;
+#pragma unroll
+    for (int pass = 0; pass < S::kPasses; ++pass) {
+      // one path with the bias read guarded (a second copy costs registers)
+      mx_stage1_write<OUT_F32, true>(accf, pass, n_base, N, bias, lane, stage);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+      const int64_t n = n_base + pass * S::kCols + (lane & 7) * kPer16;
+#pragma unroll 4
+      for (int i = 0; i < S::kReads; ++i) {
+        const u32x4 v = mx_stage1_read(stage, i, lane);
+        const int64_t m = m_base + 8 * i + (lane >> 3);
+        if (m < M) {
+          uint8_t* dst = static_cast<uint8_t*>(y) + (m * ldy + n) * S::kElem;
+          if (n + kPer16 <= N) {
+            st16_stream(dst, v);
+          } else if (n < N) {
+            const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+            for (int j = 0; j < kPer16 && n + j < N; ++j) {
+              if (OUT_F32) reinterpret_cast<uint32_t*>(dst)[j] = w[j];
+              else reinterpret_cast<uint16_t*>(dst)[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
+    barrier_after_wait();
+    issue_next(true);
+    return 0;
+   }
+  }
   wait_vmem();                               // the loads past K have landed
   __syncthreads();                           // all waves are done with the operand LDS
   uint8_t* stage = lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>();
@@ -371,7 +545,7 @@ __device__ __forceinline__ int mx_tile(
   else epilogue_store<OUT_F32, F, mx_stage_row_max<OUT_F32>()>(acc, n_base, m_base, M, N, bias, y, ldy,
                                                                lane, stage);
   lds_barrier();
-  issue_next();
+  issue_next(false);
   if (!regs) return 0;
   epilogue_store_regs<F>(out, n_base, m_base, y, ldy, lane);
   return RegEpilogue<F>::kStores;
@@ -417,19 +591,26 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   prologue(half, m0, n0);
   int pending = 0;
   while (u < units) {
-    // the next unit is looked up again after the tile rather than kept live across it
-    auto issue_next = [&]() {
-      bool nh;
-      int64_t nm, nn;
-      if (find(u + step, &nh, &nm, &nn) < units) prologue(nh, nm, nn);
+    bool nh = false;
+    int64_t nm = 0, nn = 0;
+    const int nu = find(u + step, &nh, &nm, &nn);
+    const int next_kind = nu >= units ? 0 : (nh ? 2 : 1);
+    // chained: only the low-rank operands are left to load
+    auto issue_next = [&](bool chained) {
+      if (nu >= units) return;
+      if (chained) MxLoads<kFFull>(lds_raw, ac, as, bc, bs, M, N, K, nm, nn).template lowrank_loads<R>(t, l2t, nm, nn);
+      else prologue(nh, nm, nn);
     };
     if (half)
       pending = mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0,
-                                           pending, issue_next);
+                                           pending, next_kind, nm, nn, issue_next);
     else
       pending = mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0,
-                                           pending, issue_next);
-    u = find(u + step, &half, &m0, &n0);
+                                           pending, next_kind, nm, nn, issue_next);
+    u = nu;
+    half = nh;
+    m0 = nm;
+    n0 = nn;
   }
 }
 

@@ -174,13 +174,16 @@ def test_gemm_mx_leftover_tiles_as_halves():
         _check(y, y_ref, bound, not f32, f"leftover tiles {M}x{N}x{K}")
 
 
-def test_gemm_mx_several_tiles_per_workgroup():
+@pytest.mark.parametrize("K", [256, 1024])
+def test_gemm_mx_several_tiles_per_workgroup(K):
     """About four work units per workgroup (864 tiles of 256 x 256, the leftover 96
-    as halves): each tile queues the next one's first loads before its own stores.
+    as halves): each tile queues the next one's first loads before its own stores,
+    and with K a multiple of four K-tiles (K = 1024) a whole tile followed by a whole
+    tile loads the next one's first K-tile and scale pairs in its own last K-tiles.
     Ragged M and N put masked edge tiles among the interior ones; rank-16 branch and
     bias, bf16 and fp32 output, every element checked."""
     dev = device()
-    M, N, K = 4600, 12280, 256
+    M, N = 4600, 12280
     d = synth.mlp_up_svd(seed=12, M=M, K=K, N=N, rank=16)
     bias = synth.bias(N, seed=13)
     y_ref, bound = ref_w4a4("mxfp4", d["x"], d["rt"], bias=bias, l1=d["l1"], l2=d["l2"])
