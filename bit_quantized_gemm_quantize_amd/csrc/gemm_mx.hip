@@ -350,10 +350,6 @@ __device__ __forceinline__ int mx_tile(
   };
 
   v16f acc[F][4];
-#pragma unroll
-  for (int f = 0; f < F; ++f)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
 #define Q4_MX_MMA(S, BUF) Q4_MX_MMA_F(S, BUF, 0, F)
 #define Q4_MX_MMA_F(S, BUF, F0, F1)                                                             \
@@ -380,6 +376,12 @@ __device__ __forceinline__ int mx_tile(
   else if (pending == RegEpilogue<kFHalf>::kStores) wait_vmcnt<RegEpilogue<kFHalf>::kStores>();
   else wait_vmem();
   barrier_after_wait();
+  // cleared only here, after the wait: clearing at the tile's start made that tile
+  // slower
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
   // The low-rank term t L2 goes into the accumulators first (its operands came
   // with the prologue), so the epilogue is left with the bias and the store.
   if (R > 0) {
