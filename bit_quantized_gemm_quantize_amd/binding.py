@@ -27,6 +27,7 @@ _I64 = _c.c_int64
 _I32 = _c.c_int32
 SIGNATURES = {
     "quantize_act": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P]),
+    "quantize_act_smooth": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P]),
     "pack_weights": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "gemm_w4a4": (_c.c_int, [_c.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
                              _c.c_int, _P]),
@@ -102,6 +103,16 @@ def quantize_act(fmt, x, codes, scales, tensor_scale=None, l1t=None, t=None, str
     st = load().quantize_act(_fmt(fmt), _ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(scales),
                              _ptr(tensor_scale), _ptr(l1t), r, _ptr(t), _stream(stream))
     _check("quantize_act", st)
+
+
+def quantize_act_smooth(fmt, x, inv_s, codes, scales, l1t=None, t=None, stream=None):
+    """quantize_act of x * inv_s (per channel, fp32 [K]); t = X L1 of the unsmoothed x."""
+    _rowmajor(x, "x")
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    st = load().quantize_act_smooth(_fmt(fmt), _ptr(x), M, K, x.stride(0), _ptr(inv_s), _ptr(codes),
+                                    _ptr(scales), _ptr(l1t), r, _ptr(t), _stream(stream))
+    _check("quantize_act_smooth", st)
 
 
 def pack_weights(fmt, w, K, N, stride_k, stride_n, codes, scales, zeros=None, tensor_scale=None,

@@ -69,6 +69,23 @@ q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, i
                                           (int)r, t, static_cast<hipStream_t>(stream)));
 }
 
+q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              const float* inv_s, uint8_t* codes, uint8_t* scales,
+                              const uint16_t* l1t, int32_t r, float* t, void* stream) {
+  if (fmt != Q4_MXFP4) return Q4_ERR_FORMAT;
+  if (M < 0 || K < 0 || (K % 32) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows) return Q4_ERR_SHAPE;
+  if (!x || !inv_s || !codes || !scales) return Q4_ERR_NULL;
+  if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
+  if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(codes, 16) || !aligned(scales, 4) ||
+      !aligned(inv_s, 16))
+    return Q4_ERR_ALIGN;
+  if (r > 0 && (!aligned(l1t, 16) || !aligned(t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0) return Q4_OK;
+  return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, nullptr, l1t, (int)r,
+                                          t, static_cast<hipStream_t>(stream), inv_s));
+}
+
 q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, int64_t stride_k,
                        int64_t stride_n, uint8_t* codes, void* scales, uint16_t* zeros,
                        float* tensor_scale, void* stream) {

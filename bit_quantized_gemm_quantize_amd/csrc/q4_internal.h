@@ -10,7 +10,8 @@ namespace q4 {
 // NVFP4 queues: clear tensor_scale, tensor amax, encode, amax -> s_t.
 hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                               const uint16_t* l1t, int r, float* t, hipStream_t s);
+                               const uint16_t* l1t, int r, float* t, hipStream_t s,
+                               const float* inv_s = nullptr);
 
 // Weight packer over a strided logical [K, N] bf16 matrix.  fmt 0/1/2.
 hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N, int64_t sk,

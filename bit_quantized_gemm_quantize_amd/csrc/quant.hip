@@ -76,6 +76,55 @@ __device__ __forceinline__ uint32_t nv_encode32(const uint32_t* w, float s_t, fl
   return sc;
 }
 
+// ---------------------------------------------------------------------------- smoothed MXFP4
+// floor(log2 v) of a positive fp32 magnitude given as its 31-bit pattern.
+// Normal: exponent field - 127; subnormal m * 2**-149: floor(log2 m) - 149.
+__device__ __forceinline__ int f32_floor_log2(uint32_t mag) {
+  const uint32_t e = mag >> 23;
+  if (e != 0) return (int)e - 127;
+  return (31 - __builtin_clz(mag & 0x7FFFFFu)) - 149;
+}
+
+// One MXFP4 block of the smoothed activation v_j = fp32(x_j * inv_j) (fp32 multiply,
+// round to nearest even): shared exponent E = floor(log2 max|v|) - 2, clamped to
+// [-127, 127] (-127 for a zero block), and the codes of v * 2**-E, each product exact
+// (a power of two; a result too small for fp32 encodes to a signed zero either way),
+// rounded to E2M1 by the converter with a unit scale.  w: the block's 16 dwords of
+// bf16 pairs; inv: its 32 factors.  Returns E.
+__device__ __forceinline__ int mx_encode_smoothed(const uint32_t* w, const float* __restrict__ inv,
+                                                  u32x4* codes) {
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const u32x4 f = ld16(inv + 4 * q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * q + j;
+      const uint32_t pair = w[e >> 1];
+      const float x = (e & 1) ? bf16_hi(pair) : bf16_lo(pair);
+      v[e] = x * __uint_as_float(f[j]);
+    }
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = max(amax, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+  int E = amax == 0 ? -127 : f32_floor_log2(amax) - 2;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  const float down = exp2i(-E);
+  uint32_t c[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 0] * down, v[8 * d + 1] * down, 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 2] * down, v[8 * d + 3] * down, 1.0f, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 4] * down, v[8 * d + 5] * down, 1.0f, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 6] * down, v[8 * d + 7] * down, 1.0f, 3);
+    c[d] = r;
+  }
+  *codes = u32x4{c[0], c[1], c[2], c[3]};
+  return E;
+}
+
 // ---------------------------------------------------------------------------- activation pass
 // One pair of 32-element blocks per lane half: the 64 bytes of X of block `blk` of
 // `row` (zeros past M or K).
@@ -98,11 +147,11 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
 // so the workgroups spread evenly over the CUs (lanes past it idle).  Each of the 16
 // waves takes every 16th pair of blocks, keeping the X bytes of three pairs in
 // flight per lane.
-template <int FMT, int R>
+template <int FMT, int R, bool SMOOTH = false>
 __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int rows,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax_t,
-    const uint16_t* __restrict__ l1t, float* __restrict__ t) {
+    const uint16_t* __restrict__ l1t, float* __restrict__ t, const float* __restrict__ inv_s) {
   __shared__ float red[R > 0 ? kQWaves * 32 * 32 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
@@ -129,7 +178,10 @@ __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
     const bool blk_ok = blk < nblk;
     if (row_ok && blk_ok) {
       u32x4 c;
-      if (FMT == 0) {
+      if (FMT == 0 && SMOOTH) {
+        const int E = mx_encode_smoothed(w, inv_s + blk * 32, &c);
+        scales[row * sbytes + blk] = (uint8_t)(E + 127);
+      } else if (FMT == 0) {
         const int E = mx_block_exponent(bf16_amax_bits<16>(w));
         const float sc = exp2i(E);
         c = u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
@@ -235,10 +287,10 @@ static hipError_t queue_tensor_amax(const uint16_t* x, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
-template <int FMT, int R>
+template <int FMT, int R, bool SMOOTH = false>
 static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
                         uint8_t* scales, const float* amax, const uint16_t* l1t, float* t,
-                        hipStream_t s) {
+                        hipStream_t s, const float* inv_s = nullptr) {
   // rows per workgroup: the fewest rounds of workgroups over the CUs with at most 32
   // rows each (M = 4608 on 256 CUs: 18 rows, one workgroup per CU)
   int cus = 256;
@@ -251,13 +303,20 @@ static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   while ((M + cus * waves - 1) / (cus * waves) > kQRows) ++waves;
   const int rows = (int)std::max<int64_t>(1, (M + cus * waves - 1) / (cus * waves));
   const unsigned grid = (unsigned)((M + rows - 1) / rows);
-  hipLaunchKernelGGL((quant_act_kernel<FMT, R>), dim3(grid), dim3(kQWaves * 64), 0, s, x, M, K, ldx, rows,
-                     codes, scales, amax, l1t, t);
+  hipLaunchKernelGGL((quant_act_kernel<FMT, R, SMOOTH>), dim3(grid), dim3(kQWaves * 64), 0, s, x, M, K, ldx,
+                     rows, codes, scales, amax, l1t, t, inv_s);
 }
 
 hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                               const uint16_t* l1t, int r, float* t, hipStream_t s) {
+                               const uint16_t* l1t, int r, float* t, hipStream_t s,
+                               const float* inv_s) {
+  if (fmt == 0 && inv_s != nullptr) {
+    if (r == 0) queue_quant<0, 0, true>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s, inv_s);
+    else if (r == 16) queue_quant<0, 16, true>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s, inv_s);
+    else queue_quant<0, 32, true>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s, inv_s);
+    return hipGetLastError();
+  }
   if (fmt == 1) {
     hipError_t e = queue_tensor_amax(x, M, K, ldx, 1, tensor_scale, s);
     if (e != hipSuccess) return e;

@@ -109,6 +109,67 @@ def lowrank_split(wt_bits, rank, seed, oversample=10, power_iters=2):
     return l1, l2, rt
 
 
+def smoothing_factors(x_cal_bits, wt_bits, alpha=0.5):
+    """Per-input-channel smoothing factors s [K] for X' = X diag(s)^-1, W' = diag(s) W
+    (the SVDQuant Guide, "2. SmoothQuant Pre-Conditioning for DiTs", gives the
+    transform but not how s is chosen).  Taken from SmoothQuant: s_j =
+    max|X_j|^alpha / max|W_j|^(1 - alpha) over the calibration rows and the weight's
+    output columns, alpha = 0.5; 1 for a channel that is zero on either side.
+    Returned as the fp32 reciprocals inv_s = fp32(1 / s) the quantizer multiplies
+    by, and the fp64 factors s = 1 / inv_s that exactly undo them."""
+    xa = np.abs(bf16_bits_to_f32(x_cal_bits).astype(np.float64)).max(axis=0)     # [K]
+    wa = np.abs(bf16_bits_to_f32(wt_bits).astype(np.float64)).max(axis=0)        # [K] (W^T is [N, K])
+    ok = (xa > 0) & (wa > 0)
+    s = np.ones_like(xa)
+    s[ok] = xa[ok] ** alpha / wa[ok] ** (1.0 - alpha)
+    inv_s = (1.0 / s).astype(np.float32)
+    return inv_s, 1.0 / inv_s.astype(np.float64)
+
+
+def weighted_lowrank(w, c, rank, ridge=1e-6):
+    """Best rank-r approximation L1 L2 of w [K, N] in the activation-weighted norm
+    ||C^(1/2) (w - L1 L2)||_F, C [K, K] the calibration covariance (the norm of the
+    output error X (w - L1 L2) for activations of that covariance).  The SVDQuant
+    Guide's Step 1 weights the quantization error by the covariance before its SVD;
+    whitening with C^(1/2), a truncated SVD and un-whitening with C^(-1/2) is the
+    exact minimizer of that weighted error.  A ridge of `ridge` times the mean
+    diagonal keeps C invertible.  L1 = C^(-1/2) U_r sqrt(S_r), L2 = sqrt(S_r) V_r^T.
+    Returns (l1 [K, r], l2 [r, N], s_all) in fp64, s_all the weighted singular values."""
+    K = c.shape[0]
+    c = 0.5 * (c + c.T) + ridge * np.trace(c) / K * np.eye(K)
+    lam, q = np.linalg.eigh(c)
+    root = (q * np.sqrt(lam)[None, :]) @ q.T
+    inv_root = (q / np.sqrt(lam)[None, :]) @ q.T
+    u, sv, vh = np.linalg.svd(root @ w, full_matrices=False)
+    r = np.sqrt(sv[:rank])
+    return inv_root @ (u[:, :rank] * r[None, :]), r[:, None] * vh[:rank], sv
+
+
+def svdquant_split(x_cal_bits, wt_bits, rank, alpha=0.5):
+    """Offline SVDQuant weight preparation, not part of the forward pass: smoothing
+    factors from calibration activations, W' = diag(s) W, the activation-weighted
+    rank-r split of W' (weighted by the covariance of the smoothed calibration
+    activations, torch.cov's centring as in the SVDQuant Guide's Step 1), and the
+    residual R' = W' - L1' L2 for 4-bit quantization.
+
+    The forward pass computes Q(X diag(s)^-1) Q(R')^T + (X L1) L2 with the folded
+    down-projection L1 = diag(s)^-1 L1', so the low-rank branch takes the
+    unsmoothed X.  L1 and L2 are rounded to bf16 first; R' = bf16(W' -
+    diag(s) L1 L2) in fp64 absorbs that rounding.
+    Returns dict(inv_s fp32 [K], l1 bf16 [K, r], l2 bf16 [r, N], rt bf16 [N, K] = R'^T,
+    weighted singular values)."""
+    inv_s, s = smoothing_factors(x_cal_bits, wt_bits, alpha)
+    w = bf16_bits_to_f32(wt_bits).astype(np.float64).T * s[:, None]           # W' [K, N]
+    xc = bf16_bits_to_f32(x_cal_bits).astype(np.float64) * inv_s.astype(np.float64)[None, :]
+    c = np.cov(xc.T)
+    l1p, l2, sv = weighted_lowrank(w, c, rank)
+    l1 = to_bf16_bits(l1p * inv_s.astype(np.float64)[:, None])                # folded [K, r]
+    l2 = to_bf16_bits(l2)
+    l1f = bf16_bits_to_f32(l1).astype(np.float64) * s[:, None]                 # L1' as stored
+    rt = to_bf16_bits((w - l1f @ bf16_bits_to_f32(l2).astype(np.float64)).T)
+    return dict(inv_s=inv_s, l1=l1, l2=l2, rt=rt, singular_values=sv)
+
+
 # --------------------------------------------------------------------------- workloads
 # Named by what they are; the full-size ones are the shapes of the layers above.
 
@@ -134,6 +195,19 @@ def mlp_up_svd(seed=0, M=4608, K=3072, N=12288, rank=32):
     l1, l2, rt = lowrank_split(wt, rank, seed)
     return dict(name=f"mlp_up_svd_r{rank}_{M}x{K}x{N}", x=x, wt=wt, l1=l1, l2=l2, rt=rt,
                 M=M, K=K, N=N, rank=rank)
+
+
+def attn_proj_svdquant(seed=0, M=4608, K=3072, N=3072, rank=32, calib=512):
+    """The attention projection's inputs (X N(0,1) with 1% of channels x U(30,100),
+    W N(0,0.02)) prepared the SVDQuant way: smoothing, an activation-weighted rank-r
+    split and a 4-bit residual, from `calib` calibration rows drawn with X (same
+    outlier channels, disjoint rows)."""
+    xa, ch, g = activations(M + calib, K, seed, outliers=int(round(0.01 * K)))
+    x, x_cal = xa[:M], xa[M:]
+    wt = weights(N, K, seed)
+    d = svdquant_split(x_cal, wt, rank)
+    return dict(name=f"attn_proj_svdquant_r{rank}_{M}x{K}x{N}", x=x, x_cal=x_cal, wt=wt,
+                outlier_channels=ch, outlier_gains=g, M=M, K=K, N=N, rank=rank, **d)
 
 
 def qkv_nvfp4(step, seed=0, M=16896, K=3072, N=9216):

@@ -110,6 +110,25 @@ Q4_API q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64
                        const uint16_t* l1t, int32_t r, float* t, void* stream);
 
 /*
+ * quantize_act_smooth -- quantize_act with SmoothQuant pre-conditioning of the
+ * activation: each element is divided by its channel's smoothing factor s_j
+ * before quantization (SVDQuant Guide, "2. SmoothQuant Pre-Conditioning for DiTs":
+ * X' = diag(s)^-1 X, W' = W diag(s)).  The division is a multiply by inv_s[j] =
+ * 1/s_j: the element quantized is fp32(x_j * inv_s[j]) (fp32 multiply, round to
+ * nearest even), then MXFP4 exactly as quantize_act does for a bf16 element.  The
+ * low-rank product t = X L1 is computed from the unsmoothed X, so the caller folds
+ * diag(s)^-1 into L1 offline (X' L1 = X (diag(s)^-1 L1)).
+ *
+ *   fmt       Q4_MXFP4 only (else Q4_ERR_FORMAT).
+ *   inv_s     fp32 [K], positive and finite (not checked), 16-byte aligned; NULL is
+ *             Q4_ERR_NULL.
+ *   others    as quantize_act (tensor_scale is not used).
+ */
+Q4_API q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64_t K,
+                              int64_t ldx, const float* inv_s, uint8_t* codes, uint8_t* scales,
+                              const uint16_t* l1t, int32_t r, float* t, void* stream);
+
+/*
  * pack_weights -- offline weight quantization and packing, once per model (the
  * SVDQuant Guide's "Step 1: Low-Rank Outlier Decomposition in PyTorch" quantizes
  * the residual weight once; "Quantization for the impatient" packs 4-bit weights

@@ -47,9 +47,15 @@ def mx_quantize(bits):
     Returns (codes uint8 [rows, K/2] low nibble = even k, scales uint8 [rows, K/32]).
     """
     bits = _rows(bits, MX_BLOCK)
-    rows, K = bits.shape
     x = bf16_to_f64(bits)
     check_finite(x, "activation/weight")
+    return _mx_quantize_values(x)
+
+
+def _mx_quantize_values(x):
+    """The MXFP4 steps of mx_quantize on real values x [rows, K] (fp64, each exactly
+    a bf16 or fp32 number)."""
+    rows, K = x.shape
     blocks = x.reshape(rows, K // MX_BLOCK, MX_BLOCK)
     amax = np.abs(blocks).max(axis=-1)
     E = np.where(amax > 0, floor_log2(np.where(amax > 0, amax, 1.0)) - E2M1_EMAX, -127)
@@ -57,6 +63,26 @@ def mx_quantize(bits):
     scaled = blocks * np.ldexp(1.0, -E)[..., None]          # exact: a power of two
     codes = e2m1_encode(scaled).reshape(rows, K)
     return pack_nibbles(codes), (E + 127).astype(np.uint8)
+
+
+def mx_quantize_smoothed(bits, inv_s):
+    """MXFP4 of the smoothed activation X' = X diag(s)^-1 (the SVDQuant Guide, "2.
+    SmoothQuant Pre-Conditioning for DiTs").  The division by s_j is taken as a
+    multiply by the fp32 factor inv_s[j] = 1/s_j, in fp32 with round to nearest even:
+    v = fp32(x * inv_s[j]).  v is then quantized exactly as mx_quantize quantizes a
+    bf16 element (every fp32 value is exact in fp64).
+
+    inv_s: float32 [K], positive and finite.  Returns (codes, scales) as mx_quantize.
+    """
+    bits = _rows(bits, MX_BLOCK)
+    inv_s = np.asarray(inv_s, dtype=np.float32)
+    if inv_s.shape != (bits.shape[1],) or not np.all(np.isfinite(inv_s)) or np.any(~(inv_s > 0)):
+        raise ValueError("inv_s must be a positive finite fp32 vector of length K")
+    x = bf16_to_f32(bits)
+    check_finite(x, "activation")
+    v = (x * inv_s[None, :]).astype(np.float32)              # fp32 multiply, RNE
+    check_finite(v, "smoothed activation")
+    return _mx_quantize_values(v.astype(np.float64))
 
 
 def mx_dequantize(codes, scales):

@@ -81,6 +81,27 @@ def test_quantize_act_rejections():
     assert qa(M=0) == B.Q4_OK                            # empty: nothing queued
 
 
+def qs(**kw):
+    a = dict(fmt=0, x=OK16, M=64, K=256, ldx=256, inv=OK16, codes=OK16, scales=OK16, l1t=None, r=0,
+             t=None)
+    a.update(kw)
+    return lib().quantize_act_smooth(a["fmt"], a["x"], a["M"], a["K"], a["ldx"], a["inv"], a["codes"],
+                                     a["scales"], a["l1t"], a["r"], a["t"], None)
+
+
+def test_quantize_act_smooth_rejections():
+    assert qs(fmt=1) == B.Q4_ERR_FORMAT                  # MXFP4 only
+    assert qs(fmt=2) == B.Q4_ERR_FORMAT
+    assert qs(inv=None) == B.Q4_ERR_NULL
+    assert qs(x=None) == B.Q4_ERR_NULL
+    assert qs(r=32, l1t=OK16, t=None) == B.Q4_ERR_NULL
+    assert qs(K=48, ldx=48) == B.Q4_ERR_SHAPE
+    assert qs(r=8, l1t=OK16, t=OK16) == B.Q4_ERR_SHAPE
+    assert qs(inv=ODD) == B.Q4_ERR_ALIGN
+    assert qs(x=ODD) == B.Q4_ERR_ALIGN
+    assert qs(M=0) == B.Q4_OK
+
+
 def gw(**kw):
     a = dict(fmt=0, ac=OK16, asc=OK16, ats=None, bc=OK16, bsc=OK16, bts=None, M=256, N=256, K=256,
              bias=None, y=OK16, ldy=256, out=0)
