@@ -91,7 +91,7 @@ def cpu_baseline(d, budget_s=12.0):
                       f"(+ low-rank, + error bound) against all {N} columns; {dt:.1f} s"}
 
 
-GEMM_KERNEL_PREFIX = "void q4::gemm_mx_kernel<32, false>"
+GEMM_KERNEL_PREFIX = "void q4::gemm_mx_kernel<32, false, false>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 CAL_BYTES = 256 * 2 ** 20          # the calibration copy below: 64 Mi fp32 in, 64 Mi fp32 out
 
@@ -297,6 +297,32 @@ def bench_rows(reps=50):
         emit(f"gemm_w4a4 mxfp4 {Mq}x{Kq}x{n} bf16 out", ms, flops=2.0 * Mq * n * Kq,
              peak=MXFP4_PEAK_TFLOPS, note="inputs warm in L2/MALL")
 
+    # ---- f1: the MXFP4-emitting epilogue at the MLP up-projection with the rank-32
+    # branch, against the unfused pair (bf16 store, then quantize_act reading it back)
+    dm = synth.mlp_up_svd(seed=0)
+    tq2 = torch.empty((Mq, RANK), dtype=torch.float32, device=dev)
+    l1m = bf16_dev(np.ascontiguousarray(dm["l1"].T))
+    l2m = bf16_dev(np.ascontiguousarray(dm["l2"].T))
+    bcm, bsm, _ = B.empty_quant("mxfp4", Np, Kq, dev)
+    B.pack_weights("mxfp4", bf16_dev(dm["rt"]), Kq, Np, 1, Kq, bcm, bsm, stream=stream)
+    acm, asm_, _ = B.empty_quant("mxfp4", Mq, Kq, dev)
+    B.quantize_act("mxfp4", bf16_dev(dm["x"]), acm, asm_, l1t=l1m, t=tq2, stream=stream)
+    yq_c, yq_s, _ = B.empty_quant("mxfp4", Mq, Np, dev)
+    ym = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)
+    ms_f = timed(lambda i: B.gemm_w4a4_lowrank_mxout(acm, asm_, bcm, bsm, Mq, Np, Kq, yq_c, yq_s, t=tq2,
+                                                     l2t=l2m, stream=stream), 1)
+    emit(f"gemm_w4a4_lowrank_mxout mxfp4 {Mq}x{Kq}x{Np} r={RANK}", ms_f, flops=2.0 * Mq * Np * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note="output as MXFP4 codes + scales for the next layer (no bf16 store)")
+
+    def unfused(i):
+        B.gemm_w4a4_lowrank("mxfp4", acm, asm_, None, bcm, bsm, None, Mq, Np, Kq, tq2, l2m, ym, stream=stream)
+        B.quantize_act("mxfp4", ym, yq_c, yq_s, stream=stream)
+    ms_u = timed(unfused, 1)
+    emit(f"gemm_w4a4_lowrank + quantize_act {Mq}x{Kq}x{Np} r={RANK}", ms_u, flops=2.0 * Mq * Np * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note=f"unfused: bf16 Y stored and read back; fused saves "
+                                      f"{(ms_u - ms_f) * 1e3:.1f} us")
+    del dm, ym
+
     # ---- comparison: the vendor MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on
     # the same codes and E8M0 scales, row-major scale layout
     y = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)
@@ -327,6 +353,56 @@ def bench_rows(reps=50):
         ms = timed(lambda i: torch.matmul(xw, wbf.t(), out=y), 1)
         emit(f"torch bf16 matmul {m}x{Kq}x{Np}", ms, flops=2.0 * m * Np * Kq, peak=2500.0,
              note="comparison: hipBLASLt via torch, unquantized bf16 weight")
+
+    # ---- f2: SVDQuant pre-conditioning on the attention projection (X N(0,1) with 1% of
+    # channels x U(30,100)): the smoothed quantizer's time, and the layer's error against
+    # the unquantized bf16 product for plain W4A4, the unsmoothed SVD split and SVDQuant
+    # (GPU outputs on 64 sampled rows, reference in fp64 on the host)
+    del x0, xw, wt, wbf, y
+    d = synth.attn_proj_svdquant(seed=0)
+    Ms, Ks, Ns, rs = d["M"], d["K"], d["N"], d["rank"]
+    xsv = bf16_dev(d["x"])
+    xsl = [xsv] + [xsv.clone() for _ in range(9)]
+    inv = torch.from_numpy(d["inv_s"]).to(dev)
+    l1t_s = bf16_dev(np.ascontiguousarray(d["l1"].T))
+    l2t_s = bf16_dev(np.ascontiguousarray(d["l2"].T))
+    sc_, ss_, _ = B.empty_quant("mxfp4", Ms, Ks, dev)
+    ts_ = torch.empty((Ms, rs), dtype=torch.float32, device=dev)
+    ms = timed(lambda i: B.quantize_act_smooth("mxfp4", xsl[i], inv, sc_, ss_, l1t_s, ts_, stream), len(xsl))
+    emit(f"quantize_act_smooth mxfp4 r={rs} {Ms}x{Ks}", ms,
+         bytes_=2 * Ms * Ks + Ms * Ks // 2 + Ms * Ks // 32 + 4 * Ks + 4 * Ms * rs + 2 * Ks * rs,
+         note="SmoothQuant factors applied in the quantizer; 10 rotating copies of X")
+    del xsl
+    rows_q = np.sort(np.random.default_rng(1).choice(Ms, 64, replace=False))
+    xf = synth.bf16_bits_to_f32(d["x"][rows_q]).astype(np.float64)
+    exact = xf @ synth.bf16_bits_to_f32(d["wt"]).astype(np.float64).T
+
+    def layer_err(wt_bits, l1_bits=None, l2_bits=None, smooth=False):
+        bc_, bs_, _ = B.empty_quant("mxfp4", Ns, Ks, dev)
+        B.pack_weights("mxfp4", bf16_dev(wt_bits), Ks, Ns, 1, Ks, bc_, bs_, stream=stream)
+        yq = torch.empty((Ms, Ns), dtype=torch.float32, device=dev)
+        if l1_bits is None:
+            B.quantize_act("mxfp4", xsv, sc_, ss_, stream=stream)
+            B.gemm_w4a4("mxfp4", sc_, ss_, None, bc_, bs_, None, Ms, Ns, Ks, yq, out=B.OUT_F32, stream=stream)
+        else:
+            l1d, l2d = bf16_dev(np.ascontiguousarray(l1_bits.T)), bf16_dev(np.ascontiguousarray(l2_bits.T))
+            if smooth:
+                B.quantize_act_smooth("mxfp4", xsv, inv, sc_, ss_, l1d, ts_, stream)
+            else:
+                B.quantize_act("mxfp4", xsv, sc_, ss_, l1t=l1d, t=ts_, stream=stream)
+            B.gemm_w4a4_lowrank("mxfp4", sc_, ss_, None, bc_, bs_, None, Ms, Ns, Ks, ts_, l2d, yq,
+                                out=B.OUT_F32, stream=stream)
+        torch.cuda.synchronize()
+        yh = yq.cpu().numpy()[rows_q].astype(np.float64)
+        return float(np.linalg.norm(yh - exact) / np.linalg.norm(exact))
+
+    l1p, l2p, rtp = synth.lowrank_split(d["wt"], rs, 0)
+    errs = {"w4a4": layer_err(d["wt"]), "svd_split": layer_err(rtp, l1p, l2p),
+            "svdquant": layer_err(d["rt"], d["l1"], d["l2"], smooth=True)}
+    print(json.dumps({"row": f"svdquant quality attn_proj {Ms}x{Ks}x{Ns} r={rs}",
+                      "rel_error_vs_bf16_product": {k: round(v, 5) for k, v in errs.items()},
+                      "note": "64 sampled rows; plain W4A4, the unsmoothed rank-32 SVD split, and "
+                              "smoothing + activation-weighted rank-32 split"}), flush=True)
 
 
 def summarize_rows_profile(stats_csv, command):
@@ -479,7 +555,7 @@ def main():
                    "rank": RANK, "format": "mxfp4", "output": "bf16",
                    "step": "quantize_act(+X L1) -> gemm_w4a4_lowrank", "input_sets": N_SETS},
         "pct_of_mxfp4_peak": round(100.0 * value / MXFP4_PEAK_TFLOPS, 2),
-        "roofline": {"kernel": "gemm_mx_kernel<32,false>", "bound": "mfma",
+        "roofline": {"kernel": "gemm_mx_kernel<32,false,false>", "bound": "mfma",
                      "achieved": round(gemm_tflops, 2), "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(), "avg_launch_ms": round(gemm_ms, 5),

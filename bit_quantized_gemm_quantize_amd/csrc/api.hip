@@ -136,6 +136,32 @@ q4_status gemm_w4a4_lowrank(q4_format fmt, const uint8_t* a_codes, const uint8_t
   return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
 }
 
+q4_status gemm_w4a4_lowrank_mxout(const uint8_t* a_codes, const uint8_t* a_scales,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                  int64_t N, int64_t K, const float* t, const uint16_t* l2t,
+                                  int32_t r, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                                  uint8_t* y_codes, int64_t ldc, uint8_t* y_scales, int64_t lds,
+                                  void* stream) {
+  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || (N % 32) != 0 || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || K > kMaxK) return Q4_ERR_SHAPE;
+  if (ldc < N / 2 || lds < N / 32 || (y && ldy < N)) return Q4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !y_codes || !y_scales) return Q4_ERR_NULL;
+  if (r > 0 && (!t || !l2t)) return Q4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(y_codes, 4) || (ldc % 4) != 0)
+    return Q4_ERR_ALIGN;
+  if (y && (!aligned(y, 16) || (ldy % 8) != 0)) return Q4_ERR_ALIGN;
+  if (r > 0 && (!aligned(t, 16) || !aligned(l2t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0 || N == 0) return Q4_OK;
+  q4::EpilogueArgs ep{r > 0 ? t : nullptr, r > 0 ? l2t : nullptr, (int)r, bias, y, y ? ldy : 0, 0};
+  ep.qc = y_codes;
+  ep.ldc = ldc;
+  ep.qs = y_scales;
+  ep.lds = lds;
+  return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 q4_status gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* w_codes,
                      const uint16_t* w_scales, const uint16_t* w_zeros, int64_t M, int64_t N,
                      int64_t K, int32_t group, const uint16_t* bias, void* y, int64_t ldy,

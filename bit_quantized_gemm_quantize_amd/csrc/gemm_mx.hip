@@ -200,6 +200,15 @@ struct MxLoads {
   }
 };
 
+// MXFP4 output of the tile for the next layer (QOUT): codes [M, N/2] and scale bytes
+// [M, N/32] with row strides in bytes.
+struct MxQOut {
+  uint8_t* qc;
+  int64_t ldc;
+  uint8_t* qs;
+  int64_t lds;
+};
+
 // Output staging for a tile whose successor's first K-tile already fills stage 0:
 // each wave stages 128 rows x 128 bytes at a time in 16 KB of stage 1 (wave w: the
 // stage-1 tile of operand w / 2, offset 16 KB (w % 2)), its 16-byte chunks
@@ -273,12 +282,12 @@ __device__ __forceinline__ u32x4 mx_stage1_read(const uint8_t* stage, int i, int
 // the loads past K, so only the low-rank operands remain for the next prologue.
 // Once the tile's LDS is free again, issue_next(chained) queues what remains of the
 // next tile's prologue; the return value is the number of stores queued after it.
-template <int R, bool OUT_F32, int F, class Next>
+template <int R, bool OUT_F32, bool QOUT, int F, class Next>
 __device__ __forceinline__ int mx_tile(
     uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0,
-    int pending, int next_kind, int64_t nm0, int64_t nn0, Next&& issue_next) {
+    int pending, int next_kind, int64_t nm0, int64_t nn0, const MxQOut& qo, Next&& issue_next) {
   using L = MxLoads<F>;
   constexpr int kMma = 4 * F;                    // MFMAs per wave per step
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
@@ -300,7 +309,7 @@ __device__ __forceinline__ int mx_tile(
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
-  const bool chain = F == kFFull && next_kind == 1 && (nkt & 3) == 0 && nkt >= 4;
+  const bool chain = !QOUT && F == kFFull && next_kind == 1 && (nkt & 3) == 0 && nkt >= 4;
   const L nx(lds_raw, ac, as, bc, bs, M, N, K, chain ? nm0 : m0, chain ? nn0 : n0);
   const int pairs = nkt >> 1;
   auto gload_part = [&](auto part_c, int kt, int stage) {
@@ -538,6 +547,13 @@ __device__ __forceinline__ int mx_tile(
   wait_vmem();                               // the loads past K have landed
   __syncthreads();                           // all waves are done with the operand LDS
   uint8_t* stage = lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>();
+  if constexpr (QOUT) {
+    epilogue_store_mxfp4<F>(acc, n_base, m_base, M, N, bias, static_cast<uint16_t*>(y), ldy, qo.qc,
+                            qo.ldc, qo.qs, qo.lds, lane, stage);
+    lds_barrier();
+    issue_next(false);
+    return 0;
+  }
   // A wave region inside the output, bf16: staged into registers, so that the LDS is
   // free for the next tile's loads before the stores go out.  Otherwise (edges, fp32)
   // staged and stored pass by pass.
@@ -569,12 +585,12 @@ __device__ __forceinline__ bool mx_unit(int u, int tiles_m, int tiles_n, int ful
 // still runs on XCD u % 8 when G is a multiple of 8.  Each tile queues the next
 // one's first loads as soon as its output is staged, ahead of its own stores, so
 // the stores drain while the next tile starts.
-template <int R, bool OUT_F32>
+template <int R, bool OUT_F32, bool QOUT>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
     const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
     const uint16_t* __restrict__ l2t, const uint16_t* __restrict__ bias, void* __restrict__ y,
-    int64_t ldy, int tiles_m, int tiles_n, int full, int units) {
+    int64_t ldy, int tiles_m, int tiles_n, int full, int units, MxQOut qo) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainLds];
   const int nkt = (int)((K + kKT - 1) / kKT);
   const int step = gridDim.x;
@@ -604,11 +620,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
       else prologue(nh, nm, nn);
     };
     if (half)
-      pending = mx_tile<R, OUT_F32, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0,
-                                           pending, next_kind, nm, nn, issue_next);
+      pending = mx_tile<R, OUT_F32, QOUT, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0,
+                                                 n0, pending, next_kind, nm, nn, qo, issue_next);
     else
-      pending = mx_tile<R, OUT_F32, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0,
-                                           pending, next_kind, nm, nn, issue_next);
+      pending = mx_tile<R, OUT_F32, QOUT, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0,
+                                                 n0, pending, next_kind, nm, nn, qo, issue_next);
     u = nu;
     half = nh;
     m0 = nm;
@@ -616,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   }
 }
 
-template <int R, bool F32>
+template <int R, bool F32, bool QOUT = false>
 static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                   int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
@@ -632,14 +648,19 @@ static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const
   const int units = full + 2 * (tiles - full);
   // one workgroup per CU (the LDS allows no more), each looping over its units
   const int grid = units < cus ? units : cus;
-  hipLaunchKernelGGL((gemm_mx_kernel<R, F32>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M, N,
-                     K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full, units);
+  hipLaunchKernelGGL((gemm_mx_kernel<R, F32, QOUT>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M,
+                     N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full, units,
+                     MxQOut{ep.qc, ep.ldc, ep.qs, ep.lds});
 }
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K,
                           const EpilogueArgs& ep, hipStream_t s) {
-  if (ep.out_f32) {
+  if (ep.qc != nullptr) {
+    if (ep.r == 0) queue<0, false, true>(ac, as, bc, bs, M, N, K, ep, s);
+    else if (ep.r == 16) queue<16, false, true>(ac, as, bc, bs, M, N, K, ep, s);
+    else queue<32, false, true>(ac, as, bc, bs, M, N, K, ep, s);
+  } else if (ep.out_f32) {
     if (ep.r == 0) queue<0, true>(ac, as, bc, bs, M, N, K, ep, s);
     else if (ep.r == 16) queue<16, true>(ac, as, bc, bs, M, N, K, ep, s);
     else queue<32, true>(ac, as, bc, bs, M, N, K, ep, s);

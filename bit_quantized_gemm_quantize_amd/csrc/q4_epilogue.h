@@ -278,4 +278,47 @@ __device__ __forceinline__ void epilogue_store_regs(const u32x4 (&out)[RegEpilog
     st16_stream(base + (int64_t)E::kRowsPerStore * it * ldy, out[it]);
 }
 
+// MXFP4 output for the next layer: the bf16 output of a wave's 128 x 32F region is
+// staged in one pass (as epilogue_stage_to_regs) and, instead of (or besides) being
+// stored, each row's 32-column blocks are quantized exactly as quantize_act
+// quantizes a bf16 activation: shared exponent E = floor(log2 amax) - 2 of the block's
+// bf16 values, codes RNE_E2M1(y * 2**-E).  A lane reads 8 columns; the 4 lanes of a
+// block exchange their maxima with DPP quad permutes.  Codes go to qc [M, N/2] (row
+// stride ldc bytes, low nibble = even column), scale bytes to qs [M, N/32] (stride
+// lds), the bf16 values to y when y is not null.  N is a multiple of 32, so a block
+// is either wholly inside the output or wholly outside.
+template <int F>
+__device__ __forceinline__ void epilogue_store_mxfp4(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
+                                                     int64_t M, int64_t N,
+                                                     const uint16_t* __restrict__ bias, uint16_t* y,
+                                                     int64_t ldy, uint8_t* qc, int64_t ldc, uint8_t* qs,
+                                                     int64_t lds, int lane, uint8_t* stage) {
+  using E = RegEpilogue<F>;
+  if (bias)
+    epilogue_stage_pass<false, F, 64 * F, false, true>(acc, 0, n_base, N, bias, lane, stage, 1.0f);
+  else
+    epilogue_stage_pass<false, F, 64 * F, false, false>(acc, 0, n_base, N, bias, lane, stage, 1.0f);
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
+  const int chunk = lane % E::kLanesPerRow;     // 8 columns: chunk / 4 is the block
+  const int64_t n = n_base + chunk * 8;
+#pragma unroll 4
+  for (int it = 0; it < E::kStores; ++it) {
+    const int ml = E::kRowsPerStore * it + lane / E::kLanesPerRow;
+    const int64_t m = m_base + ml;
+    const u32x4 v = ld16(stage + ml * E::S::kStageRowBytes + chunk * 16);
+    const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+    uint32_t amax = bf16_amax_bits<4>(w);
+    amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    const int ex = mx_block_exponent(amax);
+    const uint32_t codes = fp4_encode8_pow2(w, exp2i(ex));
+    if (m < M && n < N) {
+      *reinterpret_cast<uint32_t*>(qc + m * ldc + (n >> 1)) = codes;
+      if ((chunk & 3) == 0) qs[m * lds + (n >> 5)] = (uint8_t)(ex + 127);
+      if (y != nullptr) st16(y + m * ldy + n, v);
+    }
+  }
+}
+
 }  // namespace q4

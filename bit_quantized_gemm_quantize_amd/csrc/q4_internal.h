@@ -26,6 +26,12 @@ struct EpilogueArgs {
   void* y;
   int64_t ldy;
   int out_f32;            // 0: bf16, 1: fp32
+  // MXFP4 output for the next layer (MXFP4 GEMM only): codes [M, N/2] and scale
+  // bytes [M, N/32], row strides in bytes; qc == nullptr: none (y is then required)
+  uint8_t* qc = nullptr;
+  int64_t ldc = 0;
+  uint8_t* qs = nullptr;
+  int64_t lds = 0;
 };
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,

@@ -200,6 +200,29 @@ Q4_API q4_status gemm_w4a4_lowrank(q4_format fmt,
                             const uint16_t* bias, void* y, int64_t ldy, q4_out out, void* stream);
 
 /*
+ * gemm_w4a4_lowrank_mxout -- the MXFP4 gemm_w4a4_lowrank whose epilogue emits the
+ * next layer's activation in MXFP4 instead of (or besides) bf16: the output row's
+ * bf16 values, exactly as they would be stored, are quantized in 32-column blocks
+ * the way quantize_act quantizes a bf16 activation.  The next layer then needs no
+ * separate quantizer pass over Y (the fusion the "Four Bits" FLUX.2 walk-through's
+ * closing notes point to).
+ *
+ *   a_*, b_*, M, N, K, t, l2t, r, bias   as gemm_w4a4_lowrank, MXFP4 operands; r may
+ *             be 0 (no low-rank term).  N a multiple of 32.
+ *   y   (out) bf16 [M, N] (row stride ldy), or NULL not to store it; when given,
+ *             16-byte aligned, ldy a multiple of 8 and >= N.
+ *   y_codes (out)  uint8 [M, N/2], row stride ldc bytes (>= N/2, a multiple of 4),
+ *             4-byte aligned; low nibble = even column.
+ *   y_scales (out) uint8 E8M0 [M, N/32], row stride lds bytes (>= N/32).
+ */
+Q4_API q4_status gemm_w4a4_lowrank_mxout(const uint8_t* a_codes, const uint8_t* a_scales,
+                                  const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                  int64_t N, int64_t K, const float* t, const uint16_t* l2t,
+                                  int32_t r, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                                  uint8_t* y_codes, int64_t ldc, uint8_t* y_scales, int64_t lds,
+                                  void* stream);
+
+/*
  * gemm_w4a16 -- the weight-only comparison path: Y = X w_hat^T (+ bias) with
  * w_hat = bf16((q - z) s) dequantized tile by tile in LDS and a bf16 MFMA GEMM
  * (SVDQuant Guide, "Why Standard Low-Bit Quantization Fails on DiTs", third point,

@@ -18,7 +18,8 @@ transposes of its L2 and L1.
 
 import numpy as np
 
-from .formats import bf16_to_f64, bf16_ulp
+from .formats import bf16_to_f64, bf16_ulp, f32_to_bf16_rne
+from .quant import mx_quantize
 
 GEMM_REL_TOL = 1e-3
 
@@ -98,3 +99,16 @@ def unquantized_ref(x_bits, wt_bits, bias_bits=None):
     if bias_bits is not None:
         y = y + bf16_to_f64(bias_bits)[None, :]
     return y
+
+
+def mx_output(y):
+    """The layer output handed to the next layer in MXFP4: Y rounded to bf16 (nearest
+    even), then quantized along N in 32-column blocks as mx_quantize quantizes any
+    bf16 activation.  Defined here for results that are exact fp32 values (the exact
+    special cases of the tests), so the bf16 rounding is a single rounding, as in a
+    kernel that rounds its fp32 result once.  Returns (codes [M, N/2], scales
+    [M, N/32])."""
+    y = np.asarray(y, dtype=np.float64)
+    if not np.array_equal(y, y.astype(np.float32).astype(np.float64)):
+        raise ValueError("mx_output takes results that are exact fp32 values")
+    return mx_quantize(f32_to_bf16_rne(y.astype(np.float32)))

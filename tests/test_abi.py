@@ -81,6 +81,30 @@ def test_quantize_act_rejections():
     assert qa(M=0) == B.Q4_OK                            # empty: nothing queued
 
 
+def gq(**kw):
+    a = dict(ac=OK16, asc=OK16, bc=OK16, bsc=OK16, M=256, N=256, K=256, t=None, l2t=None, r=0,
+             bias=None, y=None, ldy=0, qc=OK16, ldc=128, qs=OK16, lds=8)
+    a.update(kw)
+    return lib().gemm_w4a4_lowrank_mxout(a["ac"], a["asc"], a["bc"], a["bsc"], a["M"], a["N"], a["K"],
+                                         a["t"], a["l2t"], a["r"], a["bias"], a["y"], a["ldy"],
+                                         a["qc"], a["ldc"], a["qs"], a["lds"], None)
+
+
+def test_gemm_mxout_rejections():
+    assert gq(N=48) == B.Q4_ERR_SHAPE                    # N not a multiple of 32
+    assert gq(K=192) == B.Q4_ERR_SHAPE                   # K not a multiple of 128
+    assert gq(ldc=64) == B.Q4_ERR_SHAPE                  # codes row shorter than N/2
+    assert gq(lds=4) == B.Q4_ERR_SHAPE
+    assert gq(y=OK16, ldy=128) == B.Q4_ERR_SHAPE         # ldy < N
+    assert gq(r=4, t=OK16, l2t=OK16) == B.Q4_ERR_SHAPE
+    assert gq(qc=None) == B.Q4_ERR_NULL
+    assert gq(qs=None) == B.Q4_ERR_NULL
+    assert gq(r=16, t=None, l2t=OK16) == B.Q4_ERR_NULL
+    assert gq(ldc=130) == B.Q4_ERR_ALIGN                 # code rows 4-byte aligned
+    assert gq(y=ODD, ldy=256) == B.Q4_ERR_ALIGN
+    assert gq(M=0) == B.Q4_OK
+
+
 def qs(**kw):
     a = dict(fmt=0, x=OK16, M=64, K=256, ldx=256, inv=OK16, codes=OK16, scales=OK16, l1t=None, r=0,
              t=None)
