@@ -204,8 +204,9 @@ Q4_API q4_status gemm_w4a4_lowrank(q4_format fmt,
  * next layer's activation in MXFP4 instead of (or besides) bf16: the output row's
  * bf16 values, exactly as they would be stored, are quantized in 32-column blocks
  * the way quantize_act quantizes a bf16 activation.  The next layer then needs no
- * separate quantizer pass over Y (the fusion the "Four Bits" FLUX.2 walk-through's
- * closing notes point to).
+ * separate quantizer pass over Y.  ("NVIDIA Technical Blog Details FLUX 3 Image
+ * Klein ...", first optimization layer: 4-bit GEMMs whose epilogues carry the next
+ * operation; handing the next layer its 4-bit input is that kind of fusion.)
  *
  *   a_*, b_*, M, N, K, t, l2t, r, bias   as gemm_w4a4_lowrank, MXFP4 operands; r may
  *             be 0 (no low-rank term).  N a multiple of 32.
