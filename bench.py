@@ -323,6 +323,21 @@ def bench_rows(reps=50):
                                       f"{(ms_u - ms_f) * 1e3:.1f} us")
     del dm, ym
 
+    # ---- f3: symmetric INT4 W4A4 on the INT8 MFMA (no 4-bit integer matrix
+    # instruction on gfx950), same activations and weight as the MXFP4 row above
+    xi, xis, _ = B.empty_quant("int4_sym", Mq, Kq, dev)
+    B.quantize_act("int4_sym", x0, xi, xis, stream=stream)
+    wi, wis, _ = B.empty_quant("int4_sym", Np, Kq, dev)
+    B.pack_weights("int4_sym", wt, Kq, Np, 1, Kq, wi, wis, stream=stream)
+    yi = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda i: B.gemm_w4a4("int4_sym", xi, xis, None, wi, wis, None, Mq, Np, Kq, yi, stream=stream), 1)
+    emit(f"gemm_w4a4 int4_sym {Mq}x{Kq}x{Np} bf16 out", ms, flops=2.0 * Mq * Np * Kq, peak=5000.0,
+         note="int4 widened to int8 for the INT8 MFMA; peak = dense INT8 5.0 POP/s")
+    ms = timed(lambda i: B.quantize_act("int4_sym", x0, xi, xis, stream=stream), 1)
+    emit(f"quantize_act int4_sym {Mq}x{Kq}", ms, bytes_=2 * Mq * Kq + Mq * Kq // 2 + 4 * Mq,
+         note="two passes over each row (amax, then codes; the second from the cache)")
+    del yi
+
     # ---- comparison: the vendor MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on
     # the same codes and E8M0 scales, row-major scale layout
     y = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)

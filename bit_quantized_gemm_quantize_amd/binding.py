@@ -16,9 +16,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4lin.so")
 
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_FORMAT, Q4_ERR_LAUNCH = range(6)
-MXFP4, NVFP4, INT4_G64 = 0, 1, 2
+MXFP4, NVFP4, INT4_G64, INT4_SYM = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
-FORMATS = {"mxfp4": MXFP4, "nvfp4": NVFP4, "int4_g64": INT4_G64}
+FORMATS = {"mxfp4": MXFP4, "nvfp4": NVFP4, "int4_g64": INT4_G64, "int4_sym": INT4_SYM}
 
 # name -> (restype, argtypes), in the order of include/q4lin.h
 _c = ctypes
@@ -174,5 +174,7 @@ def empty_quant(fmt, rows, K, device="cuda"):
     if fmt == NVFP4:
         return (codes, torch.empty((rows, K // 16), dtype=torch.uint8, device=device),
                 torch.empty(1, dtype=torch.float32, device=device))
+    if fmt == INT4_SYM:
+        return codes, torch.empty(rows, dtype=torch.float32, device=device), None
     return (codes, torch.empty((rows, K // 64), dtype=torch.bfloat16, device=device),
             torch.empty((rows, K // 64), dtype=torch.bfloat16, device=device))

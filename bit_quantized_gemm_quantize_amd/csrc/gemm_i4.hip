@@ -1,0 +1,161 @@
+// INT4 x INT4 GEMM, symmetric with one fp32 scale per row of each operand (the
+// per-channel quantizer of the SVDQuant Guide's "Step 1"), on the INT8 MFMA:
+// gfx950 has no 4-bit integer matrix instruction, so the nibbles are widened to
+// int8 between the LDS read and the MFMA ("Quantization for the impatient": a
+// 4-bit format pays off only where the hardware multiplies it natively).
+//
+// Y[m, n] = fp32(fp32(sum_k qa[m,k] qb[n,k]) * sa[m]) * sb[n] (+ bias), the sum exact
+// in int32 (|sum| <= 64 K < 2^31 for K <= 2^22... and exact in fp32 while below 2^24).
+//
+// Tiling as the MXFP4 GEMM: 256 x 256 output tile per workgroup of 4 waves, wave
+// (wm, wn) owning 128 x 128 as 4 x 4 tiles of v_mfma_i32_32x32x32_i8 with int32
+// accumulators in the matrix registers; K-tiles of 256 codes (128 bytes per row)
+// loaded straight into two LDS stages with 16-byte chunks XOR-swizzled by row.
+// Lane half h reads K blocks 4h + s (16 bytes, 32 codes) in step s; the 32 codes
+// feed two MFMAs of 16 int8 each.  Both operands are widened with the same
+// permutation (even nibbles, then odd), which a sum over K allows.
+#include "q4_epilogue.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kI4BM = 256, kI4BN = 256, kI4KT = 256, kI4KTB = kI4KT / 2;
+constexpr int kI4Waves = 4, kI4Threads = 64 * kI4Waves;
+constexpr int kI4Lds = 2 * 2 * kI4BM * kI4KTB;                      // [operand][stage]
+static_assert(kI4Waves * EpilogueShape<true, 4, 128>::kStageWaveBytes <= kI4Lds &&
+                  kI4Waves * EpilogueShape<false, 4, 128>::kStageWaveBytes <= kI4Lds,
+              "the epilogue stages each wave's output in the operand LDS");
+
+// 8 packed signed nibbles -> 8 int8: the even nibbles in lo, the odd ones in hi.
+// Per byte, t = v ^ 8 maps the nibble v to 8 + v (v < 8) or v - 8; adding 0x78 and
+// flipping bit 7 gives v or v - 16 as int8, with no carry between bytes.
+__device__ __forceinline__ void i4_widen(uint32_t d, uint32_t& lo, uint32_t& hi) {
+  lo = (((d & 0x0F0F0F0Fu) ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+  hi = ((((d >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// A 16-byte fragment (32 codes) -> the two int8 MFMA operands it feeds.
+__device__ __forceinline__ void i4_operands(u32x4 f, v4i& op0, v4i& op1) {
+  uint32_t a, b, c, d;
+  i4_widen(f[0], a, b);
+  i4_widen(f[1], c, d);
+  op0 = v4i{(int)a, (int)b, (int)c, (int)d};
+  i4_widen(f[2], a, b);
+  i4_widen(f[3], c, d);
+  op1 = v4i{(int)a, (int)b, (int)c, (int)d};
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kI4Threads) void gemm_i4_kernel(
+    const uint8_t* __restrict__ ac, const float* __restrict__ as, const uint8_t* __restrict__ bc,
+    const float* __restrict__ bs, int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kI4Lds];
+  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kI4BM * kI4KTB]>(lds_raw);
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, 4, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kI4BM, n0 = (int64_t)tn * kI4BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t kbytes = (uint32_t)(K >> 1), nblk = (uint32_t)(K >> 5);
+  const int nkt = (int)((K + kI4KT - 1) / kI4KT);
+  const uint32_t rows_a = rows_in(kI4BM, M, m0), rows_b = rows_in(kI4BN, N, n0);
+  const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
+  const auto rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
+
+  // K-tile kt -> stage: each wave moves 64 activation and 64 weight rows, 8 rows of
+  // 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding global
+  // chunk (i % 8) ^ (row & 7)); rows and blocks past the matrix read as zero
+  const int lr = lane >> 3, lp = lane & 7;
+  auto load_ktile = [&](int kt, int stage) {
+    const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);
+    const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t row = 64 * wave + 8 * j + lr;
+      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kI4KTB], row * kbytes + koff);
+      buf_ld16_lds(rc_b, &lds[1][stage][(64 * wave + 8 * j) * kI4KTB], row * kbytes + koff);
+    }
+  };
+  auto frag = [&](int op, int stage, int row, int s) {
+    return ld16(&lds[op][stage][row * kI4KTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+  };
+
+  v16i acc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = v16i{};
+
+  if (nkt > 0) load_ktile(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nkt) load_ktile(kt + 1, st ^ 1);          // stage st^1 was freed by the last barrier
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) i4_operands(frag(0, st, wm * 128 + 32 * g + r32, s), a0[g], a1[g]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) i4_operands(frag(1, st, wn * 128 + 32 * f + r32, s), b0[f], b1[f]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[f], a0[g], acc[f][g], 0, 0, 0);
+          acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[f], a1[g], acc[f][g], 0, 0, 0);
+        }
+    }
+    wait_vmem();                                           // K-tile kt+1 has landed
+    __syncthreads();                                       // and every read of stage st is done
+  }
+
+  // scales: acc[f][g] register j is row m = m_base + 32 g + lane % 32, column
+  // n = n_base + 32 f + 8 (j / 4) + 4 h + j % 4.  Indices past the matrix are clamped
+  // (those results are never stored), so the loads need no branches.
+  const int64_t n_base = n0 + wn * 128, m_base = m0 + wm * 128;
+  v16f accf[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    float sb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t n = n_base + 32 * f + 8 * (j >> 2) + 4 * h + (j & 3);
+      sb[j] = bs[n < N ? n : N - 1];
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t m = m_base + 32 * g + r32;
+      const float sa = as[m < M ? m : M - 1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) accf[f][g][j] = (float)acc[f][g][j] * sa * sb[j];
+    }
+  }
+  epilogue_store<OUT_F32, 4, 128>(accf, n_base, m_base, M, N, bias, y, ldy, lane,
+                                  lds_raw + wave * EpilogueShape<OUT_F32, 4, 128>::kStageWaveBytes);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_i4(const uint8_t* ac, const float* as, const uint8_t* bc, const float* bs,
+                          int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
+  const int tiles_m = (int)((M + kI4BM - 1) / kI4BM), tiles_n = (int)((N + kI4BN - 1) / kI4BN);
+  const unsigned grid = (unsigned)(tiles_m * tiles_n);
+  if (ep.out_f32)
+    hipLaunchKernelGGL((gemm_i4_kernel<true>), dim3(grid), dim3(kI4Threads), 0, s, ac, as, bc, bs, M, N, K,
+                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_i4_kernel<false>), dim3(grid), dim3(kI4Threads), 0, s, ac, as, bc, bs, M, N, K,
+                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace q4

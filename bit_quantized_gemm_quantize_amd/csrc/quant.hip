@@ -336,6 +336,64 @@ hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------- int4 symmetric
+// Signed int4, symmetric, one fp32 scale per row: scale = max(amax / 7, 1e-8) and
+// q = clamp(rint(x / scale), -8, 7), every step in fp32 (IEEE division, round half
+// to even).  One wave per row of a strided bf16 matrix (element (r, k) at
+// x[r * sr + k * sk]); two passes over the row (the second from the cache).  Codes
+// are two's-complement nibbles, the even k in the low nibble.
+__global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t K, int64_t sr, int64_t sk,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;                     // the whole wave
+  const uint16_t* row = x + r * sr;
+  const bool contig = sk == 1 && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  const int64_t chunks = K >> 3;             // 8 elements (16 bytes of bf16) each
+  auto load8 = [&](int64_t c, uint32_t* w) {
+    if (contig) {
+      const u32x4 v = ld16(row + 8 * c);
+      w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)row[(8 * c + 2 * j) * sk] | ((uint32_t)row[(8 * c + 2 * j + 1) * sk] << 16);
+    }
+  };
+  uint32_t m = 0;
+  for (int64_t c = lane; c < chunks; c += 64) {
+    uint32_t w[4];
+    load8(c, w);
+    m = max(m, bf16_amax_bits<4>(w));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  const float scale = fmaxf(__uint_as_float(m << 16) / 7.0f, 1e-8f);
+  if (lane == 0) scales[r] = scale;
+  uint8_t* out = codes + r * (K >> 1);
+  for (int64_t c = lane; c < chunks; c += 64) {
+    uint32_t w[4];
+    load8(c, w);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+      const float q = fminf(fmaxf(__builtin_rintf(v / scale), -8.0f), 7.0f);
+      packed |= ((uint32_t)(int)q & 0xFu) << (4 * j);
+    }
+    *reinterpret_cast<uint32_t*>(out + 4 * c) = packed;
+  }
+}
+
+hipError_t launch_int4_sym_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
+                                uint8_t* codes, float* scales, hipStream_t s) {
+  hipLaunchKernelGGL(int4_sym_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, x, rows,
+                     K, sr, sk, codes, scales);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------- weight packers
 // One thread per (output column n, K group); consecutive threads take consecutive
 // n, so a [K, N] row-major weight is read coalesced and a [N, K] one row-wise.

@@ -76,7 +76,15 @@ typedef enum q4_format {
    * q = clamp(RNE(w/s) + z, 0, 15); the GEMM operand is bf16((q - z) s).  The
    * weight-only (W4A16) path the SVDQuant Guide contrasts with W4A4 in
    * "Why Standard Low-Bit Quantization Fails on DiTs". */
-  Q4_INT4_G64 = 2
+  Q4_INT4_G64 = 2,
+  /* Signed int4, symmetric, one fp32 scale per row (per token / per output channel):
+   * scale = max(fp32(amax / 7), 1e-8), q = clamp(round_half_even(x / scale), -8, 7)
+   * -- the per-channel quantizer of the SVDQuant Guide's "Step 1".  Scales are
+   * float [rows].  The GEMM runs on the INT8 MFMA (gfx950 has no 4-bit integer
+   * matrix instruction): the comparison "Quantization for the impatient" draws
+   * between native and emulated 4-bit matmul.  quantize_act (r = 0),
+   * pack_weights and gemm_w4a4 only. */
+  Q4_INT4_SYM = 3
 } q4_format;
 
 typedef enum q4_out {
@@ -90,12 +98,13 @@ typedef enum q4_out {
  * DiTs"), fused with the low-rank down-projection t = X L1 of the same pass over X
  * (SVDQuant Guide, "3. The Nunchaku Fused Kernel Engine": one pass, no second read).
  *
- *   fmt           Q4_MXFP4 or Q4_NVFP4 (else Q4_ERR_FORMAT).
+ *   fmt           Q4_MXFP4, Q4_NVFP4 or Q4_INT4_SYM (r = 0 only) (else Q4_ERR_FORMAT).
  *   x             bf16 [M, K], row stride ldx elements.  16-byte aligned, ldx a
  *                 multiple of 8, ldx >= K.
  *   M, K          0 <= M <= 2^30; K >= 0 and a multiple of 32.
  *   codes  (out)  uint8 [M, K/2].  16-byte aligned.
- *   scales (out)  MXFP4: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16].
+ *   scales (out)  MXFP4: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16];
+ *                 INT4_SYM: float [M] (passed through this pointer).
  *                 4-byte aligned.
  *   tensor_scale  NVFP4: float[1], written with s_t (also used as the amax
  *                 accumulator while the call runs).  MXFP4: ignored, may be NULL.
@@ -135,7 +144,7 @@ Q4_API q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M
  * several to a word).  The same encoders as quantize_act, along K for every output
  * column n.
  *
- *   fmt               Q4_MXFP4, Q4_NVFP4 or Q4_INT4_G64.
+ *   fmt               Q4_MXFP4, Q4_NVFP4, Q4_INT4_G64 or Q4_INT4_SYM.
  *   w                 bf16, logical [K, N]: element (k, n) at w[k*stride_k + n*stride_n]
  *                     (stride_k = 1, stride_n = K for nn.Linear's [out, in] storage;
  *                     stride_k = N, stride_n = 1 for row-major [K, N]).  Strides >= 1.
@@ -144,7 +153,7 @@ Q4_API q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M
  *   K, N              K a multiple of 32 (MXFP4, NVFP4) or 64 (INT4_G64).
  *   codes  (out)      uint8 [N, K/2], 16-byte aligned.
  *   scales (out)      MXFP4: uint8 [N, K/32]; NVFP4: uint8 E4M3 [N, K/16];
- *                     INT4_G64: bf16 [N, K/64].  4-byte aligned.
+ *                     INT4_G64: bf16 [N, K/64]; INT4_SYM: float [N].  4-byte aligned.
  *   zeros  (out)      INT4_G64: bf16 [N, K/64] (integers 0..15); else ignored.
  *   tensor_scale(out) NVFP4: float[1] (s_t of the weight); else ignored.
  */
@@ -160,6 +169,9 @@ Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64
  *   fmt       Q4_MXFP4: block-scaled FP4 MFMA.  Q4_NVFP4: exact dequantization
  *             to bf16 (every E2M1 x E4M3 product fits bf16) and bf16 MFMA; the two
  *             tensor scales multiply the fp32 result.
+ *             Q4_INT4_SYM: int4 codes widened to int8 for the INT8 MFMA, int32
+ *             sums, fp32 row scales (a_scales float [M], b_scales float [N])
+ *             applied in the epilogue (gemm_w4a4 only).
  *   a_*       activation codes [M, K/2] and scales (layout as quantize_act);
  *             a_tscale: NVFP4 float[1], else ignored.
  *   b_*       weight codes [N, K/2] and scales (layout as pack_weights).

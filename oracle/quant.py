@@ -198,3 +198,39 @@ def int4_g64_dequantize(codes, scales, zeros):
         raise ValueError("bad int4 scale/zero shape")
     prod = (q.reshape(rows, K // INT4_GROUP, INT4_GROUP) - z[..., None]) * s[..., None]
     return bf16_to_f64(f32_to_bf16_rne(prod.reshape(rows, K)))
+
+
+# ----------------------------------------------------------------------------- int4 symmetric
+INT4_QMAX, INT4_QMIN = 7, -8
+INT4_SCALE_FLOOR = np.float32(1e-8)
+
+
+def int4_sym_quantize(bits):
+    """Signed int4, symmetric, one fp32 scale per row (per output channel for a
+    weight stored [N, K], per token for an activation), the per-channel quantizer of
+    the SVDQuant Guide's "Step 1: Low-Rank Outlier Decomposition in PyTorch":
+
+        scale = max(fp32(amax / 7), 1e-8)                   amax over the row's K values
+        q     = clamp(RNE(fp32(x / scale)), -8, 7)          RNE: half to even (torch.round)
+
+    Each step is taken in fp32 (the bf16 inputs are exact there).  Codes are the
+    two's-complement low 4 bits, packed two per byte with the even k in the low
+    nibble.  Returns (codes uint8 [rows, K/2], scales float32 [rows]).
+    """
+    bits = _rows(bits, 2)
+    x = bf16_to_f32(bits)
+    check_finite(x, "activation/weight")
+    amax = np.abs(x).max(axis=1)                                      # fp32, exact
+    scale = np.maximum(amax / np.float32(INT4_QMAX), INT4_SCALE_FLOOR)  # fp32 division
+    q = np.clip(np.rint(x / scale[:, None]), INT4_QMIN, INT4_QMAX)    # fp32 division, RNE
+    return pack_nibbles((q.astype(np.int64) & 0xF).astype(np.uint8)), scale.astype(np.float32)
+
+
+def int4_sym_dequantize(codes, scales):
+    """int4 codes (two's complement nibbles) and fp32 row scales -> fp64 q * scale."""
+    n = unpack_nibbles(codes).astype(np.int64)
+    q = np.where(n >= 8, n - 16, n)
+    scales = np.asarray(scales, dtype=np.float32)
+    if scales.shape != (q.shape[0],):
+        raise ValueError("bad int4 scale vector shape")
+    return q * scales.astype(np.float64)[:, None]

@@ -79,6 +79,8 @@ def test_quantize_act_rejections():
     assert qa(ldx=260) == B.Q4_ERR_ALIGN
     assert qa(r=16, l1t=ODD, t=OK16) == B.Q4_ERR_ALIGN
     assert qa(M=0) == B.Q4_OK                            # empty: nothing queued
+    assert qa(fmt=3, r=16, l1t=OK16, t=OK16) == B.Q4_ERR_FORMAT   # int4 sym: no fused t
+    assert qa(fmt=3, M=0) == B.Q4_OK
 
 
 def gq(**kw):
@@ -164,6 +166,7 @@ def test_gemm_w4a4_lowrank_rejections():
     assert call(t=None) == B.Q4_ERR_NULL
     assert call(l2t=ODD) == B.Q4_ERR_ALIGN
     assert call(fmt=9) == B.Q4_ERR_FORMAT
+    assert call(fmt=3) == B.Q4_ERR_FORMAT                # int4 sym has no low-rank GEMM
     assert call(M=0) == B.Q4_OK
 
 

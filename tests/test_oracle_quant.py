@@ -251,3 +251,40 @@ def test_int4_scale_and_zero_definition_brute_force():
             assert F.bf16_to_f64(sc[r:r + 1, g])[0] == s_t
             z = np.float32(-np.float32(lo) / np.float32(s_t))
             assert F.bf16_to_f64(zc[r:r + 1, g])[0] == min(15, max(0, round(float(z))))
+
+
+# ----------------------------------------------------------------------------- int4 symmetric
+def test_int4_sym_against_brute_force():
+    """Per row: scale = fp32(amax / 7) (struct-rounded Python float division), each
+    element rounded half-to-even with Python's round() on the fp32 quotient."""
+    import struct
+
+    def f32(v):
+        return struct.unpack("<f", struct.pack("<f", v))[0]
+
+    rng = np.random.default_rng(21)
+    x = synth.to_bf16_bits(rng.standard_normal((6, 64)) * np.exp(rng.uniform(-6, 6, (6, 1))))
+    x[5] = 0                                                   # an all-zero row: scale 1e-8, codes 0
+    codes, scales = Q.int4_sym_quantize(x)
+    xf = F.bf16_to_f64(x)
+    n = F.unpack_nibbles(codes).astype(int)
+    q = np.where(n >= 8, n - 16, n)
+    for r in range(6):
+        amax = float(np.abs(xf[r]).max())
+        s = max(f32(amax / 7.0), f32(1e-8))
+        assert scales[r] == np.float32(s)
+        for k in range(64):
+            want = max(-8, min(7, round(f32(float(xf[r, k]) / s))))
+            assert q[r, k] == want, (r, k)
+
+
+def test_int4_sym_closed_forms():
+    # the row maximum maps to +-7; multiples of the scale map to themselves; exact
+    # halves round to even (so -8 is never produced: |x| <= amax = 7 scale)
+    s = 0.5
+    vals = np.array([3.5, -3.5, 1.0, -1.0, 0.25, 0.75, -0.25, -0.75, 1.25, -1.25] + [0.0] * 22)
+    x = synth.to_bf16_bits(vals[None, :])
+    codes, scales = Q.int4_sym_quantize(x)
+    assert scales[0] == np.float32(3.5 / 7)
+    deq = Q.int4_sym_dequantize(codes, scales)[0]
+    assert list(deq[:10] / s) == [7, -7, 2, -2, 0, 2, 0, -2, 2, -2]
