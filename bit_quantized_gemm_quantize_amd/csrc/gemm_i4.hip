@@ -4,8 +4,9 @@
 // int8 between the LDS read and the MFMA ("Quantization for the impatient": a
 // 4-bit format pays off only where the hardware multiplies it natively).
 //
-// Y[m, n] = fp32(fp32(sum_k qa[m,k] qb[n,k]) * sa[m]) * sb[n] (+ bias), the sum exact
-// in int32 (|sum| <= 64 K < 2^31 for K <= 2^22... and exact in fp32 while below 2^24).
+// Y[m, n] = fp32(fp32(sum_k qa[m,k] qb[n,k]) * sa[m]) * sb[n] (+ bias).  The sum is
+// exact in int32 (|q| <= 7, so |sum| <= 49 K), and its conversion to fp32 is exact
+// for K <= 2^18.
 //
 // Tiling as the MXFP4 GEMM: 256 x 256 output tile per workgroup of 4 waves, wave
 // (wm, wn) owning 128 x 128 as 4 x 4 tiles of v_mfma_i32_32x32x32_i8 with int32
