@@ -234,3 +234,43 @@ def int4_sym_dequantize(codes, scales):
     if scales.shape != (q.shape[0],):
         raise ValueError("bad int4 scale vector shape")
     return q * scales.astype(np.float64)[:, None]
+
+
+# ----------------------------------------------------------------------------- MXFP8 (E4M3)
+E4M3_EMAX = 8                                                     # 448 = 1.75 * 2**8
+
+
+def mxfp8_quantize(bits):
+    """MXFP8: FP8 E4M3FN elements with one E8M0 scale per 32 consecutive K elements,
+    by the OCP MX v1.0 conversion as for MXFP4 but with emax(E4M3) = 8: E =
+    floor(log2 amax) - 8 clamped to [-127, 127] (-127 for a zero block), each element
+    E4M3_RNE(x * 2**-E) saturated at +-448 (a block's largest values can reach
+    2**9 * (1 - 2**-8) before saturation), sign kept (a negative value that rounds
+    to zero gives 0x80).
+
+    Returns (codes uint8 [rows, K], scales uint8 [rows, K/32]).
+    """
+    bits = _rows(bits, MX_BLOCK)
+    rows, K = bits.shape
+    x = bf16_to_f64(bits)
+    check_finite(x, "activation/weight")
+    blocks = x.reshape(rows, K // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    E = np.where(amax > 0, floor_log2(np.where(amax > 0, amax, 1.0)) - E4M3_EMAX, -127)
+    E = np.clip(E, -127, 127)
+    scaled = blocks * np.ldexp(1.0, -E)[..., None]              # exact: a power of two
+    mag = np.minimum(np.abs(scaled), E4M3_MAX)
+    codes = e4m3_encode(mag) | np.where(np.signbit(scaled), 0x80, 0).astype(np.uint8)
+    return codes.reshape(rows, K).astype(np.uint8), (E + 127).astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scales):
+    """MXFP8 codes/scales -> fp64 [rows, K]: (-1)^s * E4M3 value * 2**(byte - 127)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, K = codes.shape
+    mag = e4m3_decode(codes & 0x7F)
+    vals = np.where(codes & 0x80, -mag, mag)
+    E = np.asarray(scales, dtype=np.uint8).astype(np.int64) - 127
+    if E.shape != (rows, K // MX_BLOCK):
+        raise ValueError("bad MX scale array shape")
+    return (vals.reshape(rows, K // MX_BLOCK, MX_BLOCK) * np.ldexp(1.0, E)[..., None]).reshape(rows, K)

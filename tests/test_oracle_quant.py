@@ -288,3 +288,55 @@ def test_int4_sym_closed_forms():
     assert scales[0] == np.float32(3.5 / 7)
     deq = Q.int4_sym_dequantize(codes, scales)[0]
     assert list(deq[:10] / s) == [7, -7, 2, -2, 0, 2, 0, -2, 2, -2]
+
+
+# ----------------------------------------------------------------------------- MXFP8
+def _e4m3_values():
+    """Every non-negative finite E4M3FN value, from the format's definition (exponent
+    bias 7, 3 mantissa bits, subnormals, 0x7F is NaN)."""
+    vals = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        vals.append(Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return vals
+
+
+def test_mxfp8_against_brute_force():
+    """Blocks over a wide range: the scale from math.frexp, each element the nearest
+    E4M3 value (ties to the even code) of x * 2**-E by exhaustive search, saturating at
+    448, sign kept."""
+    import math
+    vals = _e4m3_values()
+    rng = np.random.default_rng(31)
+    x = synth.to_bf16_bits(rng.standard_normal((3, 64)) * np.exp(rng.uniform(-20, 20, (3, 64))))
+    x[2, :32] = synth.to_bf16_bits(np.linspace(-500, 500, 32)[None, :])[0]
+    codes, scales = Q.mxfp8_quantize(x)
+    xf = F.bf16_to_f64(x)
+    for r in range(3):
+        for b in range(2):
+            blk = xf[r, 32 * b:32 * b + 32]
+            amax = float(np.abs(blk).max())
+            E = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
+            assert scales[r, b] == E + 127
+            for j in range(32):
+                v = Fraction(float(blk[j])) / Fraction(2) ** E
+                m = min(abs(v), Fraction(448))
+                best = min(range(0x7F), key=lambda c: (abs(vals[c] - m), c & 1))
+                want = best | (0x80 if math.copysign(1.0, float(blk[j])) < 0 else 0)
+                assert codes[r, 32 * b + j] == want, (r, b, j)
+
+
+def test_mxfp8_round_trip_and_saturation():
+    # grid values times 2**E with 448 * 2**E present come back exactly; values between
+    # 448 and 512 (times 2**E) saturate to 448
+    grid = np.array([float(v) for v in _e4m3_values()])
+    rng = np.random.default_rng(32)
+    blk = rng.choice(grid, 32) * rng.choice([-1, 1], 32)
+    blk[0] = 448.0 * 1.0                      # floor(log2 448) = 8 -> E = 0
+    x = synth.to_bf16_bits((blk * 2.0 ** 5)[None, :])
+    codes, scales = Q.mxfp8_quantize(x)
+    assert scales[0, 0] == 127 + 5
+    assert np.array_equal(Q.mxfp8_dequantize(codes, scales)[0], blk * 2.0 ** 5)
+    y = synth.to_bf16_bits(np.array([[480.0, -496.0, 256.0] + [0.0] * 29]))
+    c2, s2 = Q.mxfp8_quantize(y)
+    assert s2[0, 0] == 127 and list(Q.mxfp8_dequantize(c2, s2)[0, :3]) == [448.0, -448.0, 256.0]
