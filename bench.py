@@ -336,7 +336,32 @@ def bench_rows(reps=50):
     ms = timed(lambda i: B.quantize_act("int4_sym", x0, xi, xis, stream=stream), 1)
     emit(f"quantize_act int4_sym {Mq}x{Kq}", ms, bytes_=2 * Mq * Kq + Mq * Kq // 2 + 4 * Mq,
          note="two passes over each row (amax, then codes; the second from the cache)")
-    del yi
+    del yi, xi, wi
+
+    # ---- f4: MXFP8 W8A8 on the same block-scaled MFMA with E4M3 operands
+    x8, x8s, _ = B.empty_quant("mxfp8", Mq, Kq, dev)
+    B.quantize_act("mxfp8", x0, x8, x8s, stream=stream)
+    w8, w8s, _ = B.empty_quant("mxfp8", Np, Kq, dev)
+    B.pack_weights("mxfp8", wt, Kq, Np, 1, Kq, w8, w8s, stream=stream)
+    y8 = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda i: B.gemm_w4a4("mxfp8", x8, x8s, None, w8, w8s, None, Mq, Np, Kq, y8, stream=stream), 1)
+    emit(f"gemm_w4a4 mxfp8 {Mq}x{Kq}x{Np} bf16 out", ms, flops=2.0 * Mq * Np * Kq, peak=5000.0,
+         note="E4M3 x E4M3 with E8M0 block scales; peak = dense FP8 5.0 PFLOP/s")
+    ms = timed(lambda i: B.quantize_act("mxfp8", x0, x8, x8s, stream=stream), 1)
+    emit(f"quantize_act mxfp8 {Mq}x{Kq}", ms, bytes_=2 * Mq * Kq + Mq * Kq + Mq * Kq // 32)
+    try:
+        a8v, b8v = x8.view(torch.float8_e4m3fn), w8.view(torch.float8_e4m3fn)
+        sa8, sb8 = x8s.view(torch.float8_e8m0fnu), w8s.view(torch.float8_e8m0fnu)
+        y_lib = torch._scaled_mm(a8v, b8v.t(), sa8, sb8, out_dtype=torch.bfloat16)
+        diff = (y_lib.float() - y8.float()).abs().max().item() / max(y8.float().abs().max().item(), 1e-30)
+        ms = timed(lambda i: torch._scaled_mm(a8v, b8v.t(), sa8, sb8, out_dtype=torch.bfloat16), 1)
+        emit(f"torch._scaled_mm mxfp8 {Mq}x{Kq}x{Np} bf16 out", ms, flops=2.0 * Mq * Np * Kq, peak=5000.0,
+             note=f"comparison: hipBLASLt MXFP8 on the same codes and scales; max |diff| / max |y| "
+                  f"vs gemm_w4a4 = {diff:.2e}")
+    except (RuntimeError, TypeError, AttributeError) as e:
+        print(json.dumps({"row": "torch._scaled_mm mxfp8", "note": f"unavailable: {str(e)[:200]}"}),
+              flush=True)
+    del y8, x8, w8
 
     # ---- comparison: the vendor MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on
     # the same codes and E8M0 scales, row-major scale layout

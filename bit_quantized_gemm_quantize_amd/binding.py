@@ -16,9 +16,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4lin.so")
 
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_FORMAT, Q4_ERR_LAUNCH = range(6)
-MXFP4, NVFP4, INT4_G64, INT4_SYM = 0, 1, 2, 3
+MXFP4, NVFP4, INT4_G64, INT4_SYM, MXFP8 = 0, 1, 2, 3, 4
 OUT_BF16, OUT_F32 = 0, 1
-FORMATS = {"mxfp4": MXFP4, "nvfp4": NVFP4, "int4_g64": INT4_G64, "int4_sym": INT4_SYM}
+FORMATS = {"mxfp4": MXFP4, "nvfp4": NVFP4, "int4_g64": INT4_G64, "int4_sym": INT4_SYM, "mxfp8": MXFP8}
 
 # name -> (restype, argtypes), in the order of include/q4lin.h
 _c = ctypes
@@ -168,6 +168,9 @@ def gemm_w4a16(x, w_codes, w_scales, w_zeros, N, y, bias=None, group=64, out=OUT
 def empty_quant(fmt, rows, K, device="cuda"):
     """Output buffers for quantize_act / pack_weights: (codes, scales, tensor_scale|zeros)."""
     fmt = _fmt(fmt)
+    if fmt == MXFP8:
+        return (torch.empty((rows, K), dtype=torch.uint8, device=device),
+                torch.empty((rows, K // 32), dtype=torch.uint8, device=device), None)
     codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
     if fmt == MXFP4:
         return codes, torch.empty((rows, K // 32), dtype=torch.uint8, device=device), None

@@ -22,7 +22,7 @@ q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_sca
                      const float* a_tscale, const uint8_t* b_codes, const uint8_t* b_scales,
                      const float* b_tscale, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy,
                      q4_out out) {
-  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM) return Q4_ERR_FORMAT;
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8) return Q4_ERR_FORMAT;
   if (out != Q4_OUT_BF16 && out != Q4_OUT_F32) return Q4_ERR_FORMAT;
   if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || ldy < N) return Q4_ERR_SHAPE;
   if (M > kMaxRows || N > kMaxRows || K > kMaxK) return Q4_ERR_SHAPE;
@@ -54,8 +54,8 @@ const char* q4_status_string(q4_status s) {
 q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                        uint8_t* codes, uint8_t* scales, float* tensor_scale,
                        const uint16_t* l1t, int32_t r, float* t, void* stream) {
-  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM) return Q4_ERR_FORMAT;
-  if (fmt == Q4_INT4_SYM && r != 0) return Q4_ERR_FORMAT;
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8) return Q4_ERR_FORMAT;
+  if ((fmt == Q4_INT4_SYM || fmt == Q4_MXFP8) && r != 0) return Q4_ERR_FORMAT;
   if (M < 0 || K < 0 || (K % 32) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
   if (M > kMaxRows) return Q4_ERR_SHAPE;
   if (!x || !codes || !scales) return Q4_ERR_NULL;
@@ -69,6 +69,8 @@ q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, i
   if (fmt == Q4_INT4_SYM)
     return launched(q4::launch_int4_sym_rows(x, M, K, ldx, 1, codes, reinterpret_cast<float*>(scales),
                                              static_cast<hipStream_t>(stream)));
+  if (fmt == Q4_MXFP8)
+    return launched(q4::launch_mxfp8_rows(x, M, K, ldx, 1, codes, scales, static_cast<hipStream_t>(stream)));
   return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t,
                                           (int)r, t, static_cast<hipStream_t>(stream)));
 }
@@ -93,7 +95,8 @@ q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64
 q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, int64_t stride_k,
                        int64_t stride_n, uint8_t* codes, void* scales, uint16_t* zeros,
                        float* tensor_scale, void* stream) {
-  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_G64 && fmt != Q4_INT4_SYM) return Q4_ERR_FORMAT;
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_G64 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8)
+    return Q4_ERR_FORMAT;
   const int64_t blk = fmt == Q4_INT4_G64 ? 64 : 32;
   if (K < 0 || N < 0 || (K % blk) != 0 || stride_k < 1 || stride_n < 1) return Q4_ERR_SHAPE;
   if (!w || !codes || !scales) return Q4_ERR_NULL;
@@ -106,6 +109,9 @@ q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, i
   if (fmt == Q4_INT4_SYM)
     return launched(q4::launch_int4_sym_rows(w, N, K, stride_n, stride_k, codes,
                                              static_cast<float*>(scales), static_cast<hipStream_t>(stream)));
+  if (fmt == Q4_MXFP8)
+    return launched(q4::launch_mxfp8_rows(w, N, K, stride_n, stride_k, codes, static_cast<uint8_t*>(scales),
+                                          static_cast<hipStream_t>(stream)));
   return launched(q4::launch_pack_weights((int)fmt, w, K, N, stride_k, stride_n, codes, scales, zeros,
                                           tensor_scale, static_cast<hipStream_t>(stream)));
 }
@@ -123,6 +129,7 @@ q4_status gemm_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scal
   if (fmt == Q4_INT4_SYM)
     return launched(q4::launch_gemm_i4(a_codes, reinterpret_cast<const float*>(a_scales), b_codes,
                                        reinterpret_cast<const float*>(b_scales), M, N, K, ep, s));
+  if (fmt == Q4_MXFP8) return launched(q4::launch_gemm_mx8(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
   if (fmt == Q4_MXFP4) return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
   return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
 }
@@ -135,7 +142,7 @@ q4_status gemm_w4a4_lowrank(q4_format fmt, const uint8_t* a_codes, const uint8_t
   q4_status st = check_w4a4(fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K,
                             y, ldy, out);
   if (st != Q4_OK) return st;
-  if (fmt == Q4_INT4_SYM) return Q4_ERR_FORMAT;
+  if (fmt == Q4_INT4_SYM || fmt == Q4_MXFP8) return Q4_ERR_FORMAT;
   if (!rank_ok(r)) return Q4_ERR_SHAPE;
   if (r > 0 && (!t || !l2t)) return Q4_ERR_NULL;
   if (r > 0 && (!aligned(t, 16) || !aligned(l2t, 16))) return Q4_ERR_ALIGN;

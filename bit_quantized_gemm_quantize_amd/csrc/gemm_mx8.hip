@@ -1,0 +1,161 @@
+// MXFP8 x MXFP8 GEMM (E4M3 elements, one E8M0 scale per 32 K elements per row) on
+// the same CDNA4 block-scaled MFMA as the MXFP4 GEMM, with format code 0 (FP8
+// E4M3) on both operands: the 8-bit member of the OCP MX family the pages set
+// beside MXFP4 ("Quantization for the impatient", formats table).  One
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes twice the cycles of its FP4 form, and
+// each operand is twice the bytes, so this GEMM has half the FP4 peak.
+//
+// Tiling: 256 x 256 output tile per workgroup of 4 waves, wave (wm, wn) owning
+// 128 x 128 as 4 x 4 MFMA tiles with fp32 accumulators in the matrix registers.
+// K advances in tiles of 128 elements (128 bytes per row, 4 scale bytes per row),
+// loaded straight into two LDS stages with the 16-byte chunks XOR-swizzled by row
+// (chunk c of row r at c ^ (r & 7)).  An MFMA step consumes 64 K elements, and
+// with 8-bit operands the instruction splits each 32-element block over the two
+// lane halves (measured on gfx950: lane half h holds K [16h, 16h+16) of the step
+// in its first 16 bytes and K [32+16h, 32+16h+16) in its last 16, and block b is
+// scaled by the scale operand of lane half b).  So in step s lane half h reads
+// chunks 4s + h and 4s + 2 + h and supplies the scale of block 2s + h: its scale
+// dword for the K-tile (blocks 0..3 of the tile for its row) is shifted right by
+// 8 h, so byte 2s of it is that scale, and op_sel 2s picks it.
+#include "q4_epilogue.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int kX8BM = 256, kX8BN = 256, kX8KT = 128, kX8KTB = kX8KT;
+constexpr int kX8Waves = 4, kX8Threads = 64 * kX8Waves;
+constexpr int kX8Lds = 2 * 2 * kX8BM * kX8KTB;                      // [operand][stage]
+constexpr int kFmtFP8 = 0;                                          // f8f6f4 operand code for E4M3
+static_assert(kX8Waves * EpilogueShape<true, 4, 128>::kStageWaveBytes <= kX8Lds &&
+                  kX8Waves * EpilogueShape<false, 4, 128>::kStageWaveBytes <= kX8Lds,
+              "the epilogue stages each wave's output in the operand LDS");
+
+// The MFMAs of step S (0 or 1) of a K-tile: the weight fragment is the MFMA's first
+// operand, so accumulator register j of lane l holds column n = acc_row(j, l) and
+// row m = l % 32 of the 32 x 32 result, the layout the epilogue takes.
+template <int S>
+__device__ __forceinline__ void mx8_step(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4],
+                                         const uint32_t (&sa)[4], const uint32_t (&sb)[4]) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[f], a[g], acc[f][g], kFmtFP8, kFmtFP8,
+                                                                  2 * S, (int)sb[f], 2 * S, (int)sa[g]);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
+    const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kX8Lds];
+  auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kX8BM * kX8KTB]>(lds_raw);
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, 4, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kX8BM, n0 = (int64_t)tn * kX8BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t kbytes = (uint32_t)K, nblk = (uint32_t)(K >> 5), nchunk = (uint32_t)(K >> 4);
+  const int nkt = (int)(K / kX8KT);
+  const uint32_t rows_a = rows_in(kX8BM, M, m0), rows_b = rows_in(kX8BN, N, n0);
+  const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
+  const auto rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
+  const auto rs_a = make_rsrc(as + m0 * nblk, rows_a * nblk);
+  const auto rs_b = make_rsrc(bs + n0 * nblk, rows_b * nblk);
+
+  // K-tile kt -> stage: each wave moves 64 activation and 64 weight rows, 8 rows of
+  // 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding global
+  // chunk (i % 8) ^ (row & 7)); rows past the matrix read as zero
+  const int lr = lane >> 3, lp = lane & 7;
+  auto load_ktile = [&](int kt, int stage) {
+    const uint32_t chunk = (uint32_t)kt * 8 + (lp ^ lr);
+    const uint32_t koff = chunk < nchunk ? chunk * 16 : kOOB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t row = 64 * wave + 8 * j + lr;
+      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff);
+      buf_ld16_lds(rc_b, &lds[1][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff);
+    }
+  };
+  // the lane's scale dwords of K-tile kt (rows past the matrix read as zero)
+  uint32_t sa_n[4], sb_n[4];
+  auto load_scales = [&](int kt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      sa_n[g] = buf_ld4(rs_a, (uint32_t)(wm * 128 + 32 * g + r32) * nblk + 4 * kt);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      sb_n[f] = buf_ld4(rs_b, (uint32_t)(wn * 128 + 32 * f + r32) * nblk + 4 * kt);
+  };
+  auto frag = [&](int op, int stage, int row, int s) {
+    const uint8_t* base = &lds[op][stage][row * kX8KTB];
+    const int c = 4 * s + h;
+    const u32x4 lo = ld16(base + ((c ^ (row & 7)) << 4)), hi = ld16(base + (((c + 2) ^ (row & 7)) << 4));
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
+
+  if (nkt > 0) {
+    load_ktile(0, 0);
+    load_scales(0);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int st = kt & 1;
+    uint32_t sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = sa_n[i] >> (8 * h);
+      sb[i] = sb_n[i] >> (8 * h);
+    }
+    if (kt + 1 < nkt) {                                    // stage st^1 was freed by the last barrier
+      load_ktile(kt + 1, st ^ 1);
+      load_scales(kt + 1);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      v8i a[4], b[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) a[g] = frag(0, st, wm * 128 + 32 * g + r32, s);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = frag(1, st, wn * 128 + 32 * f + r32, s);
+      if (s == 0)
+        mx8_step<0>(acc, a, b, sa, sb);
+      else
+        mx8_step<1>(acc, a, b, sa, sb);
+    }
+    wait_vmem();                                           // K-tile kt+1 and its scales have landed
+    __syncthreads();                                       // and every read of stage st is done
+  }
+
+  const int64_t n_base = n0 + wn * 128, m_base = m0 + wm * 128;
+  epilogue_store<OUT_F32, 4, 128>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                                  lds_raw + wave * EpilogueShape<OUT_F32, 4, 128>::kStageWaveBytes);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mx8(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                           int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
+  const int tiles_m = (int)((M + kX8BM - 1) / kX8BM), tiles_n = (int)((N + kX8BN - 1) / kX8BN);
+  const unsigned grid = (unsigned)(tiles_m * tiles_n);
+  if (ep.out_f32)
+    hipLaunchKernelGGL((gemm_mx8_kernel<true>), dim3(grid), dim3(kX8Threads), 0, s, ac, as, bc, bs, M, N, K,
+                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_mx8_kernel<false>), dim3(grid), dim3(kX8Threads), 0, s, ac, as, bc, bs, M, N, K,
+                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -37,6 +37,12 @@ struct EpilogueArgs {
 hipError_t launch_int4_sym_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
                                 uint8_t* codes, float* scales, hipStream_t s);
 
+hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+hipError_t launch_gemm_mx8(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                           int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s);
+
 hipError_t launch_gemm_i4(const uint8_t* ac, const float* as, const uint8_t* bc, const float* bs,
                           int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s);
 

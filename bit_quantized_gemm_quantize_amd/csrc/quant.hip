@@ -394,6 +394,64 @@ hipError_t launch_int4_sym_rows(const uint16_t* x, int64_t rows, int64_t K, int6
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------- MXFP8 (E4M3)
+// One thread per (row, 32-element block) of a strided bf16 matrix: E = floor(log2
+// amax) - 8 (emax of E4M3FN) clamped to [-127, 127], codes E4M3_RNE(x * 2**-E)
+// saturated at +-448 (the product is exact in fp32; the clamp comes before the
+// converter, which rounds to nearest even), 32 code bytes and one scale byte out.
+__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                         int64_t K, int64_t sr, int64_t sk,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+  const int64_t nblk = K >> 5;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= rows * nblk) return;
+  const int64_t r = q / nblk, b = q % nblk;
+  const uint16_t* src = x + r * sr + b * 32 * sk;
+  uint32_t w[16];
+  if (sk == 1 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = ld16(src + 8 * c);
+      w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = (uint32_t)src[2 * j * sk] | ((uint32_t)src[(2 * j + 1) * sk] << 16);
+  }
+  const uint32_t amax = bf16_amax_bits<16>(w);
+  int E = amax == 0 ? -127 : bf16_floor_log2(amax) - 8;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  const float down = exp2i(-E);
+  uint32_t out[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * d + j;
+      const float xv = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      v[j] = fminf(fmaxf(xv * down, -448.0f), 448.0f);
+    }
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+    out[d] = (uint32_t)word;
+  }
+  uint8_t* dst = codes + r * K + b * 32;
+  st16(dst, u32x4{out[0], out[1], out[2], out[3]});
+  st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
+  scales[r * nblk + b] = (uint8_t)(E + 127);
+}
+
+hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t work = rows * (K >> 5);
+  if (work == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_rows_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, x, rows, K,
+                     sr, sk, codes, scales);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------- weight packers
 // One thread per (output column n, K group); consecutive threads take consecutive
 // n, so a [K, N] row-major weight is read coalesced and a [N, K] one row-wise.

@@ -84,7 +84,16 @@ typedef enum q4_format {
    * matrix instruction): the comparison "Quantization for the impatient" draws
    * between native and emulated 4-bit matmul.  quantize_act (r = 0),
    * pack_weights and gemm_w4a4 only. */
-  Q4_INT4_SYM = 3
+  Q4_INT4_SYM = 3,
+  /* MXFP8: FP8 E4M3FN elements (one byte each), one E8M0 scale byte per 32
+   * consecutive K elements; the OCP MX conversion with emax(E4M3) = 8: shared
+   * exponent floor(log2 amax) - 8 clamped to [-127, 127], elements rounded to
+   * nearest even and saturated at 448, sign kept.  The 8-bit float the pages set
+   * beside FP4 (the E4M3 range +-448 in "Quantization for the impatient",
+   * stability section; the FP8 variants of the FLUX.2 [klein] model page).
+   * Codes are uint8 [rows, K] (not K/2).  quantize_act (r = 0), pack_weights and
+   * gemm_w4a4 only. */
+  Q4_MXFP8 = 4
 } q4_format;
 
 typedef enum q4_out {
@@ -98,12 +107,13 @@ typedef enum q4_out {
  * DiTs"), fused with the low-rank down-projection t = X L1 of the same pass over X
  * (SVDQuant Guide, "3. The Nunchaku Fused Kernel Engine": one pass, no second read).
  *
- *   fmt           Q4_MXFP4, Q4_NVFP4 or Q4_INT4_SYM (r = 0 only) (else Q4_ERR_FORMAT).
+ *   fmt           Q4_MXFP4, Q4_NVFP4, or Q4_INT4_SYM / Q4_MXFP8 (r = 0 only)
+ *                 (else Q4_ERR_FORMAT).
  *   x             bf16 [M, K], row stride ldx elements.  16-byte aligned, ldx a
  *                 multiple of 8, ldx >= K.
  *   M, K          0 <= M <= 2^30; K >= 0 and a multiple of 32.
- *   codes  (out)  uint8 [M, K/2].  16-byte aligned.
- *   scales (out)  MXFP4: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16];
+ *   codes  (out)  uint8 [M, K/2] (MXFP8: [M, K]).  16-byte aligned.
+ *   scales (out)  MXFP4, MXFP8: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16];
  *                 INT4_SYM: float [M] (passed through this pointer).
  *                 4-byte aligned.
  *   tensor_scale  NVFP4: float[1], written with s_t (also used as the amax
@@ -144,15 +154,15 @@ Q4_API q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M
  * several to a word).  The same encoders as quantize_act, along K for every output
  * column n.
  *
- *   fmt               Q4_MXFP4, Q4_NVFP4, Q4_INT4_G64 or Q4_INT4_SYM.
+ *   fmt               Q4_MXFP4, Q4_NVFP4, Q4_INT4_G64, Q4_INT4_SYM or Q4_MXFP8.
  *   w                 bf16, logical [K, N]: element (k, n) at w[k*stride_k + n*stride_n]
  *                     (stride_k = 1, stride_n = K for nn.Linear's [out, in] storage;
  *                     stride_k = N, stride_n = 1 for row-major [K, N]).  Strides >= 1.
  *                     w 2-byte aligned; with stride_k = 1, stride_n a multiple of 8
  *                     and w 16-byte aligned the rows are read 16 bytes at a time.
  *   K, N              K a multiple of 32 (MXFP4, NVFP4) or 64 (INT4_G64).
- *   codes  (out)      uint8 [N, K/2], 16-byte aligned.
- *   scales (out)      MXFP4: uint8 [N, K/32]; NVFP4: uint8 E4M3 [N, K/16];
+ *   codes  (out)      uint8 [N, K/2] (MXFP8: [N, K]), 16-byte aligned.
+ *   scales (out)      MXFP4, MXFP8: uint8 [N, K/32]; NVFP4: uint8 E4M3 [N, K/16];
  *                     INT4_G64: bf16 [N, K/64]; INT4_SYM: float [N].  4-byte aligned.
  *   zeros  (out)      INT4_G64: bf16 [N, K/64] (integers 0..15); else ignored.
  *   tensor_scale(out) NVFP4: float[1] (s_t of the weight); else ignored.
@@ -172,6 +182,8 @@ Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64
  *             Q4_INT4_SYM: int4 codes widened to int8 for the INT8 MFMA, int32
  *             sums, fp32 row scales (a_scales float [M], b_scales float [N])
  *             applied in the epilogue (gemm_w4a4 only).
+ *             Q4_MXFP8: the same block-scaled MFMA with E4M3 operands (codes
+ *             [rows, K]); half the FP4 rate (gemm_w4a4 only).
  *   a_*       activation codes [M, K/2] and scales (layout as quantize_act);
  *             a_tscale: NVFP4 float[1], else ignored.
  *   b_*       weight codes [N, K/2] and scales (layout as pack_weights).

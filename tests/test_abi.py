@@ -81,6 +81,9 @@ def test_quantize_act_rejections():
     assert qa(M=0) == B.Q4_OK                            # empty: nothing queued
     assert qa(fmt=3, r=16, l1t=OK16, t=OK16) == B.Q4_ERR_FORMAT   # int4 sym: no fused t
     assert qa(fmt=3, M=0) == B.Q4_OK
+    assert qa(fmt=4, r=32, l1t=OK16, t=OK16) == B.Q4_ERR_FORMAT   # mxfp8: no fused t
+    assert qa(fmt=4, K=48, ldx=48) == B.Q4_ERR_SHAPE
+    assert qa(fmt=4, M=0) == B.Q4_OK
 
 
 def gq(**kw):
@@ -151,6 +154,9 @@ def test_gemm_w4a4_rejections():
     assert gw(y=ODD) == B.Q4_ERR_ALIGN
     assert gw(bc=ODD) == B.Q4_ERR_ALIGN
     assert gw(M=0) == B.Q4_OK and gw(N=0) == B.Q4_OK
+    assert gw(fmt=4, K=96) == B.Q4_ERR_SHAPE
+    assert gw(fmt=4, asc=ODD) == B.Q4_ERR_ALIGN
+    assert gw(fmt=4, M=0) == B.Q4_OK
 
 
 def test_gemm_w4a4_lowrank_rejections():
@@ -167,6 +173,7 @@ def test_gemm_w4a4_lowrank_rejections():
     assert call(l2t=ODD) == B.Q4_ERR_ALIGN
     assert call(fmt=9) == B.Q4_ERR_FORMAT
     assert call(fmt=3) == B.Q4_ERR_FORMAT                # int4 sym has no low-rank GEMM
+    assert call(fmt=4) == B.Q4_ERR_FORMAT                # nor has mxfp8
     assert call(M=0) == B.Q4_OK
 
 
@@ -192,3 +199,5 @@ def test_gemm_w4a16_and_pack_rejections():
     assert pw(fmt=2, K=96, zeros=OK16) == B.Q4_ERR_SHAPE   # int4 needs K % 64
     assert pw(sk=0) == B.Q4_ERR_SHAPE
     assert pw(K=-32) == B.Q4_ERR_SHAPE
+    assert pw(fmt=4, K=48) == B.Q4_ERR_SHAPE
+    assert pw(fmt=4, sk=0) == B.Q4_ERR_SHAPE
