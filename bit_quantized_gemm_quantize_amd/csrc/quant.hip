@@ -1,7 +1,8 @@
 // Activation quantizer (MXFP4 / NVFP4) fused with the low-rank down-projection,
 // and the offline weight packers.
 //
-// Activation pass (one read of X):
+// Activation pass (one read of X).  Without the low-rank term, MXFP4 takes one
+// thread per block instead (mx_rows_kernel, shared with MXFP8).  With it:
 //   * a workgroup owns up to 32 rows (as many as spread M evenly over the CUs) and
 //     all of K; its 16 waves stride over K in pairs of 32-element blocks, so a lane
 //     (row l%32, half l/32) owns one whole block per step: 64 contiguous bytes of X
@@ -123,6 +124,92 @@ __device__ __forceinline__ int mx_encode_smoothed(const uint32_t* w, const float
   }
   *codes = u32x4{c[0], c[1], c[2], c[3]};
   return E;
+}
+
+// ---------------------------------------------------------------------------- MX per block
+// One thread per (row, 32-element block) of a strided bf16 matrix, consecutive
+// threads on consecutive blocks of a row (contiguous loads and stores).
+//   MXFP8: E = floor(log2 amax) - 8 (emax of E4M3FN) clamped to [-127, 127], codes
+//   E4M3_RNE(x * 2**-E) saturated at +-448 (the product is exact in fp32; the clamp
+//   comes before the converter, which rounds to nearest even), 32 code bytes.
+//   MXFP4 (the activation pass without the low-rank term): E = floor(log2 amax) - 2,
+//   codes by the E2M1 converter, 16 code bytes.
+// One scale byte E + 127 per block.
+template <bool FP8>
+__device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t K, int64_t sr, int64_t sk,
+                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                         int64_t nblk, int64_t q) {
+  const int64_t r = q / nblk, b = q % nblk;
+  const uint16_t* src = x + r * sr + b * 32 * sk;
+  uint32_t w[16];
+  if (sk == 1 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = ld16(src + 8 * c);
+      w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = (uint32_t)src[2 * j * sk] | ((uint32_t)src[(2 * j + 1) * sk] << 16);
+  }
+  const uint32_t amax = bf16_amax_bits<16>(w);
+  if (!FP8) {
+    const int E = mx_block_exponent(amax);
+    const float sc = exp2i(E);
+    st16(codes + r * (K >> 1) + b * 16, u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
+                                               fp4_encode8_pow2(w + 8, sc), fp4_encode8_pow2(w + 12, sc)});
+    scales[r * nblk + b] = (uint8_t)(E + 127);
+    return;
+  }
+  int E = amax == 0 ? -127 : bf16_floor_log2(amax) - 8;
+  E = E < -127 ? -127 : (E > 127 ? 127 : E);
+  const float down = exp2i(-E);
+  uint32_t out[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * d + j;
+      const float xv = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      v[j] = fminf(fmaxf(xv * down, -448.0f), 448.0f);
+    }
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+    out[d] = (uint32_t)word;
+  }
+  uint8_t* dst = codes + r * K + b * 32;
+  st16(dst, u32x4{out[0], out[1], out[2], out[3]});
+  st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
+  scales[r * nblk + b] = (uint8_t)(E + 127);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                      int64_t K, int64_t sr, int64_t sk,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  const int64_t nblk = K >> 5, work = rows * nblk;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += (int64_t)gridDim.x * blockDim.x)
+    mx_block<FP8>(x, K, sr, sk, codes, scales, nblk, q);
+}
+
+// Launch of mx_rows_kernel: one thread per block, the grid capped (the threads
+// then stride over the blocks).
+template <bool FP8>
+static hipError_t queue_mx_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
+                                uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t work = rows * (K >> 5);
+  if (work == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((work + 255) / 256, int64_t(1) << 20);
+  hipLaunchKernelGGL(mx_rows_kernel<FP8>, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, sr, sk, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  return queue_mx_rows<true>(x, rows, K, sr, sk, codes, scales, s);
 }
 
 // ---------------------------------------------------------------------------- activation pass
@@ -322,7 +409,12 @@ hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K,
     if (e != hipSuccess) return e;
   }
   if (fmt == 0) {
-    if (r == 0) queue_quant<0, 0>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
+    // without the low-rank term, one thread per block: the row-per-lane layout only
+    // serves the MFMA of t = X L1
+    if (r == 0) {
+      const hipError_t e = queue_mx_rows<false>(x, M, K, ldx, 1, codes, scales, s);
+      if (e != hipSuccess) return e;
+    }
     else if (r == 16) queue_quant<0, 16>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
     else queue_quant<0, 32>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
   } else {
@@ -391,64 +483,6 @@ hipError_t launch_int4_sym_rows(const uint16_t* x, int64_t rows, int64_t K, int6
                                 uint8_t* codes, float* scales, hipStream_t s) {
   hipLaunchKernelGGL(int4_sym_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, x, rows,
                      K, sr, sk, codes, scales);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------- MXFP8 (E4M3)
-// One thread per (row, 32-element block) of a strided bf16 matrix: E = floor(log2
-// amax) - 8 (emax of E4M3FN) clamped to [-127, 127], codes E4M3_RNE(x * 2**-E)
-// saturated at +-448 (the product is exact in fp32; the clamp comes before the
-// converter, which rounds to nearest even), 32 code bytes and one scale byte out.
-__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                         int64_t K, int64_t sr, int64_t sk,
-                                                         uint8_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales) {
-  const int64_t nblk = K >> 5;
-  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= rows * nblk) return;
-  const int64_t r = q / nblk, b = q % nblk;
-  const uint16_t* src = x + r * sr + b * 32 * sk;
-  uint32_t w[16];
-  if (sk == 1 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 v = ld16(src + 8 * c);
-      w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) w[j] = (uint32_t)src[2 * j * sk] | ((uint32_t)src[(2 * j + 1) * sk] << 16);
-  }
-  const uint32_t amax = bf16_amax_bits<16>(w);
-  int E = amax == 0 ? -127 : bf16_floor_log2(amax) - 8;
-  E = E < -127 ? -127 : (E > 127 ? 127 : E);
-  const float down = exp2i(-E);
-  uint32_t out[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * d + j;
-      const float xv = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      v[j] = fminf(fmaxf(xv * down, -448.0f), 448.0f);
-    }
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-    out[d] = (uint32_t)word;
-  }
-  uint8_t* dst = codes + r * K + b * 32;
-  st16(dst, u32x4{out[0], out[1], out[2], out[3]});
-  st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
-  scales[r * nblk + b] = (uint8_t)(E + 127);
-}
-
-hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
-                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  const int64_t work = rows * (K >> 5);
-  if (work == 0) return hipSuccess;
-  hipLaunchKernelGGL(mxfp8_rows_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, x, rows, K,
-                     sr, sk, codes, scales);
   return hipGetLastError();
 }
 

@@ -70,7 +70,8 @@ def test_quantize_mx_full_attention_projection():
 
 # ------------------------------------------------------------------ low-rank t = X L1
 @pytest.mark.parametrize("M,K,r,fmt", [(64, 256, 32, "mxfp4"), (100, 352, 16, "mxfp4"),
-                                       (70, 512, 32, "nvfp4"), (4608, 3072, 32, "mxfp4")])
+                                       (70, 512, 32, "nvfp4"), (4608, 3072, 32, "mxfp4"),
+                                       (8192, 3104, 32, "mxfp4"), (4700, 1056, 16, "nvfp4")])
 def test_quantize_fused_lowrank_t(M, K, r, fmt):
     dev = device()
     x = synth.activations(M, K, seed=5, dist="student_t3")[0]
