@@ -119,14 +119,14 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None,
     GEMM are the counters' per-dispatch KiB, each scaled by the ratio of the bytes
     the calibration copy really moves to what the same counter reports for it."""
     lines = [f"# rocprofv3 summary: MXFP4 W4A4 GEMM + low-rank epilogue, M={M} K={K} N={N} r={RANK}",
-             "", "command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", ""]
+             "", "commands (R = the repository root; each run after `cd /tmp && export TMPDIR=/tmp`):", ""]
     lines += ["    " + c for c in command]
     lines += ["", "## kernel stats (--kernel-trace --stats)", "",
               "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     gemm_avg_ns = None
     for r in _csv_rows(stats_csv):
         name = r["Name"]
-        short = name.split("(")[0].replace("void ", "")
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
         if name.startswith(GEMM_KERNEL_PREFIX):
@@ -449,11 +449,11 @@ def summarize_rows_profile(stats_csv, command):
     """rocprofv3 --kernel-trace --stats of `bench.py --rows` -> a text table of every
     kernel's average duration (the per-row numbers' own kernels)."""
     lines = ["# rocprofv3 summary: every kernel of `bench.py --rows` (one MI355X)", "",
-             "command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", ""]
+             "commands (R = the repository root; each run after `cd /tmp && export TMPDIR=/tmp`):", ""]
     lines += ["    " + c for c in command]
     lines += ["", "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in _csv_rows(stats_csv):
-        short = r["Name"].split("(")[0].replace("void ", "")
+        short = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         lines.append(f"| `{short[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "Kernels named `Cijk_*` are hipBLASLt's bf16 GEMMs behind the torch comparison rows;",
