@@ -17,6 +17,8 @@
 // chunks 4s + h and 4s + 2 + h and supplies the scale of block 2s + h: its scale
 // dword for the K-tile (blocks 0..3 of the tile for its row) is shifted right by
 // 8 h, so byte 2s of it is that scale, and op_sel 2s picks it.
+#include <type_traits>
+
 #include "q4_epilogue.h"
 
 namespace q4 {
@@ -81,21 +83,29 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
       buf_ld16_lds(rc_b, &lds[1][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff);
     }
   };
-  // the lane's scale dwords of K-tile kt (rows past the matrix read as zero)
-  uint32_t sa_n[4], sb_n[4];
-  auto load_scales = [&](int kt) {
+  // the lane's scale dwords of K-tile kt (rows past the matrix, and K-tiles past K,
+  // read whatever the view holds there or zero: never used)
+  auto load_scales = [&](int kt, uint32_t* da, uint32_t* db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      sa_n[g] = buf_ld4(rs_a, (uint32_t)(wm * 128 + 32 * g + r32) * nblk + 4 * kt);
+      da[g] = buf_ld4(rs_a, (uint32_t)(wm * 128 + 32 * g + r32) * nblk + 4 * kt);
 #pragma unroll
     for (int f = 0; f < 4; ++f)
-      sb_n[f] = buf_ld4(rs_b, (uint32_t)(wn * 128 + 32 * f + r32) * nblk + 4 * kt);
+      db[f] = buf_ld4(rs_b, (uint32_t)(wn * 128 + 32 * f + r32) * nblk + 4 * kt);
   };
+  // fragment registers, double-buffered across MFMA steps
+  v8i fa[2][4], fb[2][4];
   auto frag = [&](int op, int stage, int row, int s) {
     const uint8_t* base = &lds[op][stage][row * kX8KTB];
     const int c = 4 * s + h;
     const u32x4 lo = ld16(base + ((c ^ (row & 7)) << 4)), hi = ld16(base + (((c + 2) ^ (row & 7)) << 4));
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto read_frags = [&](int buf, int stage, int s) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fa[buf][g] = frag(0, stage, wm * 128 + 32 * g + r32, s);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) fb[buf][f] = frag(1, stage, wn * 128 + 32 * f + r32, s);
   };
 
   v16f acc[4][4];
@@ -104,39 +114,58 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
-  if (nkt > 0) {
-    load_ktile(0, 0);
-    load_scales(0);
-  }
+  // Pipeline: K-tiles kt and kt+1 sit in the two stages; the scale dwords of even
+  // and odd K-tiles in two register sets.  In K-tile kt, step 0 runs while the
+  // fragments of step 1 are read; then every wave waits for K-tile kt+1 (loaded a
+  // whole K-tile earlier) and passes the barrier, which frees stage kt % 2 for the
+  // loads of K-tile kt+2; step 1 runs while the fragments of K-tile kt+1's step 0
+  // are read.  The scale loads for kt+2 go out after step 1 (issued earlier, they
+  // would keep a third register set live through it).  Loads past K read zeros
+  // (codes) and are never used.
+  uint32_t sx_a[4], sx_b[4], sy_a[4], sy_b[4];
+  load_ktile(0, 0);
+  load_scales(0, sx_a, sx_b);
+  load_ktile(1, 1);
+  load_scales(1, sy_a, sy_b);
   wait_vmem();
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & 1;
-    uint32_t sa[4], sb[4];
+  read_frags(0, 0, 0);
+  auto ktile = [&](auto stage_c, int kt, uint32_t* sr_a, uint32_t* sr_b) {
+    constexpr int st = decltype(stage_c)::value;
+    // step 0's fragments were read during the last K-tile's step 1: waiting for them
+    // here keeps the 16 reads below from counting against them (the LDS counter
+    // holds at most 15)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    uint32_t ca[4], cb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa[i] = sa_n[i] >> (8 * h);
-      sb[i] = sb_n[i] >> (8 * h);
+      ca[i] = sr_a[i] >> (8 * h);
+      cb[i] = sr_b[i] >> (8 * h);
     }
-    if (kt + 1 < nkt) {                                    // stage st^1 was freed by the last barrier
-      load_ktile(kt + 1, st ^ 1);
-      load_scales(kt + 1);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i a[4], b[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) a[g] = frag(0, st, wm * 128 + 32 * g + r32, s);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) b[f] = frag(1, st, wn * 128 + 32 * f + r32, s);
-      if (s == 0)
-        mx8_step<0>(acc, a, b, sa, sb);
-      else
-        mx8_step<1>(acc, a, b, sa, sb);
-    }
-    wait_vmem();                                           // K-tile kt+1 and its scales have landed
-    __syncthreads();                                       // and every read of stage st is done
+    read_frags(1, st, 1);
+    mx8_step<0>(acc, fa[0], fb[0], ca, cb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmem();                                 // K-tile kt+1 and its scales have landed
+    __syncthreads();                             // and every read of stage st is done
+    load_ktile(kt + 2, st);
+    read_frags(0, st ^ 1, 0);
+    mx8_step<1>(acc, fa[1], fb[1], ca, cb);
+    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_scales(kt + 2, sr_a, sr_b);
+  };
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    ktile(std::integral_constant<int, 0>{}, kt, sx_a, sx_b);
+    ktile(std::integral_constant<int, 1>{}, kt + 1, sy_a, sy_b);
   }
+  if (kt < nkt) ktile(std::integral_constant<int, 0>{}, kt, sx_a, sx_b);
+  wait_vmem();                                   // the loads past K have landed
+  __syncthreads();                               // before the epilogue reuses the LDS
 
   const int64_t n_base = n0 + wn * 128, m_base = m0 + wm * 128;
   epilogue_store<OUT_F32, 4, 128>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
