@@ -17,6 +17,9 @@
 // chunks 4s + h and 4s + 2 + h and supplies the scale of block 2s + h: its scale
 // dword for the K-tile (blocks 0..3 of the tile for its row) is shifted right by
 // 8 h, so byte 2s of it is that scale, and op_sel 2s picks it.
+//
+// Tail: as in the MXFP4 GEMM, the tiles that do not fill a last round over the CUs
+// run as two halves of 128 weight rows each (wave tiles 128 x 64), dispatched first.
 #include <type_traits>
 
 #include "q4_epilogue.h"
@@ -35,43 +38,42 @@ static_assert(kX8Waves * EpilogueShape<true, 4, 128>::kStageWaveBytes <= kX8Lds 
 
 // The MFMAs of step S (0 or 1) of a K-tile: the weight fragment is the MFMA's first
 // operand, so accumulator register j of lane l holds column n = acc_row(j, l) and
-// row m = l % 32 of the 32 x 32 result, the layout the epilogue takes.
-template <int S>
-__device__ __forceinline__ void mx8_step(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4],
-                                         const uint32_t (&sa)[4], const uint32_t (&sb)[4]) {
+// row m = l % 32 of the 32 x 32 result, the layout the epilogue takes.  F weight
+// sub-tiles of 32 rows per wave: 4 in a whole tile, 2 in a half.
+template <int S, int F>
+__device__ __forceinline__ void mx8_step(v16f (&acc)[F][4], const v8i (&a)[4], const v8i (&b)[F],
+                                         const uint32_t (&sa)[4], const uint32_t (&sb)[F]) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[f], a[g], acc[f][g], kFmtFP8, kFmtFP8,
                                                                   2 * S, (int)sb[f], 2 * S, (int)sa[g]);
 }
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
-    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
-    const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ bias,
-    void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kX8Lds];
+// One output tile: 256 activation rows x 64 F weight rows at (m0, n0).
+template <bool OUT_F32, int F>
+__device__ __forceinline__ void mx8_tile(
+    uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
+  constexpr int kTN = 64 * F, kRowsB = kTN / kX8Waves;     // weight rows: per tile, per wave
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kX8BM * kX8KTB]>(lds_raw);
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, 4, &tm, &tn);
-  const int64_t m0 = (int64_t)tm * kX8BM, n0 = (int64_t)tn * kX8BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1, wm = wave & 1;
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t kbytes = (uint32_t)K, nblk = (uint32_t)(K >> 5), nchunk = (uint32_t)(K >> 4);
   const int nkt = (int)(K / kX8KT);
-  const uint32_t rows_a = rows_in(kX8BM, M, m0), rows_b = rows_in(kX8BN, N, n0);
+  const uint32_t rows_a = rows_in(kX8BM, M, m0), rows_b = rows_in(kTN, N, n0);
   const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
   const auto rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
   const auto rs_a = make_rsrc(as + m0 * nblk, rows_a * nblk);
   const auto rs_b = make_rsrc(bs + n0 * nblk, rows_b * nblk);
 
-  // K-tile kt -> stage: each wave moves 64 activation and 64 weight rows, 8 rows of
-  // 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding global
-  // chunk (i % 8) ^ (row & 7)); rows past the matrix read as zero
+  // K-tile kt -> stage: each wave moves 64 activation and kRowsB weight rows, 8 rows
+  // of 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding
+  // global chunk (i % 8) ^ (row & 7)); rows past the matrix read as zero
   const int lr = lane >> 3, lp = lane & 7;
   auto load_ktile = [&](int kt, int stage) {
     const uint32_t chunk = (uint32_t)kt * 8 + (lp ^ lr);
@@ -80,7 +82,11 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
     for (int j = 0; j < 8; ++j) {
       const uint32_t row = 64 * wave + 8 * j + lr;
       buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff);
-      buf_ld16_lds(rc_b, &lds[1][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff);
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsB / 8; ++j) {
+      const uint32_t row = kRowsB * wave + 8 * j + lr;
+      buf_ld16_lds(rc_b, &lds[1][stage][(kRowsB * wave + 8 * j) * kX8KTB], row * kbytes + koff);
     }
   };
   // the lane's scale dwords of K-tile kt (rows past the matrix, and K-tiles past K,
@@ -90,11 +96,11 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
     for (int g = 0; g < 4; ++g)
       da[g] = buf_ld4(rs_a, (uint32_t)(wm * 128 + 32 * g + r32) * nblk + 4 * kt);
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      db[f] = buf_ld4(rs_b, (uint32_t)(wn * 128 + 32 * f + r32) * nblk + 4 * kt);
+    for (int f = 0; f < F; ++f)
+      db[f] = buf_ld4(rs_b, (uint32_t)(wn * 32 * F + 32 * f + r32) * nblk + 4 * kt);
   };
   // fragment registers, double-buffered across MFMA steps
-  v8i fa[2][4], fb[2][4];
+  v8i fa[2][4], fb[2][F];
   auto frag = [&](int op, int stage, int row, int s) {
     const uint8_t* base = &lds[op][stage][row * kX8KTB];
     const int c = 4 * s + h;
@@ -105,12 +111,12 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) fa[buf][g] = frag(0, stage, wm * 128 + 32 * g + r32, s);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) fb[buf][f] = frag(1, stage, wn * 128 + 32 * f + r32, s);
+    for (int f = 0; f < F; ++f) fb[buf][f] = frag(1, stage, wn * 32 * F + 32 * f + r32, s);
   };
 
-  v16f acc[4][4];
+  v16f acc[F][4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
 
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
   // are read.  The scale loads for kt+2 go out after step 1 (issued earlier, they
   // would keep a third register set live through it).  Loads past K read zeros
   // (codes) and are never used.
-  uint32_t sx_a[4], sx_b[4], sy_a[4], sy_b[4];
+  uint32_t sx_a[4], sx_b[F], sy_a[4], sy_b[F];
   load_ktile(0, 0);
   load_scales(0, sx_a, sx_b);
   load_ktile(1, 1);
@@ -136,25 +142,24 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
     // here keeps the 16 reads below from counting against them (the LDS counter
     // holds at most 15)
     __builtin_amdgcn_s_waitcnt(0xC07F);
-    uint32_t ca[4], cb[4];
+    uint32_t ca[4], cb[F];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ca[i] = sr_a[i] >> (8 * h);
-      cb[i] = sr_b[i] >> (8 * h);
-    }
+    for (int i = 0; i < 4; ++i) ca[i] = sr_a[i] >> (8 * h);
+#pragma unroll
+    for (int i = 0; i < F; ++i) cb[i] = sr_b[i] >> (8 * h);
     read_frags(1, st, 1);
-    mx8_step<0>(acc, fa[0], fb[0], ca, cb);
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    mx8_step<0, F>(acc, fa[0], fb[0], ca, cb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * F, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmem();                                 // K-tile kt+1 and its scales have landed
     __syncthreads();                             // and every read of stage st is done
     load_ktile(kt + 2, st);
     read_frags(0, st ^ 1, 0);
-    mx8_step<1>(acc, fa[1], fb[1], ca, cb);
-    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    mx8_step<1, F>(acc, fa[1], fb[1], ca, cb);
+    __builtin_amdgcn_sched_group_barrier(0x020, 8 + F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * F, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * F, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_scales(kt + 2, sr_a, sr_b);
   };
@@ -167,9 +172,28 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
   wait_vmem();                                   // the loads past K have landed
   __syncthreads();                               // before the epilogue reuses the LDS
 
-  const int64_t n_base = n0 + wn * 128, m_base = m0 + wm * 128;
-  epilogue_store<OUT_F32, 4, 128>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
-                                  lds_raw + wave * EpilogueShape<OUT_F32, 4, 128>::kStageWaveBytes);
+  const int64_t n_base = n0 + wn * 32 * F, m_base = m0 + wm * 128;
+  epilogue_store<OUT_F32, F, 128>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                                  lds_raw + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
+}
+
+// Workgroup b -> a whole tile or, for b < 2 (tiles - full), a half of a leftover
+// tile (weight rows 128 h .. +127), with the XCD-aware order of tile_of.
+template <bool OUT_F32>
+__global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
+    const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
+    const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ bias,
+    void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n, int full) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kX8Lds];
+  int vt, half, tm, tn;
+  const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
+  tile_of(vt, tiles_m, tiles_n, 4, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kX8BM, n0 = (int64_t)tn * kX8BN + (is_half ? 128 * half : 0);
+  if (n0 >= N) return;                                   // a half past the last weight row
+  if (is_half)
+    mx8_tile<OUT_F32, 2>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0);
+  else
+    mx8_tile<OUT_F32, 4>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0);
 }
 
 }  // namespace
@@ -177,13 +201,22 @@ __global__ __launch_bounds__(kX8Threads) void gemm_mx8_kernel(
 hipError_t launch_gemm_mx8(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                            int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kX8BM - 1) / kX8BM), tiles_n = (int)((N + kX8BN - 1) / kX8BN);
-  const unsigned grid = (unsigned)(tiles_m * tiles_n);
+  const int tiles = tiles_m * tiles_n;
+  // leftover tiles of the last round over the CUs (one workgroup per CU) run as halves
+  int cus = 256, dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+  }
+  const int rem = tiles % cus;
+  const int full = (tiles > cus && rem > 0 && 2 * rem <= cus) ? tiles - rem : tiles;
+  const unsigned grid = (unsigned)(full + 2 * (tiles - full));
   if (ep.out_f32)
     hipLaunchKernelGGL((gemm_mx8_kernel<true>), dim3(grid), dim3(kX8Threads), 0, s, ac, as, bc, bs, M, N, K,
-                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
   else
     hipLaunchKernelGGL((gemm_mx8_kernel<false>), dim3(grid), dim3(kX8Threads), 0, s, ac, as, bc, bs, M, N, K,
-                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n);
+                       ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
   return hipGetLastError();
 }
 

@@ -130,6 +130,19 @@ def test_gemm_mxfp8_parity(M, N, K, f32):
     _check(y, y_ref, bound, not f32, f"mxfp8 {M}x{N}x{K}")
 
 
+def test_gemm_mxfp8_half_tiles():
+    # 2 x 130 tiles on 256 CUs: the 4 leftover tiles run as 8 halves (with ragged M
+    # and N); every output checked
+    dev = device()
+    M, N, K = 300, 130 * 256 - 160, 256
+    x = synth.activations(M, K, seed=11, outliers=3)[0]
+    wt = synth.weights(N, K, seed=12)
+    say(f"gemm_w4a4 mxfp8 half tiles {M}x{N}x{K}")
+    y = run_x8(x, wt, dev, f32=True)
+    y_ref, bound = ref_x8(x, wt)
+    _check(y, y_ref, bound, False, "mxfp8 half tiles")
+
+
 def test_full_mxfp8_mlp_up_sampled_rows():
     dev = device()
     d = synth.attn_proj(seed=1, N=12288)
