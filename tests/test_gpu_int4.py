@@ -94,6 +94,19 @@ def test_gemm_int4_sym_parity(M, N, K, f32):
     _check(y, y_ref, bound, not f32, f"int4_sym {M}x{N}x{K}")
 
 
+def test_gemm_int4_sym_half_tiles():
+    # 2 x 130 tiles on 256 CUs: the 4 leftover tiles run as 8 halves (with ragged M
+    # and N); every output checked
+    dev = device()
+    M, N, K = 300, 130 * 256 - 160, 512
+    x = synth.activations(M, K, seed=13, outliers=3)[0]
+    wt = synth.weights(N, K, seed=14)
+    say(f"gemm_w4a4 int4_sym half tiles {M}x{N}x{K}")
+    y = run_i4(x, wt, dev, f32=True)
+    y_ref, bound = ref_i4(x, wt)
+    _check(y, y_ref, bound, False, "int4_sym half tiles")
+
+
 def test_full_int4_sym_mlp_up_sampled_rows():
     dev = device()
     d = synth.attn_proj(seed=1, N=12288)
