@@ -112,3 +112,52 @@ def mx_output(y):
     if not np.array_equal(y, y.astype(np.float32).astype(np.float64)):
         raise ValueError("mx_output takes results that are exact fp32 values")
     return mx_quantize(f32_to_bf16_rne(y.astype(np.float32)))
+
+
+# ----------------------------------------------------------------------------- SwiGLU epilogue
+SWIGLU_BLOCK = 64          # output columns per gate/up block of weight rows
+SILU_SLOPE_MAX = 1.0999    # max over z of |d/dz (z sigmoid(z))| (1.09984 near z = 2.40)
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + e^-z) in fp64 (SiLU, the Swish of SwiGLU's gate)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ref(y, bound, block=SWIGLU_BLOCK):
+    """The SwiGLU epilogue fused into the GEMM (a fusion the NVIDIA Technical Blog
+    summary names for its FLUX kernels, first optimization layer), on the GEMM's
+    fp64 result y [M, N] and its bound (both from ``gemm_ref``, bias included).
+
+    Weight rows come in groups of 2 * block: the first `block` are the gate and the
+    next `block` the up projection of output columns block * j .. + block - 1 of
+    group j.  out = silu(gate) * up, [M, N / 2].
+
+    Returns (out, out_bound): out_bound is in the units of ``gemm_ref``'s bound, so
+    that ``check_close`` applies: with |gate error| <= 1e-3 bound_g and |up error|
+    <= 1e-3 bound_u,
+        |d out| <= 1e-3 (SILU_SLOPE_MAX bound_g (|up| + 1e-3 bound_u) + |silu(gate)| bound_u)
+    plus the fp32 evaluation of silu(gate) * up (an exp whose argument carries a
+    relative error of 2^-23, a division and a product): |out| (|gate| 2^-23 + 2^-20).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    bound = np.asarray(bound, dtype=np.float64)
+    M, N = y.shape
+    if N % (2 * block):
+        raise ValueError("N must be a multiple of 2 * block")
+    groups = N // (2 * block)
+
+    def split(a):
+        a = a.reshape(M, groups, 2, block)
+        return a[:, :, 0, :].reshape(M, N // 2), a[:, :, 1, :].reshape(M, N // 2)
+
+    gate, up = split(y)
+    bg, bu = split(bound)
+    sg = silu(gate)
+    out = sg * up
+    eval_err = np.abs(out) * (np.abs(gate) * 2.0 ** -23 + 2.0 ** -20)
+    out_bound = (SILU_SLOPE_MAX * bg * (np.abs(up) + GEMM_REL_TOL * bu) + np.abs(sg) * bu
+                 + eval_err / GEMM_REL_TOL)
+    return out, out_bound

@@ -136,15 +136,18 @@ def test_gemm_mx_all_ones_closed_form():
         assert np.all(y == K * 16 * 2.0 ** (a + b))
 
 
-def test_gemm_k_zero_gives_bias():
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "int4_sym"])
+def test_gemm_k_zero_gives_bias(fmt):
     dev = device()
     M, N = 40, 72
     bias = synth.bias(N, seed=5)
-    dummy = torch.zeros(64, dtype=torch.uint8, device=dev)
+    # no codes or block scales are read at K = 0; int4_sym reads its float row scales
+    # [M] and [N] (zeros here)
+    dummy = torch.zeros(4 * max(M, N), dtype=torch.uint8, device=dev)
     y = out_buffer(M, N, dev, f32=True)
     b = bf16_dev(bias[None, :], dev)[0]
-    say("gemm_w4a4 K=0")
-    B.gemm_w4a4("mxfp4", dummy, dummy, None, dummy, dummy, None, M, N, 0, y, bias=b, out=B.OUT_F32)
+    say(f"gemm_w4a4 {fmt} K=0")
+    B.gemm_w4a4(fmt, dummy, dummy, None, dummy, dummy, None, M, N, 0, y, bias=b, out=B.OUT_F32)
     torch.cuda.synchronize()
     yh, ok = y_host(y, N)
     assert ok and np.array_equal(yh, np.broadcast_to(F.bf16_to_f64(bias), (M, N)))
