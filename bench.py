@@ -91,7 +91,7 @@ def cpu_baseline(d, budget_s=12.0):
                       f"(+ low-rank, + error bound) against all {N} columns; {dt:.1f} s"}
 
 
-GEMM_KERNEL_PREFIX = "void q4::gemm_mx_kernel<32, false, false>"
+GEMM_KERNEL_PREFIX = "void q4::gemm_mx_kernel<32, false, 0>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 CAL_BYTES = 256 * 2 ** 20          # the calibration copy below: 64 Mi fp32 in, 64 Mi fp32 out
 
@@ -321,6 +321,24 @@ def bench_rows(reps=50):
     emit(f"gemm_w4a4_lowrank + quantize_act {Mq}x{Kq}x{Np} r={RANK}", ms_u, flops=2.0 * Mq * Np * Kq,
          peak=MXFP4_PEAK_TFLOPS, note=f"unfused: bf16 Y stored and read back; fused saves "
                                       f"{(ms_u - ms_f) * 1e3:.1f} us")
+
+    # ---- f1: the SwiGLU epilogue on the same operands read as 6144 gate/up pairs
+    # (weight rows grouped 32 gate + 32 up), against the GEMM's bf16 store followed by
+    # torch's silu and product
+    ysw = torch.empty((Mq, Np // 2), dtype=torch.bfloat16, device=dev)
+    ms_s = timed(lambda i: B.gemm_w4a4_lowrank_swiglu(acm, asm_, bcm, bsm, Mq, Np, Kq, ysw, t=tq2, l2t=l2m,
+                                                      stream=stream), 1)
+    emit(f"gemm_w4a4_lowrank_swiglu mxfp4 {Mq}x{Kq}x{Np} r={RANK}", ms_s, flops=2.0 * Mq * Np * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note="SwiGLU epilogue: bf16 [M, N/2] out")
+
+    def unfused_swiglu(i):
+        B.gemm_w4a4_lowrank("mxfp4", acm, asm_, None, bcm, bsm, None, Mq, Np, Kq, tq2, l2m, ym, stream=stream)
+        gu = ym.view(Mq, Np // 64, 2, 32)
+        torch.mul(torch.nn.functional.silu(gu[:, :, 0, :]), gu[:, :, 1, :], out=ysw.view(Mq, Np // 64, 32))
+    ms_su = timed(unfused_swiglu, 1)
+    emit(f"gemm_w4a4_lowrank + torch silu*up {Mq}x{Kq}x{Np} r={RANK}", ms_su, flops=2.0 * Mq * Np * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note=f"unfused comparison; the fused epilogue saves {(ms_su - ms_s) * 1e3:.1f} us")
+    del ysw
     del dm, ym
 
     # ---- f3: symmetric INT4 W4A4 on the INT8 MFMA (no 4-bit integer matrix
@@ -595,7 +613,7 @@ def main():
                    "rank": RANK, "format": "mxfp4", "output": "bf16",
                    "step": "quantize_act(+X L1) -> gemm_w4a4_lowrank", "input_sets": N_SETS},
         "pct_of_mxfp4_peak": round(100.0 * value / MXFP4_PEAK_TFLOPS, 2),
-        "roofline": {"kernel": "gemm_mx_kernel<32,false,false>", "bound": "mfma",
+        "roofline": {"kernel": "gemm_mx_kernel<32,false,0>", "bound": "mfma",
                      "achieved": round(gemm_tflops, 2), "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(), "avg_launch_ms": round(gemm_ms, 5),

@@ -35,6 +35,8 @@ SIGNATURES = {
                                      _I32, _P, _P, _I64, _c.c_int, _P]),
     "gemm_w4a4_lowrank_mxout": (_c.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P,
                                            _I64, _P, _I64, _P, _I64, _P]),
+    "gemm_w4a4_lowrank_swiglu": (_c.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P,
+                                            _I64, _P]),
     "gemm_w4a16": (_c.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _I64, _c.c_int,
                               _P]),
     "q4_status_string": (_c.c_char_p, [_c.c_int]),
@@ -154,6 +156,17 @@ def gemm_w4a4_lowrank_mxout(a_codes, a_scales, b_codes, b_scales, M, N, K, y_cod
                                         y_codes.stride(0), _ptr(y_scales), y_scales.stride(0),
                                         _stream(stream))
     _check("gemm_w4a4_lowrank_mxout", st)
+
+
+def gemm_w4a4_lowrank_swiglu(a_codes, a_scales, b_codes, b_scales, M, N, K, y, t=None, l2t=None,
+                             bias=None, stream=None):
+    """MXFP4 GEMM (+ t L2) over N weight rows grouped as 32 gate + 32 up rows per 32
+    output columns; y bf16 [M, N/2] receives silu(gate) * up."""
+    r = 0 if l2t is None else l2t.shape[1]
+    st = load().gemm_w4a4_lowrank_swiglu(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M,
+                                         N, K, _ptr(t), _ptr(l2t), r, _ptr(bias), _ptr(y), y.stride(0),
+                                         _stream(stream))
+    _check("gemm_w4a4_lowrank_swiglu", st)
 
 
 def gemm_w4a16(x, w_codes, w_scales, w_zeros, N, y, bias=None, group=64, out=OUT_BF16, stream=None):

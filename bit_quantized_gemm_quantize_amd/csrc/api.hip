@@ -154,6 +154,26 @@ q4_status gemm_w4a4_lowrank(q4_format fmt, const uint8_t* a_codes, const uint8_t
   return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
 }
 
+q4_status gemm_w4a4_lowrank_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                   int64_t N, int64_t K, const float* t, const uint16_t* l2t,
+                                   int32_t r, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                                   void* stream) {
+  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || (N % 64) != 0 || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || K > kMaxK || ldy < N / 2) return Q4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return Q4_ERR_NULL;
+  if (r > 0 && (!t || !l2t)) return Q4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(y, 16) || (ldy % 8) != 0)
+    return Q4_ERR_ALIGN;
+  if (r > 0 && (!aligned(t, 16) || !aligned(l2t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0 || N == 0) return Q4_OK;
+  q4::EpilogueArgs ep{r > 0 ? t : nullptr, r > 0 ? l2t : nullptr, (int)r, bias, y, ldy, 0};
+  ep.swiglu = 1;
+  return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 q4_status gemm_w4a4_lowrank_mxout(const uint8_t* a_codes, const uint8_t* a_scales,
                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                   int64_t N, int64_t K, const float* t, const uint16_t* l2t,

@@ -200,7 +200,11 @@ struct MxLoads {
   }
 };
 
-// MXFP4 output of the tile for the next layer (QOUT): codes [M, N/2] and scale bytes
+// What the epilogue writes: Y (bf16 or fp32), Y as MXFP4 codes and scales for the
+// next layer, or the SwiGLU of Y's gate and up columns.
+constexpr int kOutY = 0, kOutMx = 1, kOutSwiglu = 2;
+
+// MXFP4 output of the tile for the next layer (kOutMx): codes [M, N/2] and scale bytes
 // [M, N/32] with row strides in bytes.
 struct MxQOut {
   uint8_t* qc;
@@ -272,6 +276,41 @@ __device__ __forceinline__ u32x4 mx_stage1_read(const uint8_t* stage, int i, int
   return ld16(stage + row * 128 + (((c ^ (row >> 1)) & 7) << 4));
 }
 
+// SwiGLU of a tile's accumulators (kOutSwiglu).  Weight rows come in groups of 64:
+// the first 32 are the gate and the last 32 the up projection of output columns
+// 32 j .. 32 j + 31 of group j.  A wave's weight sub-tiles (32 rows each, F of them)
+// are F/2 whole groups, so acc[2p] (gate) and acc[2p + 1] (up) hold the same
+// outputs.  With each weight row's bias added first, y = gate / (1 + exp(-gate)) * up
+// in fp32, stored as bf16 [M, N/2] through the standard staging.
+template <int F>
+__device__ __forceinline__ void epilogue_store_swiglu(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
+                                                      int64_t M, int64_t N, const uint16_t* __restrict__ bias,
+                                                      uint16_t* y, int64_t ldy, int lane, uint8_t* stage) {
+  constexpr int P = F / 2;
+  const int h = lane >> 5;
+  v16f v[P][4];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t n = n_base + 64 * p + 8 * vq + 4 * h + jj;    // gate row; up row n + 32
+        float bg = 0.0f, bu = 0.0f;
+        if (bias != nullptr && n + 32 < N) {
+          bg = __uint_as_float((uint32_t)bias[n] << 16);
+          bu = __uint_as_float((uint32_t)bias[n + 32] << 16);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float gate = acc[2 * p][g][4 * vq + jj] + bg;
+          const float up = acc[2 * p + 1][g][4 * vq + jj] + bu;
+          v[p][g][4 * vq + jj] = gate / (1.0f + __expf(-gate)) * up;
+        }
+      }
+  epilogue_store<false, P, 128>(v, n_base / 2, m_base, M, N / 2, nullptr, y, ldy, lane, stage);
+}
+
 // One output tile of 256 activation rows x kTN weight rows starting at (m0, n0),
 // whose prologue loads (MxLoads::prologue) are already issued: wave (wm, wn) owns m
 // in [128 wm, +128) and n in [32 F wn, +32 F).  `pending` is the number of this
@@ -282,7 +321,7 @@ __device__ __forceinline__ u32x4 mx_stage1_read(const uint8_t* stage, int i, int
 // the loads past K, so only the low-rank operands remain for the next prologue.
 // Once the tile's LDS is free again, issue_next(chained) queues what remains of the
 // next tile's prologue; the return value is the number of stores queued after it.
-template <int R, bool OUT_F32, bool QOUT, int F, class Next>
+template <int R, bool OUT_F32, int OUTM, int F, class Next>
 __device__ __forceinline__ int mx_tile(
     uint8_t* lds_raw, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K,
@@ -309,7 +348,7 @@ __device__ __forceinline__ int mx_tile(
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
-  const bool chain = !QOUT && F == kFFull && next_kind == 1 && (nkt & 3) == 0 && nkt >= 4;
+  const bool chain = OUTM == kOutY && F == kFFull && next_kind == 1 && (nkt & 3) == 0 && nkt >= 4;
   const L nx(lds_raw, ac, as, bc, bs, M, N, K, chain ? nm0 : m0, chain ? nn0 : n0);
   const int pairs = nkt >> 1;
   auto gload_part = [&](auto part_c, int kt, int stage) {
@@ -547,9 +586,15 @@ __device__ __forceinline__ int mx_tile(
   wait_vmem();                               // the loads past K have landed
   __syncthreads();                           // all waves are done with the operand LDS
   uint8_t* stage = lds_raw + wave * mx_stage_wave_bytes<OUT_F32, F>();
-  if constexpr (QOUT) {
+  if constexpr (OUTM == kOutMx) {
     epilogue_store_mxfp4<F>(acc, n_base, m_base, M, N, bias, static_cast<uint16_t*>(y), ldy, qo.qc,
                             qo.ldc, qo.qs, qo.lds, lane, stage);
+    lds_barrier();
+    issue_next(false);
+    return 0;
+  }
+  if constexpr (OUTM == kOutSwiglu) {
+    epilogue_store_swiglu<F>(acc, n_base, m_base, M, N, bias, static_cast<uint16_t*>(y), ldy, lane, stage);
     lds_barrier();
     issue_next(false);
     return 0;
@@ -585,7 +630,7 @@ __device__ __forceinline__ bool mx_unit(int u, int tiles_m, int tiles_n, int ful
 // still runs on XCD u % 8 when G is a multiple of 8.  Each tile queues the next
 // one's first loads as soon as its output is staged, ahead of its own stores, so
 // the stores drain while the next tile starts.
-template <int R, bool OUT_F32, bool QOUT>
+template <int R, bool OUT_F32, int OUTM>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bc,
     const uint8_t* __restrict__ bs, int64_t M, int64_t N, int64_t K, const float* __restrict__ t,
@@ -620,10 +665,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
       else prologue(nh, nm, nn);
     };
     if (half)
-      pending = mx_tile<R, OUT_F32, QOUT, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0,
+      pending = mx_tile<R, OUT_F32, OUTM, kFHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0,
                                                  n0, pending, next_kind, nm, nn, qo, issue_next);
     else
-      pending = mx_tile<R, OUT_F32, QOUT, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0,
+      pending = mx_tile<R, OUT_F32, OUTM, kFFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0,
                                                  n0, pending, next_kind, nm, nn, qo, issue_next);
     u = nu;
     half = nh;
@@ -632,7 +677,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(
   }
 }
 
-template <int R, bool F32, bool QOUT = false>
+template <int R, bool F32, int OUTM = kOutY>
 static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                   int64_t M, int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
@@ -648,7 +693,7 @@ static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const
   const int units = full + 2 * (tiles - full);
   // one workgroup per CU (the LDS allows no more), each looping over its units
   const int grid = units < cus ? units : cus;
-  hipLaunchKernelGGL((gemm_mx_kernel<R, F32, QOUT>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M,
+  hipLaunchKernelGGL((gemm_mx_kernel<R, F32, OUTM>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M,
                      N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full, units,
                      MxQOut{ep.qc, ep.ldc, ep.qs, ep.lds});
 }
@@ -656,10 +701,14 @@ static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K,
                           const EpilogueArgs& ep, hipStream_t s) {
-  if (ep.qc != nullptr) {
-    if (ep.r == 0) queue<0, false, true>(ac, as, bc, bs, M, N, K, ep, s);
-    else if (ep.r == 16) queue<16, false, true>(ac, as, bc, bs, M, N, K, ep, s);
-    else queue<32, false, true>(ac, as, bc, bs, M, N, K, ep, s);
+  if (ep.swiglu) {
+    if (ep.r == 0) queue<0, false, kOutSwiglu>(ac, as, bc, bs, M, N, K, ep, s);
+    else if (ep.r == 16) queue<16, false, kOutSwiglu>(ac, as, bc, bs, M, N, K, ep, s);
+    else queue<32, false, kOutSwiglu>(ac, as, bc, bs, M, N, K, ep, s);
+  } else if (ep.qc != nullptr) {
+    if (ep.r == 0) queue<0, false, kOutMx>(ac, as, bc, bs, M, N, K, ep, s);
+    else if (ep.r == 16) queue<16, false, kOutMx>(ac, as, bc, bs, M, N, K, ep, s);
+    else queue<32, false, kOutMx>(ac, as, bc, bs, M, N, K, ep, s);
   } else if (ep.out_f32) {
     if (ep.r == 0) queue<0, true>(ac, as, bc, bs, M, N, K, ep, s);
     else if (ep.r == 16) queue<16, true>(ac, as, bc, bs, M, N, K, ep, s);

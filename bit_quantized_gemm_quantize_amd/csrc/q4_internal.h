@@ -32,6 +32,9 @@ struct EpilogueArgs {
   int64_t ldc = 0;
   uint8_t* qs = nullptr;
   int64_t lds = 0;
+  // SwiGLU epilogue (MXFP4 GEMM only): y is bf16 [M, N/2], silu(gate) * up of the
+  // weight rows' gate/up groups of 2 x 32
+  int swiglu = 0;
 };
 
 hipError_t launch_int4_sym_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,

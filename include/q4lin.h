@@ -248,6 +248,31 @@ Q4_API q4_status gemm_w4a4_lowrank_mxout(const uint8_t* a_codes, const uint8_t* 
                                   void* stream);
 
 /*
+ * gemm_w4a4_lowrank_swiglu -- the MXFP4 gemm_w4a4_lowrank with a SwiGLU epilogue: the
+ * GEMM computes the gate and up projections of an MLP together and stores only
+ * silu(gate) * up, so the 2x wider intermediate never reaches HBM.  ("NVIDIA
+ * Technical Blog Details FLUX 3 Image Klein ...", first optimization layer: GEMMs
+ * with SwiGLU epilogues.  silu(z) = z / (1 + e^-z), applied to the gate, the plain
+ * reading of SwiGLU, which the page names without defining.)
+ *
+ *   a_*, b_*, M, K, t, l2t, r, bias   as gemm_w4a4_lowrank, MXFP4 operands; r may be
+ *             0.  The weight rows (and bias entries, and L2^T rows) come in groups
+ *             of 64: rows 64 j .. 64 j + 31 are the gate and rows
+ *             64 j + 32 .. 64 j + 63 the up projection of output columns
+ *             32 j .. 32 j + 31.
+ *   N         the number of weight rows: a multiple of 64; the output has N/2
+ *             columns.
+ *   y   (out) bf16 [M, N/2], row stride ldy >= N/2 (a multiple of 8), 16-byte
+ *             aligned: silu(gate + b_gate) * (up + b_up), evaluated in fp32 from the
+ *             fp32 accumulators and rounded to nearest even.
+ */
+Q4_API q4_status gemm_w4a4_lowrank_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                   int64_t N, int64_t K, const float* t, const uint16_t* l2t,
+                                   int32_t r, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                                   void* stream);
+
+/*
  * gemm_w4a16 -- the weight-only comparison path: Y = X w_hat^T (+ bias) with
  * w_hat = bf16((q - z) s) dequantized tile by tile in LDS and a bf16 MFMA GEMM
  * (SVDQuant Guide, "Why Standard Low-Bit Quantization Fails on DiTs", third point,

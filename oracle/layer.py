@@ -115,7 +115,7 @@ def mx_output(y):
 
 
 # ----------------------------------------------------------------------------- SwiGLU epilogue
-SWIGLU_BLOCK = 64          # output columns per gate/up block of weight rows
+SWIGLU_BLOCK = 32          # output columns per gate/up group of weight rows
 SILU_SLOPE_MAX = 1.0999    # max over z of |d/dz (z sigmoid(z))| (1.09984 near z = 2.40)
 
 

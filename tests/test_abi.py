@@ -110,6 +110,29 @@ def test_gemm_mxout_rejections():
     assert gq(M=0) == B.Q4_OK
 
 
+def gs(**kw):
+    a = dict(ac=OK16, asc=OK16, bc=OK16, bsc=OK16, M=256, N=256, K=256, t=None, l2t=None, r=0,
+             bias=None, y=OK16, ldy=128)
+    a.update(kw)
+    return lib().gemm_w4a4_lowrank_swiglu(a["ac"], a["asc"], a["bc"], a["bsc"], a["M"], a["N"], a["K"],
+                                          a["t"], a["l2t"], a["r"], a["bias"], a["y"], a["ldy"], None)
+
+
+def test_gemm_swiglu_rejections():
+    assert gs(N=160) == B.Q4_ERR_SHAPE                   # N not a multiple of 64
+    assert gs(K=192) == B.Q4_ERR_SHAPE
+    assert gs(ldy=120) == B.Q4_ERR_SHAPE                 # ldy < N/2
+    assert gs(r=8, t=OK16, l2t=OK16) == B.Q4_ERR_SHAPE
+    assert gs(M=-1) == B.Q4_ERR_SHAPE
+    assert gs(y=None) == B.Q4_ERR_NULL
+    assert gs(bc=None) == B.Q4_ERR_NULL
+    assert gs(r=32, t=None, l2t=OK16) == B.Q4_ERR_NULL
+    assert gs(y=ODD) == B.Q4_ERR_ALIGN
+    assert gs(ldy=132) == B.Q4_ERR_ALIGN
+    assert gs(r=16, t=OK16, l2t=ODD) == B.Q4_ERR_ALIGN
+    assert gs(M=0) == B.Q4_OK and gs(N=0) == B.Q4_OK
+
+
 def qs(**kw):
     a = dict(fmt=0, x=OK16, M=64, K=256, ldx=256, inv=OK16, codes=OK16, scales=OK16, l1t=None, r=0,
              t=None)
