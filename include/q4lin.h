@@ -19,9 +19,10 @@
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - 4-bit codes are packed two per byte along K: element 2j in the low nibble,
  *     element 2j+1 in the high nibble; a row of K elements is K/2 bytes.  FP4 codes
- *     are E2M1 (sign in bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *     are E2M1 (sign in bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  The 8-bit
+ *     format (Q4_MXFP8) takes one E4M3FN byte per element.
  *   - Matrices are row-major.  Packed codes and scales are dense (row stride
- *     K/2 bytes, K/32 or K/16 bytes, K/64 elements).
+ *     K/2 or K bytes, K/32 or K/16 bytes, K/64 elements).
  *   - `stream` is a hipStream_t (NULL: the default stream).  Work is queued on it
  *     and the call returns without synchronizing.
  *   - Arguments are checked on the host before anything is queued; a failed check
