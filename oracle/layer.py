@@ -161,3 +161,52 @@ def swiglu_ref(y, bound, block=SWIGLU_BLOCK):
     out_bound = (SILU_SLOPE_MAX * bg * (np.abs(up) + GEMM_REL_TOL * bu) + np.abs(sg) * bu
                  + eval_err / GEMM_REL_TOL)
     return out, out_bound
+
+
+# ----------------------------------------------------------------------------- QKV split + RoPE
+def qkv_rope_ref(y, bound, cs, head_dim):
+    """The QKV-split and RoPE epilogue fused into the GEMM (the NVIDIA Technical Blog
+    summary names QKV-projection and RoPE epilogues for its FLUX kernels, first
+    optimization layer), on the GEMM's fp64 result y [M, 3 D] and its bound (both from
+    ``gemm_ref``, bias included).
+
+    Columns [0, D) are Q, [D, 2 D) K and [2 D, 3 D) V.  In Q and K, each head's
+    adjacent column pair (2 i, 2 i + 1) (i < head_dim / 2, counted inside the head) is
+    rotated by the angle whose cosine and sine are cs[m, i] = (c, s) for row m:
+        (a, b) -> (a c - b s, a s + b c);
+    V is passed through.  cs: fp32 [M, head_dim / 2, 2], used exactly.
+
+    Returns ((q, k, v), (bq, bk, bv)): the outputs [M, D] each and their bounds in the
+    units of ``gemm_ref``'s bound: a rotated element's error is at most
+    |c| e_a + |s| e_b (or |s| e_a + |c| e_b) for input errors e_a, e_b, plus the fp32
+    evaluation (two products and a sum: 2^-22 (|a c| + |b s|)).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    bound = np.asarray(bound, dtype=np.float64)
+    M, N = y.shape
+    if N % 3 or (N // 3) % head_dim or head_dim % 2:
+        raise ValueError("N = 3 D with D a multiple of an even head_dim")
+    D = N // 3
+    cs = np.asarray(cs, dtype=np.float64)
+    if cs.shape != (M, head_dim // 2, 2):
+        raise ValueError("cs must be [M, head_dim / 2, 2]")
+    heads = D // head_dim
+    c = np.tile(cs[:, :, 0], (1, heads))          # [M, D / 2]: pair p of the section
+    s = np.tile(cs[:, :, 1], (1, heads))
+
+    def rotate(part, bpart):
+        a, b = part[:, 0::2], part[:, 1::2]
+        ea, eb = bpart[:, 0::2], bpart[:, 1::2]
+        out = np.empty_like(part)
+        ob = np.empty_like(part)
+        out[:, 0::2] = a * c - b * s
+        out[:, 1::2] = a * s + b * c
+        ev = (np.abs(a * c) + np.abs(b * s)) * 2.0 ** -22 / GEMM_REL_TOL
+        ev2 = (np.abs(a * s) + np.abs(b * c)) * 2.0 ** -22 / GEMM_REL_TOL
+        ob[:, 0::2] = np.abs(c) * ea + np.abs(s) * eb + ev
+        ob[:, 1::2] = np.abs(s) * ea + np.abs(c) * eb + ev2
+        return out, ob
+
+    q, bq = rotate(y[:, :D], bound[:, :D])
+    k, bk = rotate(y[:, D:2 * D], bound[:, D:2 * D])
+    return (q, k, y[:, 2 * D:].copy()), (bq, bk, bound[:, 2 * D:].copy())
