@@ -339,6 +339,40 @@ def bench_rows(reps=50):
     emit(f"gemm_w4a4_lowrank + torch silu*up {Mq}x{Kq}x{Np} r={RANK}", ms_su, flops=2.0 * Mq * Np * Kq,
          peak=MXFP4_PEAK_TFLOPS, note=f"unfused comparison; the fused epilogue saves {(ms_su - ms_s) * 1e3:.1f} us")
     del ysw
+
+    # ---- f1: the QKV-split + RoPE epilogue on a fused QKV projection (3072 -> 3 x
+    # 3072, head width 128), against the GEMM's bf16 store followed by torch's split
+    # and rotation
+    dq = synth.mlp_up_svd(seed=1, N=9216)
+    bcq, bsq, _ = B.empty_quant("mxfp4", 9216, Kq, dev)
+    B.pack_weights("mxfp4", bf16_dev(dq["rt"]), Kq, 9216, 1, Kq, bcq, bsq, stream=stream)
+    l2q = bf16_dev(np.ascontiguousarray(dq["l2"].T))
+    hd = 128
+    pos = torch.arange(Mq, device=dev, dtype=torch.float32)[:, None]
+    ang = pos * (10000.0 ** (-torch.arange(hd // 2, device=dev, dtype=torch.float32) * 2.0 / hd))[None, :]
+    csq = torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).contiguous()
+    yqkv = [torch.empty((Mq, 3072), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    ms_q = timed(lambda i: B.gemm_w4a4_lowrank_qkv_rope(acm, asm_, bcq, bsq, Mq, 9216, Kq, *yqkv, t=tq2,
+                                                        l2t=l2q, cs=csq, head_dim=hd, stream=stream), 1)
+    emit(f"gemm_w4a4_lowrank_qkv_rope mxfp4 {Mq}x{Kq}x9216 r={RANK}", ms_q, flops=2.0 * Mq * 9216 * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note="Q, K, V outputs, RoPE on Q and K (head width 128)")
+    yfull = torch.empty((Mq, 9216), dtype=torch.bfloat16, device=dev)
+    cq, sq = csq[..., 0].repeat(1, 3072 // hd), csq[..., 1].repeat(1, 3072 // hd)
+
+    def unfused_qkv(i):
+        B.gemm_w4a4_lowrank("mxfp4", acm, asm_, None, bcq, bsq, None, Mq, 9216, Kq, tq2, l2q, yfull,
+                            stream=stream)
+        for sec in range(2):
+            part = yfull[:, 3072 * sec:3072 * (sec + 1)].float()
+            a, b = part[:, 0::2], part[:, 1::2]
+            out = yqkv[sec].view(Mq, 3072 // 2, 2)
+            out[:, :, 0] = (a * cq - b * sq).to(torch.bfloat16)
+            out[:, :, 1] = (a * sq + b * cq).to(torch.bfloat16)
+        yqkv[2].copy_(yfull[:, 6144:])
+    ms_qu = timed(unfused_qkv, 1)
+    emit(f"gemm_w4a4_lowrank + torch split/rope {Mq}x{Kq}x9216 r={RANK}", ms_qu, flops=2.0 * Mq * 9216 * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note=f"unfused comparison; the fused epilogue saves {(ms_qu - ms_q) * 1e3:.1f} us")
+    del dq, yqkv, yfull
     del dm, ym
 
     # ---- f3: symmetric INT4 W4A4 on the INT8 MFMA (no 4-bit integer matrix

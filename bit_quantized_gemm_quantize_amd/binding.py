@@ -37,6 +37,8 @@ SIGNATURES = {
                                            _I64, _P, _I64, _P, _I64, _P]),
     "gemm_w4a4_lowrank_swiglu": (_c.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P,
                                             _I64, _P]),
+    "gemm_w4a4_lowrank_qkv_rope": (_c.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P,
+                                              _I32, _P, _P, _P, _I64, _P]),
     "gemm_w4a16": (_c.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _I64, _c.c_int,
                               _P]),
     "q4_status_string": (_c.c_char_p, [_c.c_int]),
@@ -167,6 +169,19 @@ def gemm_w4a4_lowrank_swiglu(a_codes, a_scales, b_codes, b_scales, M, N, K, y, t
                                          N, K, _ptr(t), _ptr(l2t), r, _ptr(bias), _ptr(y), y.stride(0),
                                          _stream(stream))
     _check("gemm_w4a4_lowrank_swiglu", st)
+
+
+def gemm_w4a4_lowrank_qkv_rope(a_codes, a_scales, b_codes, b_scales, M, N, K, yq, yk, yv, t=None,
+                               l2t=None, bias=None, cs=None, head_dim=0, stream=None):
+    """MXFP4 GEMM (+ t L2) of a fused QKV projection (N = 3 D weight rows): Q, K, V
+    stored to yq, yk, yv (bf16 [M, D], one row stride), Q and K rotated by cs
+    (float [M, head_dim/2, 2] of cos, sin) when given."""
+    r = 0 if l2t is None else l2t.shape[1]
+    assert yk.stride(0) == yq.stride(0) == yv.stride(0), "yq, yk, yv share one row stride"
+    st = load().gemm_w4a4_lowrank_qkv_rope(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M,
+                                           N, K, _ptr(t), _ptr(l2t), r, _ptr(bias), _ptr(cs), head_dim,
+                                           _ptr(yq), _ptr(yk), _ptr(yv), yq.stride(0), _stream(stream))
+    _check("gemm_w4a4_lowrank_qkv_rope", st)
 
 
 def gemm_w4a16(x, w_codes, w_scales, w_zeros, N, y, bias=None, group=64, out=OUT_BF16, stream=None):

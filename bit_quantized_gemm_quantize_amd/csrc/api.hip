@@ -174,6 +174,35 @@ q4_status gemm_w4a4_lowrank_swiglu(const uint8_t* a_codes, const uint8_t* a_scal
                                      static_cast<hipStream_t>(stream)));
 }
 
+q4_status gemm_w4a4_lowrank_qkv_rope(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                     int64_t N, int64_t K, const float* t, const uint16_t* l2t,
+                                     int32_t r, const uint16_t* bias, const float* cs,
+                                     int32_t head_dim, uint16_t* yq, uint16_t* yk, uint16_t* yv,
+                                     int64_t ldy, void* stream) {
+  const int64_t D = N / 3;
+  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || (N % 384) != 0 || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || K > kMaxK || ldy < D) return Q4_ERR_SHAPE;
+  if (cs && (head_dim < 2 || (head_dim % 2) != 0 || (D % head_dim) != 0)) return Q4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !yq || !yk || !yv) return Q4_ERR_NULL;
+  if (r > 0 && (!t || !l2t)) return Q4_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(yq, 16) || !aligned(yk, 16) || !aligned(yv, 16) ||
+      (ldy % 8) != 0)
+    return Q4_ERR_ALIGN;
+  if (cs && !aligned(cs, 8)) return Q4_ERR_ALIGN;
+  if (r > 0 && (!aligned(t, 16) || !aligned(l2t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0 || N == 0) return Q4_OK;
+  q4::EpilogueArgs ep{r > 0 ? t : nullptr, r > 0 ? l2t : nullptr, (int)r, bias, yq, ldy, 0};
+  ep.qkv = 1;
+  ep.yk = yk;
+  ep.yv = yv;
+  ep.cs = cs;
+  ep.head_dim = cs ? (int)head_dim : 0;
+  return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 q4_status gemm_w4a4_lowrank_mxout(const uint8_t* a_codes, const uint8_t* a_scales,
                                   const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                                   int64_t N, int64_t K, const float* t, const uint16_t* l2t,

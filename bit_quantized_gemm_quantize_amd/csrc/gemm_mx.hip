@@ -201,16 +201,22 @@ struct MxLoads {
 };
 
 // What the epilogue writes: Y (bf16 or fp32), Y as MXFP4 codes and scales for the
-// next layer, or the SwiGLU of Y's gate and up columns.
-constexpr int kOutY = 0, kOutMx = 1, kOutSwiglu = 2;
+// next layer, the SwiGLU of Y's gate and up columns, or Y split into Q, K and V with
+// RoPE on Q and K.
+constexpr int kOutY = 0, kOutMx = 1, kOutSwiglu = 2, kOutQkv = 3;
 
-// MXFP4 output of the tile for the next layer (kOutMx): codes [M, N/2] and scale bytes
-// [M, N/32] with row strides in bytes.
+// Outputs beyond Y.  kOutMx: codes [M, N/2] and scale bytes [M, N/32] with row
+// strides in bytes.  kOutQkv: K and V outputs (Q goes to y), the RoPE table
+// (float [M, head_dim/2, 2] of (cos, sin), or null) and the head width.
 struct MxQOut {
   uint8_t* qc;
   int64_t ldc;
   uint8_t* qs;
   int64_t lds;
+  uint16_t* yk;
+  uint16_t* yv;
+  const float* cs;
+  int head_dim;
 };
 
 // Output staging for a tile whose successor's first K-tile already fills stage 0:
@@ -309,6 +315,58 @@ __device__ __forceinline__ void epilogue_store_swiglu(v16f (&acc)[F][4], int64_t
         }
       }
   epilogue_store<false, P, 128>(v, n_base / 2, m_base, M, N / 2, nullptr, y, ldy, lane, stage);
+}
+
+// QKV split and RoPE of a tile (kOutQkv).  N = 3 D with D a multiple of 128, so a
+// wave's columns lie in one section: Q [0, D), K [D, 2 D) or V.  The bias is added
+// first; in Q and K each head's adjacent column pair (2 i, 2 i + 1) is rotated by row
+// m's (cos, sin) of pair i, (a, b) -> (a c - b s, a s + b c), in fp32.  Accumulator
+// registers j and j + 1 (j even) of a lane are such a pair.  Each section is stored
+// bf16 [M, D] to its own output through the standard staging.
+template <int F>
+__device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
+                                                   int64_t M, int64_t N, const uint16_t* __restrict__ bias,
+                                                   uint16_t* yq, int64_t ldy, int lane, uint8_t* stage,
+                                                   const MxQOut& qo) {
+  if (n_base >= N) return;                               // wave-uniform: past the last column
+  const int64_t D = N / 3;
+  const int sec = (int)(n_base / D);
+  const int64_t col0 = n_base - sec * D;
+  const int r32 = lane & 31, h = lane >> 5;
+  if (bias != nullptr) {
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float b = __uint_as_float((uint32_t)bias[n_base + 32 * f + acc_row(j, lane)] << 16);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[f][g][j] += b;
+      }
+  }
+  if (sec < 2 && qo.cs != nullptr) {
+    const int hd = qo.head_dim, half = hd >> 1;
+    const float2* cs = reinterpret_cast<const float2*>(qo.cs);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      int64_t m = m_base + 32 * g + r32;
+      m = m < M ? m : M - 1;                             // rows past M are never stored
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int64_t col = col0 + 32 * f + 8 * vq + 4 * h + 2 * pr;   // even
+            const float2 t = cs[m * half + (col % hd) / 2];
+            const int j = 4 * vq + 2 * pr;
+            const float a = acc[f][g][j], b = acc[f][g][j + 1];
+            acc[f][g][j] = a * t.x - b * t.y;
+            acc[f][g][j + 1] = a * t.y + b * t.x;
+          }
+    }
+  }
+  uint16_t* dst = sec == 0 ? yq : (sec == 1 ? qo.yk : qo.yv);
+  epilogue_store<false, F, mx_stage_row_max<false>()>(acc, col0, m_base, M, D, nullptr, dst, ldy, lane, stage);
 }
 
 // One output tile of 256 activation rows x kTN weight rows starting at (m0, n0),
@@ -599,6 +657,12 @@ __device__ __forceinline__ int mx_tile(
     issue_next(false);
     return 0;
   }
+  if constexpr (OUTM == kOutQkv) {
+    epilogue_store_qkv<F>(acc, n_base, m_base, M, N, bias, static_cast<uint16_t*>(y), ldy, lane, stage, qo);
+    lds_barrier();
+    issue_next(false);
+    return 0;
+  }
   // A wave region inside the output, bf16: staged into registers, so that the LDS is
   // free for the next tile's loads before the stores go out.  Otherwise (edges, fp32)
   // staged and stored pass by pass.
@@ -695,13 +759,17 @@ static void queue(const uint8_t* ac, const uint8_t* as, const uint8_t* bc, const
   const int grid = units < cus ? units : cus;
   hipLaunchKernelGGL((gemm_mx_kernel<R, F32, OUTM>), dim3(grid), dim3(kThreads), 0, s, ac, as, bc, bs, M,
                      N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full, units,
-                     MxQOut{ep.qc, ep.ldc, ep.qs, ep.lds});
+                     MxQOut{ep.qc, ep.ldc, ep.qs, ep.lds, ep.yk, ep.yv, ep.cs, ep.head_dim});
 }
 
 hipError_t launch_gemm_mx(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K,
                           const EpilogueArgs& ep, hipStream_t s) {
-  if (ep.swiglu) {
+  if (ep.qkv) {
+    if (ep.r == 0) queue<0, false, kOutQkv>(ac, as, bc, bs, M, N, K, ep, s);
+    else if (ep.r == 16) queue<16, false, kOutQkv>(ac, as, bc, bs, M, N, K, ep, s);
+    else queue<32, false, kOutQkv>(ac, as, bc, bs, M, N, K, ep, s);
+  } else if (ep.swiglu) {
     if (ep.r == 0) queue<0, false, kOutSwiglu>(ac, as, bc, bs, M, N, K, ep, s);
     else if (ep.r == 16) queue<16, false, kOutSwiglu>(ac, as, bc, bs, M, N, K, ep, s);
     else queue<32, false, kOutSwiglu>(ac, as, bc, bs, M, N, K, ep, s);

@@ -35,6 +35,13 @@ struct EpilogueArgs {
   // SwiGLU epilogue (MXFP4 GEMM only): y is bf16 [M, N/2], silu(gate) * up of the
   // weight rows' gate/up groups of 2 x 32
   int swiglu = 0;
+  // QKV split + RoPE (MXFP4 GEMM only): y receives Q, yk K and yv V (bf16 [M, N/3]
+  // each, row stride ldy); cs: float [M, head_dim/2, 2] (cos, sin) or nullptr
+  int qkv = 0;
+  uint16_t* yk = nullptr;
+  uint16_t* yv = nullptr;
+  const float* cs = nullptr;
+  int head_dim = 0;
 };
 
 hipError_t launch_int4_sym_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,

@@ -274,6 +274,32 @@ Q4_API q4_status gemm_w4a4_lowrank_swiglu(const uint8_t* a_codes, const uint8_t*
                                    void* stream);
 
 /*
+ * gemm_w4a4_lowrank_qkv_rope -- the MXFP4 gemm_w4a4_lowrank of a fused QKV projection
+ * whose epilogue splits Y into Q, K and V and applies the rotary position embedding
+ * to Q and K, so the projection's output is written once, in place for attention.
+ * ("NVIDIA Technical Blog Details FLUX 3 Image Klein ...", first optimization layer:
+ * GEMMs with QKV-projection and RoPE epilogues.  The rotation of adjacent pairs by a
+ * per-token angle table is the plain reading; the page defines neither.)
+ *
+ *   a_*, b_*, M, K, t, l2t, r, bias   as gemm_w4a4_lowrank, MXFP4 operands; r may be
+ *             0.  Weight rows [0, D) are Q, [D, 2 D) K and [2 D, 3 D) V.
+ *   N         3 D with D a multiple of 128.
+ *   cs        float [M, head_dim/2, 2]: (cos, sin) of the angle of pair i for row m,
+ *             8-byte aligned; or NULL for the split alone.  In Q and K, columns
+ *             (2 i, 2 i + 1) of every head (counted inside the head) become
+ *             (a c - b s, a s + b c), after the bias, in fp32.
+ *   head_dim  even, dividing D (ignored when cs is NULL).
+ *   yq, yk, yv (out)  bf16 [M, D] each, row stride ldy >= D (a multiple of 8),
+ *             16-byte aligned.
+ */
+Q4_API q4_status gemm_w4a4_lowrank_qkv_rope(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                                     int64_t N, int64_t K, const float* t, const uint16_t* l2t,
+                                     int32_t r, const uint16_t* bias, const float* cs,
+                                     int32_t head_dim, uint16_t* yq, uint16_t* yk, uint16_t* yv,
+                                     int64_t ldy, void* stream);
+
+/*
  * gemm_w4a16 -- the weight-only comparison path: Y = X w_hat^T (+ bias) with
  * w_hat = bf16((q - z) s) dequantized tile by tile in LDS and a bf16 MFMA GEMM
  * (SVDQuant Guide, "Why Standard Low-Bit Quantization Fails on DiTs", third point,

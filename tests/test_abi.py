@@ -133,6 +133,30 @@ def test_gemm_swiglu_rejections():
     assert gs(M=0) == B.Q4_OK and gs(N=0) == B.Q4_OK
 
 
+def gr(**kw):
+    a = dict(ac=OK16, asc=OK16, bc=OK16, bsc=OK16, M=256, N=768, K=256, t=None, l2t=None, r=0,
+             bias=None, cs=OK16, hd=64, yq=OK16, yk=OK16, yv=OK16, ldy=256)
+    a.update(kw)
+    return lib().gemm_w4a4_lowrank_qkv_rope(a["ac"], a["asc"], a["bc"], a["bsc"], a["M"], a["N"], a["K"],
+                                            a["t"], a["l2t"], a["r"], a["bias"], a["cs"], a["hd"], a["yq"],
+                                            a["yk"], a["yv"], a["ldy"], None)
+
+
+def test_gemm_qkv_rope_rejections():
+    assert gr(N=384 + 192) == B.Q4_ERR_SHAPE             # D not a multiple of 128
+    assert gr(ldy=128) == B.Q4_ERR_SHAPE                 # ldy < D
+    assert gr(hd=3) == B.Q4_ERR_SHAPE                    # odd head width
+    assert gr(hd=96) == B.Q4_ERR_SHAPE                   # does not divide D = 256
+    assert gr(cs=None, hd=3, M=0) == B.Q4_OK             # head_dim ignored without a table
+    assert gr(yk=None) == B.Q4_ERR_NULL
+    assert gr(yv=None) == B.Q4_ERR_NULL
+    assert gr(r=16, t=None, l2t=OK16) == B.Q4_ERR_NULL
+    assert gr(cs=P((1 << 20) + 4)) == B.Q4_ERR_ALIGN     # table 8-byte aligned
+    assert gr(yv=ODD) == B.Q4_ERR_ALIGN
+    assert gr(ldy=260) == B.Q4_ERR_ALIGN
+    assert gr(M=0) == B.Q4_OK and gr(N=0) == B.Q4_OK
+
+
 def qs(**kw):
     a = dict(fmt=0, x=OK16, M=64, K=256, ldx=256, inv=OK16, codes=OK16, scales=OK16, l1t=None, r=0,
              t=None)
