@@ -318,11 +318,13 @@ __device__ __forceinline__ void epilogue_store_swiglu(v16f (&acc)[F][4], int64_t
 }
 
 // QKV split and RoPE of a tile (kOutQkv).  N = 3 D with D a multiple of 128, so a
-// wave's columns lie in one section: Q [0, D), K [D, 2 D) or V.  The bias is added
-// first; in Q and K each head's adjacent column pair (2 i, 2 i + 1) is rotated by row
-// m's (cos, sin) of pair i, (a, b) -> (a c - b s, a s + b c), in fp32.  Accumulator
-// registers j and j + 1 (j even) of a lane are such a pair.  Each section is stored
-// bf16 [M, D] to its own output through the standard staging.
+// wave's columns lie in one section: Q [0, D), K [D, 2 D) or V.  Each section goes to
+// its own output [M, D] (bf16).  V, or everything without a table, takes the
+// standard bf16 staging.  Q and K are staged in fp32 with the bias added (32 columns
+// per pass), and each lane's 32-byte read-back (four adjacent column pairs of a row)
+// is rotated by that row's (cos, sin) of the pairs' indices inside the head,
+// (a, b) -> (a c - b s, a s + b c), in fp32 before the one rounding to bf16, and
+// stored as 16 bytes.
 template <int F>
 __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
                                                    int64_t M, int64_t N, const uint16_t* __restrict__ bias,
@@ -332,41 +334,50 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
   const int64_t D = N / 3;
   const int sec = (int)(n_base / D);
   const int64_t col0 = n_base - sec * D;
-  const int r32 = lane & 31, h = lane >> 5;
-  if (bias != nullptr) {
-#pragma unroll
-    for (int f = 0; f < F; ++f)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float b = __uint_as_float((uint32_t)bias[n_base + 32 * f + acc_row(j, lane)] << 16);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) acc[f][g][j] += b;
-      }
+  const uint16_t* bsec = bias != nullptr ? bias + sec * D : nullptr;
+  uint16_t* dst = sec == 0 ? yq : (sec == 1 ? qo.yk : qo.yv);
+  if (sec == 2 || qo.cs == nullptr) {
+    epilogue_store<false, F, mx_stage_row_max<false>()>(acc, col0, m_base, M, D, bsec, dst, ldy, lane, stage);
+    return;
   }
-  if (sec < 2 && qo.cs != nullptr) {
-    const int hd = qo.head_dim, half = hd >> 1;
-    const float2* cs = reinterpret_cast<const float2*>(qo.cs);
+  using S = EpilogueShape<true, F, 128>;
+  static_assert(S::kFPerPass == 1, "one 32-column sub-tile per fp32 pass");
+  const int hd = qo.head_dim, half = hd >> 1;
+  const float2* cs = reinterpret_cast<const float2*>(qo.cs);
+  const int cl = lane & 3;                               // 32-byte chunk: columns 8 cl .. 8 cl + 7
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      int64_t m = m_base + 32 * g + r32;
-      m = m < M ? m : M - 1;                             // rows past M are never stored
+  for (int pass = 0; pass < S::kPasses; ++pass) {
+    if (pass > 0) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): previous pass read back
+      __builtin_amdgcn_wave_barrier();
+    }
+    epilogue_stage_pass<true, F, 128, false, true>(acc, pass, col0, D, bsec, lane, stage, 1.0f);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
+    int ip[4];
 #pragma unroll
-      for (int f = 0; f < F; ++f)
+    for (int q = 0; q < 4; ++q) ip[q] = (int)(((col + 2 * q) % hd) >> 1);
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int ml = 16 * it + (lane >> 2);
+      const int64_t m = m_base + ml;
+      if (m < M) {
+        const uint8_t* src = stage + ml * S::kStageRowBytes + cl * 32;
+        const v4f va = *reinterpret_cast<const v4f*>(src), vb = *reinterpret_cast<const v4f*>(src + 16);
+        const float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        uint32_t w[4];
 #pragma unroll
-        for (int vq = 0; vq < 4; ++vq)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const int64_t col = col0 + 32 * f + 8 * vq + 4 * h + 2 * pr;   // even
-            const float2 t = cs[m * half + (col % hd) / 2];
-            const int j = 4 * vq + 2 * pr;
-            const float a = acc[f][g][j], b = acc[f][g][j + 1];
-            acc[f][g][j] = a * t.x - b * t.y;
-            acc[f][g][j + 1] = a * t.y + b * t.x;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const float2 t = cs[m * half + ip[q]];
+          const v2bf p = {(__bf16)(v[2 * q] * t.x - v[2 * q + 1] * t.y),
+                          (__bf16)(v[2 * q] * t.y + v[2 * q + 1] * t.x)};
+          w[q] = __builtin_bit_cast(uint32_t, p);
+        }
+        st16_stream(dst + m * ldy + col, u32x4{w[0], w[1], w[2], w[3]});
+      }
     }
   }
-  uint16_t* dst = sec == 0 ? yq : (sec == 1 ? qo.yk : qo.yv);
-  epilogue_store<false, F, mx_stage_row_max<false>()>(acc, col0, m_base, M, D, nullptr, dst, ldy, lane, stage);
 }
 
 // One output tile of 256 activation rows x kTN weight rows starting at (m0, n0),
