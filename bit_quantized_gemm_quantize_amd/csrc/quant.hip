@@ -126,19 +126,21 @@ __device__ __forceinline__ int mx_encode_smoothed(const uint32_t* w, const float
   return E;
 }
 
-// ---------------------------------------------------------------------------- MX per block
+// ---------------------------------------------------------------------------- per block
 // One thread per (row, 32-element block) of a strided bf16 matrix, consecutive
 // threads on consecutive blocks of a row (contiguous loads and stores).
 //   MXFP8: E = floor(log2 amax) - 8 (emax of E4M3FN) clamped to [-127, 127], codes
 //   E4M3_RNE(x * 2**-E) saturated at +-448 (the product is exact in fp32; the clamp
-//   comes before the converter, which rounds to nearest even), 32 code bytes.
-//   MXFP4 (the activation pass without the low-rank term): E = floor(log2 amax) - 2,
-//   codes by the E2M1 converter, 16 code bytes.
-// One scale byte E + 127 per block.
-template <bool FP8>
+//   comes before the converter, which rounds to nearest even), 32 code bytes, one
+//   scale byte E + 127.
+//   MXFP4 and NVFP4 (the activation pass without the low-rank term): the encodes of
+//   the row-per-lane pass (one MX block and its scale byte, or two NVFP4 blocks of 16
+//   and their two E4M3 scale bytes), 16 code bytes.
+constexpr int kBlkMXFP4 = 0, kBlkNVFP4 = 1, kBlkMXFP8 = 2;
+template <int KIND>
 __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t K, int64_t sr, int64_t sk,
                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                         int64_t nblk, int64_t q) {
+                                         int64_t nblk, int64_t q, float s_t, float d6) {
   const int64_t r = q / nblk, b = q % nblk;
   const uint16_t* src = x + r * sr + b * 32 * sk;
   uint32_t w[16];
@@ -152,8 +154,15 @@ __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t
 #pragma unroll
     for (int j = 0; j < 16; ++j) w[j] = (uint32_t)src[2 * j * sk] | ((uint32_t)src[(2 * j + 1) * sk] << 16);
   }
+  if (KIND == kBlkNVFP4) {
+    u32x4 c;
+    const uint32_t sc = nv_encode32(w, s_t, d6, &c);
+    st16(codes + r * (K >> 1) + b * 16, c);
+    *reinterpret_cast<uint16_t*>(scales + r * (2 * nblk) + 2 * b) = (uint16_t)sc;
+    return;
+  }
   const uint32_t amax = bf16_amax_bits<16>(w);
-  if (!FP8) {
+  if (KIND == kBlkMXFP4) {
     const int E = mx_block_exponent(amax);
     const float sc = exp2i(E);
     st16(codes + r * (K >> 1) + b * 16, u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
@@ -184,32 +193,40 @@ __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t
   scales[r * nblk + b] = (uint8_t)(E + 127);
 }
 
-template <bool FP8>
+// amax_t: NVFP4's tensor amax (the tensor scale is derived from it), else unused.
+template <int KIND>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                       int64_t K, int64_t sr, int64_t sk,
                                                       uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales) {
+                                                      uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ amax_t) {
+  float s_t = 1.0f, d6 = 6.0f;
+  if (KIND == kBlkNVFP4) {
+    s_t = nv_tensor_scale(*amax_t);
+    d6 = 6.0f * s_t;
+  }
   const int64_t nblk = K >> 5, work = rows * nblk;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += (int64_t)gridDim.x * blockDim.x)
-    mx_block<FP8>(x, K, sr, sk, codes, scales, nblk, q);
+    mx_block<KIND>(x, K, sr, sk, codes, scales, nblk, q, s_t, d6);
 }
 
 // Launch of mx_rows_kernel: one thread per block, the grid capped (the threads
 // then stride over the blocks).
-template <bool FP8>
+template <int KIND>
 static hipError_t queue_mx_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
-                                uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                                uint8_t* codes, uint8_t* scales, hipStream_t s,
+                                const float* amax_t = nullptr) {
   const int64_t work = rows * (K >> 5);
   if (work == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, int64_t(1) << 20);
-  hipLaunchKernelGGL(mx_rows_kernel<FP8>, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, sr, sk, codes,
-                     scales);
+  hipLaunchKernelGGL(mx_rows_kernel<KIND>, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, sr, sk, codes,
+                     scales, amax_t);
   return hipGetLastError();
 }
 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
                              uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  return queue_mx_rows<true>(x, rows, K, sr, sk, codes, scales, s);
+  return queue_mx_rows<kBlkMXFP8>(x, rows, K, sr, sk, codes, scales, s);
 }
 
 // ---------------------------------------------------------------------------- activation pass
@@ -412,14 +429,16 @@ hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K,
     // without the low-rank term, one thread per block: the row-per-lane layout only
     // serves the MFMA of t = X L1
     if (r == 0) {
-      const hipError_t e = queue_mx_rows<false>(x, M, K, ldx, 1, codes, scales, s);
+      const hipError_t e = queue_mx_rows<kBlkMXFP4>(x, M, K, ldx, 1, codes, scales, s);
       if (e != hipSuccess) return e;
     }
     else if (r == 16) queue_quant<0, 16>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
     else queue_quant<0, 32>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
   } else {
-    if (r == 0) queue_quant<1, 0>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
-    else if (r == 16) queue_quant<1, 16>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
+    if (r == 0) {
+      const hipError_t e = queue_mx_rows<kBlkNVFP4>(x, M, K, ldx, 1, codes, scales, s, tensor_scale);
+      if (e != hipSuccess) return e;
+    } else if (r == 16) queue_quant<1, 16>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
     else queue_quant<1, 32>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
