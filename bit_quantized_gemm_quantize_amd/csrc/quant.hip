@@ -1,8 +1,9 @@
 // Activation quantizer (MXFP4 / NVFP4) fused with the low-rank down-projection,
 // and the offline weight packers.
 //
-// Activation pass (one read of X).  Without the low-rank term, MXFP4 takes one
-// thread per block instead (mx_rows_kernel, shared with MXFP8).  With it:
+// Activation pass (one read of X).  Without the low-rank term, MXFP4 and NVFP4 take
+// one thread per 32-element block instead (mx_rows_kernel, shared with MXFP8).  With
+// it:
 //   * a workgroup owns up to 32 rows (as many as spread M evenly over the CUs) and
 //     all of K; its 16 waves stride over K in pairs of 32-element blocks, so a lane
 //     (row l%32, half l/32) owns one whole block per step: 64 contiguous bytes of X
