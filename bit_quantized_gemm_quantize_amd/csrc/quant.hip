@@ -354,16 +354,22 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   const int64_t total = rows * cols;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (sc == 1 && (cols & 31) == 0 && (sr & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-    // 64 bytes per thread per step, four 16-byte loads in flight
-    const int64_t per_row = cols >> 5;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < rows * per_row; q += stride) {
-      const int64_t r = q / per_row, c = q % per_row;
-      const uint16_t* src = x + r * sr + c * 32;
-      u32x4 v[4];
+    // 64 bytes per thread per step, two steps (eight 16-byte loads) in flight
+    const int64_t per_row = cols >> 5, nq = rows * per_row;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += 2 * stride) {
+      u32x4 v[2][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = ld16(src + 8 * j);
+      for (int u = 0; u < 2; ++u) {
+        const int64_t qu = q + u * stride;
+        const int64_t r = qu / per_row, c = qu % per_row;
+        const uint16_t* src = x + r * sr + c * 32;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v[j])));
+        for (int j = 0; j < 4; ++j) v[u][j] = qu < nq ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v[u][j])));
     }
   } else {
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
