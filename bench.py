@@ -387,7 +387,7 @@ def bench_rows(reps=50):
          note="int4 widened to int8 for the INT8 MFMA; peak = dense INT8 5.0 POP/s")
     ms = timed(lambda i: B.quantize_act("int4_sym", x0, xi, xis, stream=stream), 1)
     emit(f"quantize_act int4_sym {Mq}x{Kq}", ms, bytes_=2 * Mq * Kq + Mq * Kq // 2 + 4 * Mq,
-         note="two passes over each row (amax, then codes; the second from the cache)")
+         note="one wave per row, the row read once into registers (amax, then codes)")
     del yi, xi, wi
 
     # ---- f4: MXFP8 W8A8 on the same block-scaled MFMA with E4M3 operands

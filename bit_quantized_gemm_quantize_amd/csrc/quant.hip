@@ -458,7 +458,8 @@ hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K,
 // Signed int4, symmetric, one fp32 scale per row: scale = max(amax / 7, 1e-8) and
 // q = clamp(rint(x / scale), -8, 7), every step in fp32 (IEEE division, round half
 // to even).  One wave per row of a strided bf16 matrix (element (r, k) at
-// x[r * sr + k * sk]); two passes over the row (the second from the cache).  Codes
+// x[r * sr + k * sk]); a contiguous row of up to 4096 elements is read once into
+// registers, others in two passes (the second from the cache).  Codes
 // are two's-complement nibbles, the even k in the low nibble.
 __global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t K, int64_t sr, int64_t sk,
@@ -480,20 +481,15 @@ __global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __re
         w[j] = (uint32_t)row[(8 * c + 2 * j) * sk] | ((uint32_t)row[(8 * c + 2 * j + 1) * sk] << 16);
     }
   };
-  uint32_t m = 0;
-  for (int64_t c = lane; c < chunks; c += 64) {
-    uint32_t w[4];
-    load8(c, w);
-    m = max(m, bf16_amax_bits<4>(w));
-  }
+  auto wave_scale = [&](uint32_t m) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  const float scale = fmaxf(__uint_as_float(m << 16) / 7.0f, 1e-8f);
-  if (lane == 0) scales[r] = scale;
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    const float scale = fmaxf(__uint_as_float(m << 16) / 7.0f, 1e-8f);
+    if (lane == 0) scales[r] = scale;
+    return scale;
+  };
   uint8_t* out = codes + r * (K >> 1);
-  for (int64_t c = lane; c < chunks; c += 64) {
-    uint32_t w[4];
-    load8(c, w);
+  auto encode8 = [&](int64_t c, const uint32_t* w, float scale) {
     uint32_t packed = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -502,6 +498,37 @@ __global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __re
       packed |= ((uint32_t)(int)q & 0xFu) << (4 * j);
     }
     *reinterpret_cast<uint32_t*>(out + 4 * c) = packed;
+  };
+  constexpr int kRegChunks = 8;              // rows up to 64 * 8 chunks stay in registers
+  if (contig && chunks <= 64 * kRegChunks) {
+    // one read of the row: every chunk's load in flight at once
+    uint32_t w[kRegChunks][4];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kRegChunks; ++i) {
+      const int64_t c = lane + 64 * i;
+      if (c < chunks) load8(c, w[i]);
+      else w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kRegChunks; ++i) m = max(m, bf16_amax_bits<4>(w[i]));
+    const float scale = wave_scale(m);
+#pragma unroll
+    for (int i = 0; i < kRegChunks; ++i)
+      if (lane + 64 * i < chunks) encode8(lane + 64 * i, w[i], scale);
+    return;
+  }
+  uint32_t m = 0;
+  for (int64_t c = lane; c < chunks; c += 64) {
+    uint32_t w[4];
+    load8(c, w);
+    m = max(m, bf16_amax_bits<4>(w));
+  }
+  const float scale = wave_scale(m);
+  for (int64_t c = lane; c < chunks; c += 64) {
+    uint32_t w[4];
+    load8(c, w);
+    encode8(c, w, scale);
   }
 }
 
