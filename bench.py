@@ -193,7 +193,7 @@ def bench_rows(reps=50):
     peak, and W4A16 next to a plain bf16 GEMM (torch, hipBLASLt) of the same shape."""
     import torch
     from bit_quantized_gemm_quantize_amd import binding as B
-    from bit_quantized_gemm_quantize_amd import synth
+    from bit_quantized_gemm_quantize_amd import synth, weight_prep
 
     if not os.path.exists(B.LIB_PATH):
         import __graft_entry__
@@ -299,7 +299,7 @@ def bench_rows(reps=50):
 
     # ---- f1: the MXFP4-emitting epilogue at the MLP up-projection with the rank-32
     # branch, against the unfused pair (bf16 store, then quantize_act reading it back)
-    dm = synth.mlp_up_svd(seed=0)
+    dm = weight_prep.mlp_up_svd(seed=0)
     tq2 = torch.empty((Mq, RANK), dtype=torch.float32, device=dev)
     l1m = bf16_dev(np.ascontiguousarray(dm["l1"].T))
     l2m = bf16_dev(np.ascontiguousarray(dm["l2"].T))
@@ -343,7 +343,7 @@ def bench_rows(reps=50):
     # ---- f1: the QKV-split + RoPE epilogue on a fused QKV projection (3072 -> 3 x
     # 3072, head width 128), against the GEMM's bf16 store followed by torch's split
     # and rotation
-    dq = synth.mlp_up_svd(seed=1, N=9216)
+    dq = weight_prep.mlp_up_svd(seed=1, N=9216)
     bcq, bsq, _ = B.empty_quant("mxfp4", 9216, Kq, dev)
     B.pack_weights("mxfp4", bf16_dev(dq["rt"]), Kq, 9216, 1, Kq, bcq, bsq, stream=stream)
     l2q = bf16_dev(np.ascontiguousarray(dq["l2"].T))
@@ -451,7 +451,7 @@ def bench_rows(reps=50):
     # the unquantized bf16 product for plain W4A4, the unsmoothed SVD split and SVDQuant
     # (GPU outputs on 64 sampled rows, reference in fp64 on the host)
     del x0, xw, wt, wbf, y
-    d = synth.attn_proj_svdquant(seed=0)
+    d = weight_prep.attn_proj_svdquant(seed=0)
     Ms, Ks, Ns, rs = d["M"], d["K"], d["N"], d["rank"]
     xsv = bf16_dev(d["x"])
     xsl = [xsv] + [xsv.clone() for _ in range(9)]
@@ -488,13 +488,16 @@ def bench_rows(reps=50):
         yh = yq.cpu().numpy()[rows_q].astype(np.float64)
         return float(np.linalg.norm(yh - exact) / np.linalg.norm(exact))
 
-    l1p, l2p, rtp = synth.lowrank_split(d["wt"], rs, 0)
+    l1p, l2p, rtp = weight_prep.lowrank_split(d["wt"], rs, 0)
+    gd = weight_prep.guide_step1_split(d["x_cal"], d["wt"], rs)
     errs = {"w4a4": layer_err(d["wt"]), "svd_split": layer_err(rtp, l1p, l2p),
+            "guide_step1_literal": layer_err(gd["rt"], gd["l1"], gd["l2"]),
             "svdquant": layer_err(d["rt"], d["l1"], d["l2"], smooth=True)}
     print(json.dumps({"row": f"svdquant quality attn_proj {Ms}x{Ks}x{Ns} r={rs}",
                       "rel_error_vs_bf16_product": {k: round(v, 5) for k, v in errs.items()},
-                      "note": "64 sampled rows; plain W4A4, the unsmoothed rank-32 SVD split, and "
-                              "smoothing + activation-weighted rank-32 split"}), flush=True)
+                      "note": "64 sampled rows; plain W4A4, the unsmoothed rank-32 SVD split, the "
+                              "Guide's Step-1 recipe as printed (SVD of dW C, residual W - L1 L2), "
+                              "and smoothing + activation-weighted rank-32 split"}), flush=True)
 
 
 def summarize_rows_profile(stats_csv, command):
@@ -561,7 +564,7 @@ def main():
 
     import torch
     from bit_quantized_gemm_quantize_amd import binding as B
-    from bit_quantized_gemm_quantize_amd import synth
+    from bit_quantized_gemm_quantize_amd import synth, weight_prep
 
     if not os.path.exists(B.LIB_PATH):
         import __graft_entry__
@@ -574,7 +577,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     # ---- inputs: one weight split, eight activation sets, all resident in HBM
-    d = synth.mlp_up_svd(seed=0)
+    d = weight_prep.mlp_up_svd(seed=0)
     sets = []
     for i in range(N_SETS):
         x_bits = d["x"] if i == 0 else synth.activations(M, K, seed=i, dist="student_t3")[0]

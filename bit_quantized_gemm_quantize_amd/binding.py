@@ -13,7 +13,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libq4lin.so")
+# the in-tree build; Q4LIN_LIBRARY names another build of the same library
+LIB_PATH = os.environ.get("Q4LIN_LIBRARY") or os.path.join(_PKG, "libq4lin.so")
 
 Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_FORMAT, Q4_ERR_LAUNCH = range(6)
 MXFP4, NVFP4, INT4_G64, INT4_SYM, MXFP8 = 0, 1, 2, 3, 4
@@ -99,6 +100,75 @@ def _fmt(fmt):
     return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
 
 
+# ----------------------------------------------------------------------------- host checks
+# The C ABI takes bare pointers and cannot see a buffer's size, type or device, so
+# every wrapper checks its tensors here first: a short or mistyped buffer would
+# otherwise be read or written past its end by the kernels.
+
+def _device(t, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.device
+
+
+def _span_ok(t, nbytes):
+    avail = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    return nbytes <= avail
+
+
+def _packed(t, name, dtype, rows, cols, dev):
+    """A buffer the library reads or writes as a dense [rows, cols] array."""
+    if _device(t, name) != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < rows * cols:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {rows} x {cols}")
+
+
+def _strided(t, name, dtypes, rows, cols, dev):
+    """A [rows, cols] matrix with contiguous rows and the row stride t.stride(0)."""
+    if _device(t, name) != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1 or t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} must be a 2-D tensor of at least {rows} x {cols} with contiguous rows")
+    if rows and cols and not _span_ok(t, ((rows - 1) * t.stride(0) + cols) * t.element_size()):
+        raise ValueError(f"{name} is too small for {rows} x {cols}")
+
+
+def _scales_spec(fmt, K):
+    """(dtype, columns) of a format's scale buffer per row, and the code bytes per row."""
+    if fmt == MXFP4:
+        return torch.uint8, K // 32, K // 2
+    if fmt == NVFP4:
+        return torch.uint8, K // 16, K // 2
+    if fmt == INT4_SYM:
+        return torch.float32, 1, K // 2
+    if fmt == MXFP8:
+        return torch.uint8, K // 32, K
+    if fmt == INT4_G64:
+        return torch.bfloat16, K // 64, K // 2
+    raise ValueError(f"unknown format {fmt}")
+
+
+def _operand(fmt, codes, scales, tscale, rows, K, dev, name):
+    sdt, scols, cbytes = _scales_spec(fmt, K)
+    _packed(codes, f"{name}_codes", torch.uint8, rows, cbytes, dev)
+    _packed(scales, f"{name}_scales", sdt, rows, scols, dev)
+    if fmt == NVFP4:
+        _packed(tscale, f"{name}_tscale", torch.float32, 1, 1, dev)
+
+
+def _out_dtype(out):
+    return torch.float32 if int(out) == OUT_F32 else torch.bfloat16
+
+
 # ----------------------------------------------------------------------------- entry points
 def quantize_act(fmt, x, codes, scales, tensor_scale=None, l1t=None, t=None, stream=None):
     """x bf16 [M, K] -> codes uint8 [M, K/2], scales uint8 [M, K/32|K/16],
@@ -106,6 +176,13 @@ def quantize_act(fmt, x, codes, scales, tensor_scale=None, l1t=None, t=None, str
     _rowmajor(x, "x")
     M, K = x.shape
     r = 0 if l1t is None else l1t.shape[0]
+    f = _fmt(fmt)
+    dev = _device(x, "x")
+    _strided(x, "x", (torch.bfloat16,), M, K, dev)
+    _operand(f, codes, scales, tensor_scale, M, K, dev, "x")
+    if r:
+        _packed(l1t, "l1t", torch.bfloat16, r, K, dev)
+        _packed(t, "t", torch.float32, M, r, dev)
     st = load().quantize_act(_fmt(fmt), _ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(scales),
                              _ptr(tensor_scale), _ptr(l1t), r, _ptr(t), _stream(stream))
     _check("quantize_act", st)
@@ -116,6 +193,13 @@ def quantize_act_smooth(fmt, x, inv_s, codes, scales, l1t=None, t=None, stream=N
     _rowmajor(x, "x")
     M, K = x.shape
     r = 0 if l1t is None else l1t.shape[0]
+    dev = _device(x, "x")
+    _strided(x, "x", (torch.bfloat16,), M, K, dev)
+    _operand(_fmt(fmt), codes, scales, None, M, K, dev, "x")
+    _packed(inv_s, "inv_s", torch.float32, 1, K, dev)
+    if r:
+        _packed(l1t, "l1t", torch.bfloat16, r, K, dev)
+        _packed(t, "t", torch.float32, M, r, dev)
     st = load().quantize_act_smooth(_fmt(fmt), _ptr(x), M, K, x.stride(0), _ptr(inv_s), _ptr(codes),
                                     _ptr(scales), _ptr(l1t), r, _ptr(t), _stream(stream))
     _check("quantize_act_smooth", st)
@@ -124,13 +208,35 @@ def quantize_act_smooth(fmt, x, inv_s, codes, scales, l1t=None, t=None, stream=N
 def pack_weights(fmt, w, K, N, stride_k, stride_n, codes, scales, zeros=None, tensor_scale=None,
                  stream=None):
     """w bf16, logical [K, N] with element strides (stride_k, stride_n)."""
+    f = _fmt(fmt)
+    dev = _device(w, "w")
+    if w.dtype != torch.bfloat16:
+        raise ValueError("w must be bfloat16")
+    if K > 0 and N > 0 and not _span_ok(w, ((K - 1) * stride_k + (N - 1) * stride_n + 1) * 2):
+        raise ValueError(f"w is too small for [{K}, {N}] with strides ({stride_k}, {stride_n})")
+    _operand(f, codes, scales, tensor_scale, N, K, dev, "w")
+    if f == INT4_G64:
+        _packed(zeros, "zeros", torch.bfloat16, N, K // 64, dev)
     st = load().pack_weights(_fmt(fmt), _ptr(w), K, N, stride_k, stride_n, _ptr(codes),
                              _ptr(scales), _ptr(zeros), _ptr(tensor_scale), _stream(stream))
     _check("pack_weights", st)
 
 
+def _gemm_checks(f, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, y, bias, ydt,
+                 ycols=None):
+    dev = _device(y, "y")
+    _operand(f, a_codes, a_scales, a_tscale, M, K, dev, "a")
+    _operand(f, b_codes, b_scales, b_tscale, N, K, dev, "b")
+    _strided(y, "y", ydt, M, N if ycols is None else ycols, dev)
+    if bias is not None:
+        _packed(bias, "bias", torch.bfloat16, 1, N, dev)
+    return dev
+
+
 def gemm_w4a4(fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, y,
               bias=None, out=OUT_BF16, stream=None):
+    _gemm_checks(_fmt(fmt), a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, y, bias,
+                 (_out_dtype(out),))
     st = load().gemm_w4a4(_fmt(fmt), _ptr(a_codes), _ptr(a_scales), _ptr(a_tscale), _ptr(b_codes),
                           _ptr(b_scales), _ptr(b_tscale), M, N, K, _ptr(bias), _ptr(y), y.stride(0),
                           int(out), _stream(stream))
@@ -140,6 +246,11 @@ def gemm_w4a4(fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, 
 def gemm_w4a4_lowrank(fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, t,
                       l2t, y, bias=None, out=OUT_BF16, stream=None):
     r = 0 if l2t is None else l2t.shape[1]
+    dev = _gemm_checks(_fmt(fmt), a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, y,
+                       bias, (_out_dtype(out),))
+    if r:
+        _packed(t, "t", torch.float32, M, r, dev)
+        _packed(l2t, "l2t", torch.bfloat16, N, r, dev)
     st = load().gemm_w4a4_lowrank(_fmt(fmt), _ptr(a_codes), _ptr(a_scales), _ptr(a_tscale),
                                   _ptr(b_codes), _ptr(b_scales), _ptr(b_tscale), M, N, K, _ptr(t),
                                   _ptr(l2t), r, _ptr(bias), _ptr(y), y.stride(0), int(out),
@@ -152,6 +263,18 @@ def gemm_w4a4_lowrank_mxout(a_codes, a_scales, b_codes, b_scales, M, N, K, y_cod
     """MXFP4 GEMM (+ t L2) whose output is written as MXFP4 codes [M, N/2] and scales
     [M, N/32] (and as bf16 into y when given)."""
     r = 0 if l2t is None else l2t.shape[1]
+    dev = _device(y_codes, "y_codes")
+    _operand(MXFP4, a_codes, a_scales, None, M, K, dev, "a")
+    _operand(MXFP4, b_codes, b_scales, None, N, K, dev, "b")
+    _strided(y_codes, "y_codes", (torch.uint8,), M, N // 2, dev)
+    _strided(y_scales, "y_scales", (torch.uint8,), M, N // 32, dev)
+    if y is not None:
+        _strided(y, "y", (torch.bfloat16,), M, N, dev)
+    if bias is not None:
+        _packed(bias, "bias", torch.bfloat16, 1, N, dev)
+    if r:
+        _packed(t, "t", torch.float32, M, r, dev)
+        _packed(l2t, "l2t", torch.bfloat16, N, r, dev)
     st = load().gemm_w4a4_lowrank_mxout(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M,
                                         N, K, _ptr(t), _ptr(l2t), r, _ptr(bias), _ptr(y),
                                         0 if y is None else y.stride(0), _ptr(y_codes),
@@ -165,6 +288,11 @@ def gemm_w4a4_lowrank_swiglu(a_codes, a_scales, b_codes, b_scales, M, N, K, y, t
     """MXFP4 GEMM (+ t L2) over N weight rows grouped as 32 gate + 32 up rows per 32
     output columns; y bf16 [M, N/2] receives silu(gate) * up."""
     r = 0 if l2t is None else l2t.shape[1]
+    dev = _gemm_checks(MXFP4, a_codes, a_scales, None, b_codes, b_scales, None, M, N, K, y, bias,
+                       (torch.bfloat16,), ycols=N // 2)
+    if r:
+        _packed(t, "t", torch.float32, M, r, dev)
+        _packed(l2t, "l2t", torch.bfloat16, N, r, dev)
     st = load().gemm_w4a4_lowrank_swiglu(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M,
                                          N, K, _ptr(t), _ptr(l2t), r, _ptr(bias), _ptr(y), y.stride(0),
                                          _stream(stream))
@@ -177,7 +305,17 @@ def gemm_w4a4_lowrank_qkv_rope(a_codes, a_scales, b_codes, b_scales, M, N, K, yq
     stored to yq, yk, yv (bf16 [M, D], one row stride), Q and K rotated by cs
     (float [M, head_dim/2, 2] of cos, sin) when given."""
     r = 0 if l2t is None else l2t.shape[1]
-    assert yk.stride(0) == yq.stride(0) == yv.stride(0), "yq, yk, yv share one row stride"
+    dev = _gemm_checks(MXFP4, a_codes, a_scales, None, b_codes, b_scales, None, M, N, K, yq, bias,
+                       (torch.bfloat16,), ycols=N // 3)
+    for name, yo in (("yk", yk), ("yv", yv)):
+        _strided(yo, name, (torch.bfloat16,), M, N // 3, dev)
+    if yk.stride(0) != yq.stride(0) or yv.stride(0) != yq.stride(0):
+        raise ValueError("yq, yk, yv share one row stride")
+    if cs is not None:
+        _packed(cs, "cs", torch.float32, M, max(head_dim, 0), dev)
+    if r:
+        _packed(t, "t", torch.float32, M, r, dev)
+        _packed(l2t, "l2t", torch.bfloat16, N, r, dev)
     st = load().gemm_w4a4_lowrank_qkv_rope(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M,
                                            N, K, _ptr(t), _ptr(l2t), r, _ptr(bias), _ptr(cs), head_dim,
                                            _ptr(yq), _ptr(yk), _ptr(yv), yq.stride(0), _stream(stream))
@@ -187,6 +325,13 @@ def gemm_w4a4_lowrank_qkv_rope(a_codes, a_scales, b_codes, b_scales, M, N, K, yq
 def gemm_w4a16(x, w_codes, w_scales, w_zeros, N, y, bias=None, group=64, out=OUT_BF16, stream=None):
     _rowmajor(x, "x")
     M, K = x.shape
+    dev = _device(x, "x")
+    _strided(x, "x", (torch.bfloat16,), M, K, dev)
+    _operand(INT4_G64, w_codes, w_scales, None, N, K, dev, "w")
+    _packed(w_zeros, "w_zeros", torch.bfloat16, N, K // 64, dev)
+    _strided(y, "y", (_out_dtype(out),), M, N, dev)
+    if bias is not None:
+        _packed(bias, "bias", torch.bfloat16, 1, N, dev)
     st = load().gemm_w4a16(_ptr(x), x.stride(0), _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros), M, N,
                            K, group, _ptr(bias), _ptr(y), y.stride(0), int(out), _stream(stream))
     _check("gemm_w4a16", st)

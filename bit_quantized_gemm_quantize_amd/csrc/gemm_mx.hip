@@ -109,8 +109,14 @@ struct MxLoads {
                                         int stage) const {
     auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);   // [operand][stage]
     const int lr = lane >> 3, lp = lane & 7;
-    const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);      // row & 7 == lr
-    const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
+    // row = 16 q + 8 (j % 2) + lr (per * wave is a multiple of 16): its swizzle
+    // lds_swz<8>(row) is 4 (j % 2) + lr / 2, so two block offsets serve every row
+    uint32_t koff[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t blk = (uint32_t)kt * 8 + (lp ^ (4 * jp + (lr >> 1)));
+      koff[jp] = blk < nblk ? blk * 16 : kOOB;
+    }
 #pragma unroll
     for (int idx = begin(PART); idx < begin(PART + 1); ++idx) {
       const int op = idx < kNA ? 0 : 1;
@@ -118,7 +124,7 @@ struct MxLoads {
       const int j = op == 0 ? idx : idx - kNA;
       const uint32_t row = per * wave + 8 * j + lr;
       // koff = kOOB keeps the sum past the buffer size (rows * kbytes < 2^31): no select
-      buf_ld16_lds(op == 0 ? ra : rb, &lds[op][stage][(per * wave + 8 * j) * kKTB], row * kbytes + koff);
+      buf_ld16_lds(op == 0 ? ra : rb, &lds[op][stage][(per * wave + 8 * j) * kKTB], row * kbytes + koff[j & 1]);
     }
   }
   template <int PART>
@@ -162,23 +168,28 @@ struct MxLoads {
   __device__ __forceinline__ void lowrank_loads(const float* __restrict__ t,
                                                 const uint16_t* __restrict__ l2t, int64_t m0,
                                                 int64_t n0) const {
-    if (R > 0) {
+    if constexpr (R > 0) {
       auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kBM * kKTB]>(lds_raw);
       const auto rt = make_rsrc(t + m0 * R, rows_a * (uint32_t)(4 * R));
       const auto rl = make_rsrc(l2t + n0 * R, rows_b * (uint32_t)(2 * R));
       uint8_t* lt = &lds[0][1][0];                 // kBM * 4R <= 32 KB
       uint8_t* ll = &lds[1][1][0];                 // kTN * 2R <= 16 KB
+      // 1 KB pieces; lane i fills LDS bytes 16 i .. of its piece, which hold the
+      // swizzled chunk (lds_swz) of row 16 i / rowbytes
+      constexpr int kCT = 4 * R / 16, kCL = 2 * R / 16;   // 16-byte chunks per t / L2^T row
       constexpr int kPiecesT = kBM * 4 * R / 1024;  // kBM * 4R bytes in 1 KB pieces
 #pragma unroll
       for (int j = 0; j < kPiecesT / kWaves; ++j) {
         const int piece = wave * (kPiecesT / kWaves) + j;
-        buf_ld16_lds(rt, lt + piece * 1024, piece * 1024 + lane * 16);
+        const int row = (piece * 64 + lane) / kCT, c = (piece * 64 + lane) % kCT;
+        buf_ld16_lds(rt, lt + piece * 1024, row * (4 * R) + ((c ^ lds_swz<kCT>(row)) << 4));
       }
       constexpr int kPieces = kTN * 2 * R / 1024;  // kTN * 2R bytes
 #pragma unroll
       for (int j = 0; j < (kPieces + kWaves - 1) / kWaves; ++j) {
         const int piece = j * kWaves + wave;
-        if (piece < kPieces) buf_ld16_lds(rl, ll + piece * 1024, piece * 1024 + lane * 16);
+        const int row = (piece * 64 + lane) / kCL, c = (piece * 64 + lane) % kCL;
+        if (piece < kPieces) buf_ld16_lds(rl, ll + piece * 1024, row * (2 * R) + ((c ^ lds_swz<kCL>(row)) << 4));
       }
     }
   }
@@ -457,12 +468,12 @@ __device__ __forceinline__ int mx_tile(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int row = wm * 128 + 32 * g + r32;
-      fa[buf][g] = ld16(&lds[0][stage][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+      fa[buf][g] = ld16(&lds[0][stage][row * kKTB + (((4 * h + s) ^ lds_swz<8>(row)) << 4)]);
     }
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int row = wn * 32 * F + 32 * f + r32;
-      fb[buf][f] = ld16(&lds[1][stage][row * kKTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+      fb[buf][f] = ld16(&lds[1][stage][row * kKTB + (((4 * h + s) ^ lds_swz<8>(row)) << 4)]);
     }
   };
 
@@ -501,7 +512,7 @@ __device__ __forceinline__ int mx_tile(
     for (int g = 0; g < 4; ++g) acc[f][g] = v16f{};
   // The low-rank term t L2 goes into the accumulators first (its operands came
   // with the prologue), so the epilogue is left with the bias and the store.
-  if (R > 0) {
+  if constexpr (R > 0) {
     lowrank_accumulate_lds<R>(acc, &lds[0][1][0], &lds[1][1][0], 128 * wm, 32 * F * wn, lane);
     // stage 1 is free again for K-tile 1.  The prologue loads were waited for above;
     // a fenced barrier would also wait for the previous tile's stores.

@@ -99,6 +99,18 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(u32x4 a, u32x4 b, v16f c) {
 // Row index (within the 32x32 MFMA result) of accumulator register v of lane l.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
+// LDS swizzle.  The gfx950 LDS has 64 banks of 4 bytes: a 16-byte access by 16 lanes
+// is served in one pass when the lanes' addresses fall in 16 different 16-byte slots
+// of a 256-byte bank row.  A row of C 16-byte chunks (C = 2, 4 or 8) shares its bank
+// row with 16 / C - 1 neighbours; storing chunk c of row r at c ^ lds_swz<C>(r) (the
+// row's bank-row index modulo C) gives any 16 consecutive rows, read at one logical
+// chunk, 16 distinct slots.
+template <int C>
+__device__ __forceinline__ int lds_swz(int row) {
+  static_assert(C == 2 || C == 4 || C == 8, "16-byte chunks per row");
+  return (row >> (C == 8 ? 1 : (C == 4 ? 2 : 3))) & (C - 1);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

@@ -71,20 +71,23 @@ __device__ __forceinline__ void lowrank_accumulate(v16f (&acc)[F][4], int64_t n_
 
 // The same t L2 term with both operands already in LDS: lds_t holds the tile's t
 // rows (fp32, 4R bytes each, row m_local at m_local * 4R), lds_l2 its L2^T rows
-// (bf16, 2R bytes each).  m_loc / n_loc: first row of the wave's region within
-// the tile.
+// (bf16, 2R bytes each), both with their 16-byte chunks swizzled by lds_swz.
+// m_loc / n_loc: first row of the wave's region within the tile (multiples of 16).
 template <int R, int F>
 __device__ __forceinline__ void lowrank_accumulate_lds(v16f (&acc)[F][4], const uint8_t* lds_t,
                                                        const uint8_t* lds_l2, int m_loc, int n_loc,
                                                        int lane) {
+  constexpr int kCT = 4 * R / 16, kCL = 2 * R / 16;     // 16-byte chunks per row
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < R / 16; ++ks) {
     u32x4 thi[4], tlo[4], l2f[F];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint8_t* src = lds_t + (m_loc + 32 * g + r32) * (4 * R) + (16 * ks + 8 * h) * 4;
-      const u32x4 a = ld16(src), b = ld16(src + 16);
+      const int row = m_loc + 32 * g + r32, c = 4 * ks + 2 * h;   // chunks c, c + 1: t[16 ks + 8 h ..]
+      const uint8_t* src = lds_t + row * (4 * R);
+      const u32x4 a = ld16(src + ((c ^ lds_swz<kCT>(row)) << 4)),
+                  b = ld16(src + (((c + 1) ^ lds_swz<kCT>(row)) << 4));
       const uint32_t tv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -95,8 +98,10 @@ __device__ __forceinline__ void lowrank_accumulate_lds(v16f (&acc)[F][4], const 
       }
     }
 #pragma unroll
-    for (int f = 0; f < F; ++f)
-      l2f[f] = ld16(lds_l2 + (n_loc + 32 * f + r32) * (2 * R) + (16 * ks + 8 * h) * 2);
+    for (int f = 0; f < F; ++f) {
+      const int row = n_loc + 32 * f + r32, c = 2 * ks + h;       // L2^T[16 ks + 8 h ..]
+      l2f[f] = ld16(lds_l2 + row * (2 * R) + ((c ^ lds_swz<kCL>(row)) << 4));
+    }
 #pragma unroll
     for (int f = 0; f < F; ++f)
 #pragma unroll

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from bit_quantized_gemm_quantize_amd import binding as B
-from bit_quantized_gemm_quantize_amd import synth
+from bit_quantized_gemm_quantize_amd import synth, weight_prep
 from oracle import formats as F
 from oracle import layer as L
 from oracle import quant as Q
@@ -93,7 +93,7 @@ def test_gemm_w4a4_parity(fmt, M, N, K):
 @pytest.mark.parametrize("M,N,K,r", [(64, 256, 256, 32), (300, 520, 384, 16), (200, 384, 512, 32)])
 def test_gemm_w4a4_lowrank_parity(fmt, M, N, K, r):
     dev = device()
-    d = synth.mlp_up_svd(seed=2, M=M, K=K, N=N, rank=r)
+    d = weight_prep.mlp_up_svd(seed=2, M=M, K=K, N=N, rank=r)
     bias = synth.bias(N, seed=3)
     for f32 in (True, False):
         say(f"gemm_w4a4_lowrank {fmt} M={M} N={N} K={K} r={r} f32={f32}")
@@ -144,10 +144,11 @@ def test_gemm_k_zero_gives_bias(fmt):
     # no codes or block scales are read at K = 0; int4_sym reads its float row scales
     # [M] and [N] (zeros here)
     dummy = torch.zeros(4 * max(M, N), dtype=torch.uint8, device=dev)
+    sdummy = torch.zeros(max(M, N), dtype=torch.float32, device=dev) if fmt == "int4_sym" else dummy
     y = out_buffer(M, N, dev, f32=True)
     b = bf16_dev(bias[None, :], dev)[0]
     say(f"gemm_w4a4 {fmt} K=0")
-    B.gemm_w4a4(fmt, dummy, dummy, None, dummy, dummy, None, M, N, 0, y, bias=b, out=B.OUT_F32)
+    B.gemm_w4a4(fmt, dummy, sdummy, None, dummy, sdummy, None, M, N, 0, y, bias=b, out=B.OUT_F32)
     torch.cuda.synchronize()
     yh, ok = y_host(y, N)
     assert ok and np.array_equal(yh, np.broadcast_to(F.bf16_to_f64(bias), (M, N)))
@@ -155,7 +156,7 @@ def test_gemm_k_zero_gives_bias(fmt):
 
 def test_gemm_deterministic():
     dev = device()
-    d = synth.mlp_up_svd(seed=6, M=512, K=1024, N=768, rank=32)
+    d = weight_prep.mlp_up_svd(seed=6, M=512, K=1024, N=768, rank=32)
     say("gemm_w4a4_lowrank determinism")
     y1 = run_w4a4("mxfp4", d["x"], d["rt"], dev, f32=False, l1=d["l1"], l2=d["l2"])
     y2 = run_w4a4("mxfp4", d["x"], d["rt"], dev, f32=False, l1=d["l1"], l2=d["l2"])
@@ -168,7 +169,7 @@ def test_gemm_mx_leftover_tiles_as_halves():
     rank-32 branch and bias, every element checked."""
     dev = device()
     M, N, K = 4335, 4024, 256
-    d = synth.mlp_up_svd(seed=10, M=M, K=K, N=N, rank=32)
+    d = weight_prep.mlp_up_svd(seed=10, M=M, K=K, N=N, rank=32)
     bias = synth.bias(N, seed=11)
     for f32 in (True, False):
         say(f"gemm_w4a4_lowrank mxfp4 leftover tiles M={M} N={N} K={K} f32={f32}")
@@ -187,7 +188,7 @@ def test_gemm_mx_several_tiles_per_workgroup(K):
     bias, bf16 and fp32 output, every element checked."""
     dev = device()
     M, N = 4600, 12280
-    d = synth.mlp_up_svd(seed=12, M=M, K=K, N=N, rank=16)
+    d = weight_prep.mlp_up_svd(seed=12, M=M, K=K, N=N, rank=16)
     bias = synth.bias(N, seed=13)
     y_ref, bound = ref_w4a4("mxfp4", d["x"], d["rt"], bias=bias, l1=d["l1"], l2=d["l2"])
     for f32 in (False, True):
@@ -201,7 +202,7 @@ def test_full_mlp_up_svd_layer_sampled_rows():
     """The benchmarked configuration: M=4608, K=3072, N=12288, rank 32, bf16 output,
     quantize_act (+ t) -> gemm_w4a4_lowrank, checked on sampled rows x all columns."""
     dev = device()
-    d = synth.mlp_up_svd(seed=0)
+    d = weight_prep.mlp_up_svd(seed=0)
     M, N = d["M"], d["N"]
     say("full layer mxfp4 4608x3072x12288 r=32 bf16")
     y = run_w4a4("mxfp4", d["x"], d["rt"], dev, f32=False, l1=d["l1"], l2=d["l2"])

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from bit_quantized_gemm_quantize_amd import binding as B
-from bit_quantized_gemm_quantize_amd import synth
+from bit_quantized_gemm_quantize_amd import synth, weight_prep
 from oracle import formats as F
 from oracle import layer as L
 from oracle import quant as Q
@@ -99,7 +99,7 @@ def test_mxout_matches_the_stored_output(M, N, K, r):
     scales are the oracle's quantization of exactly that stored output, and a launch
     without the bf16 output emits the same codes."""
     dev = device()
-    d = synth.mlp_up_svd(seed=M, M=M, K=K, N=N, rank=r)
+    d = weight_prep.mlp_up_svd(seed=M, M=M, K=K, N=N, rank=r)
     bias = synth.bias(N, seed=M + 1)
     say(f"gemm_w4a4_lowrank_mxout M={M} N={N} K={K} r={r}")
     qc, qs, yb = run_mxout(d["x"], d["rt"], dev, l1=d["l1"], l2=d["l2"], bias=bias)
@@ -119,7 +119,7 @@ def test_mxout_full_mlp_up_sampled_rows():
     dequantized values on sampled rows lie within the MXFP4 step of the oracle's Y
     plus the GEMM bound."""
     dev = device()
-    d = synth.mlp_up_svd(seed=0)
+    d = weight_prep.mlp_up_svd(seed=0)
     M, K, N = d["M"], d["K"], d["N"]
     say("gemm_w4a4_lowrank_mxout full 4608x3072x12288 r=32")
     qc, qs, _ = run_mxout(d["x"], d["rt"], dev, l1=d["l1"], l2=d["l2"], with_y=False)

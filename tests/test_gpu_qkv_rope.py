@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from bit_quantized_gemm_quantize_amd import binding as B
-from bit_quantized_gemm_quantize_amd import synth
+from bit_quantized_gemm_quantize_amd import synth, weight_prep
 from oracle import formats as F
 from oracle import layer as L
 from oracle import quant as Q
@@ -135,7 +135,7 @@ def test_qkv_rope_full_attention_qkv_sampled_rows():
     # a fused QKV projection of the attention blocks: 4608 tokens, 3072 -> 3 x 3072,
     # head width 128, rank-32 branch; 40 sampled rows against the oracle
     dev = device()
-    d = synth.mlp_up_svd(seed=3, N=9216)
+    d = weight_prep.mlp_up_svd(seed=3, N=9216)
     M, hd = d["M"], 128
     cs = rope_table(M, hd, seed=22)
     say("qkv rope full 4608x3072x9216 r=32")

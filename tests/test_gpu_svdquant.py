@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from bit_quantized_gemm_quantize_amd import binding as B
-from bit_quantized_gemm_quantize_amd import synth
+from bit_quantized_gemm_quantize_amd import synth, weight_prep
 from oracle import formats as F
 from oracle import layer as L
 from oracle import quant as Q
@@ -68,7 +68,7 @@ def test_quantize_smooth_wide_range_and_padded_rows():
 def test_quantize_smooth_fused_t_uses_unsmoothed_x():
     dev = device()
     M, K, r = 96, 512, 32
-    d = synth.attn_proj_svdquant(seed=2, M=M, K=K, N=256, rank=r, calib=256)
+    d = weight_prep.attn_proj_svdquant(seed=2, M=M, K=K, N=256, rank=r, calib=256)
     say(f"quantize_act_smooth mxfp4 + t=X L1 M={M} K={K} r={r}")
     g = quantize_smooth(d["x"], d["inv_s"], dev, l1_bits=d["l1"])
     X, L1 = F.bf16_to_f64(d["x"]), F.bf16_to_f64(d["l1"])
@@ -104,7 +104,7 @@ def ref_svdquant_layer(d, rows=None):
 @pytest.mark.parametrize("f32", [True, False])
 def test_svdquant_layer_parity(f32):
     dev = device()
-    d = synth.attn_proj_svdquant(seed=6, M=300, K=1024, N=520, rank=32, calib=512)
+    d = weight_prep.attn_proj_svdquant(seed=6, M=300, K=1024, N=520, rank=32, calib=512)
     say(f"svdquant layer 300x1024x520 r=32 f32={f32}")
     y = run_svdquant_layer(d, dev, f32)
     y_ref, bound = ref_svdquant_layer(d)
@@ -116,7 +116,7 @@ def test_full_svdquant_attention_projection_sampled_rows():
     on sampled rows against the oracle; and its error against the unquantized bf16
     product is far below plain W4A4's on the same activations (reported)."""
     dev = device()
-    d = synth.attn_proj_svdquant(seed=0)
+    d = weight_prep.attn_proj_svdquant(seed=0)
     M = d["M"]
     say("full svdquant attention projection 4608x3072x3072 r=32 bf16")
     y = run_svdquant_layer(d, dev, f32=False)

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from bit_quantized_gemm_quantize_amd import binding as B
-from bit_quantized_gemm_quantize_amd import synth
+from bit_quantized_gemm_quantize_amd import synth, weight_prep
 from oracle import formats as F
 from oracle import layer as L
 from oracle import quant as Q
@@ -102,7 +102,7 @@ def test_swiglu_full_mlp_up_sampled_rows():
     # the MLP up-projection shape with its rank-32 branch: 4608 x 3072 against 12288
     # weight rows (6144 outputs); 40 sampled rows against the oracle
     dev = device()
-    d = synth.mlp_up_svd(seed=2)
+    d = weight_prep.mlp_up_svd(seed=2)
     M = d["M"]
     say("swiglu full 4608x3072x12288 r=32")
     y = run_swiglu(d["x"], d["rt"], dev, l1=d["l1"], l2=d["l2"])

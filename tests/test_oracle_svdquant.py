@@ -9,7 +9,7 @@ from fractions import Fraction
 import numpy as np
 
 import oracle
-from bit_quantized_gemm_quantize_amd import synth
+from bit_quantized_gemm_quantize_amd import synth, weight_prep
 
 F, Q = oracle.formats, oracle.quant
 GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
@@ -70,7 +70,7 @@ def test_smoothing_factors_closed_form():
     wt = synth.weights(40, 96, seed=3)
     wt = wt.copy()
     wt[:, 5] = 0                                            # a zero weight channel -> s = 1
-    inv, s = synth.smoothing_factors(x, wt)
+    inv, s = weight_prep.smoothing_factors(x, wt)
     xa = np.abs(F.bf16_to_f64(x)).max(axis=0)
     wa = np.abs(F.bf16_to_f64(wt)).max(axis=0)
     want = np.sqrt(xa / np.where(wa > 0, wa, 1.0))
@@ -84,7 +84,7 @@ def test_smoothing_factors_closed_form():
 def test_weighted_lowrank_identity_is_truncated_svd():
     rng = np.random.default_rng(7)
     w = rng.standard_normal((48, 40))
-    l1, l2, sv = synth.weighted_lowrank(w, np.eye(48), 6, ridge=0.0)
+    l1, l2, sv = weight_prep.weighted_lowrank(w, np.eye(48), 6, ridge=0.0)
     u, s, vh = np.linalg.svd(w, full_matrices=False)
     assert np.allclose(l1 @ l2, (u[:, :6] * s[:6]) @ vh[:6], atol=1e-10)
     assert np.allclose(sv, s)
@@ -96,7 +96,7 @@ def test_weighted_lowrank_error_closed_form_and_optimality():
     a = rng.standard_normal((200, K)) * np.exp(rng.uniform(-2, 2, K))[None, :]
     c = np.cov(a.T)
     w = rng.standard_normal((K, N))
-    l1, l2, sv = synth.weighted_lowrank(w, c, r, ridge=0.0)
+    l1, l2, sv = weight_prep.weighted_lowrank(w, c, r, ridge=0.0)
     lam, q = np.linalg.eigh(0.5 * (c + c.T))
     root = (q * np.sqrt(lam)[None, :]) @ q.T
     err = np.linalg.norm(root @ (w - l1 @ l2))
@@ -107,7 +107,7 @@ def test_weighted_lowrank_error_closed_form_and_optimality():
 
 
 def test_svdquant_split_reconstructs_the_smoothed_weight():
-    d = synth.attn_proj_svdquant(seed=4, M=64, K=256, N=192, rank=16, calib=256)
+    d = weight_prep.attn_proj_svdquant(seed=4, M=64, K=256, N=192, rank=16, calib=256)
     s = 1.0 / d["inv_s"].astype(np.float64)
     w = F.bf16_to_f64(d["wt"]).T * s[:, None]                      # W' [K, N]
     approx = (F.bf16_to_f64(d["l1"]) * s[:, None]) @ F.bf16_to_f64(d["l2"])
@@ -124,15 +124,74 @@ def test_svdquant_lowers_the_layer_error():
     weighted low-rank branch beats plain W4A4 and the unsmoothed SVD split by a wide
     margin on activations with 1% outlier channels."""
     M, K, N, r = 256, 512, 512, 32
-    d = synth.attn_proj_svdquant(seed=3, M=M, K=K, N=N, rank=r, calib=512)
+    d = weight_prep.attn_proj_svdquant(seed=3, M=M, K=K, N=N, rank=r, calib=512)
     x = F.bf16_to_f64(d["x"])
     y = x @ F.bf16_to_f64(d["wt"]).T
     rel = lambda yq: np.linalg.norm(yq - y) / np.linalg.norm(y)
     A = Q.mx_dequantize(*Q.mx_quantize(d["x"]))
     plain = rel(A @ Q.mx_dequantize(*Q.mx_quantize(d["wt"])).T)
-    l1, l2, rt = synth.lowrank_split(d["wt"], r, 3)
+    l1, l2, rt = weight_prep.lowrank_split(d["wt"], r, 3)
     split = rel(A @ Q.mx_dequantize(*Q.mx_quantize(rt)).T + (x @ F.bf16_to_f64(l1)) @ F.bf16_to_f64(l2))
     As = Q.mx_dequantize(*Q.mx_quantize_smoothed(d["x"], d["inv_s"]))
     svdq = rel(As @ Q.mx_dequantize(*Q.mx_quantize(d["rt"])).T
                + (x @ F.bf16_to_f64(d["l1"])) @ F.bf16_to_f64(d["l2"]))
     assert svdq < 0.3 * plain and svdq < 0.3 * split, (plain, split, svdq)
+
+
+def test_int4_channel_estimate_against_brute_force():
+    """The Guide's per-channel INT4 estimate: every entry is the nearest of the 16
+    grid points q * step (q = -8 .. 7, step = row amax / 7 floored at 1e-8), ties
+    to the even q, found by exhaustive search in exact arithmetic."""
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((6, 40)) * np.exp(rng.uniform(-3, 3, (6, 1)))
+    w[2] = 0.0                                   # an all-zero channel: step 1e-8, all zeros
+    w[3, :8] = np.array([0.5, 1.5, -0.5, -2.5, 3.5, 7.0, -7.0, 2.0]) * (7.0 / 7.0)   # ties at step 1
+    w[3, 8:] = 0.0
+    est = weight_prep.int4_channel_estimate(w)
+    for n in range(w.shape[0]):
+        step = max(Fraction(float(np.abs(w[n]).max())) / 7, Fraction(1e-8))
+        for k in range(w.shape[1]):
+            v = Fraction(float(w[n, k]))
+            q = min(range(-8, 8), key=lambda c: (abs(c * step - v), c & 1))
+            assert Fraction(float(est[n, k])) == Fraction(float(q * step)) or \
+                abs(Fraction(float(est[n, k])) - q * step) <= step * Fraction(2) ** -50, (n, k)
+
+
+def test_guide_step1_factors_pins():
+    """The Guide's literal Step-1 factors: (1) a weight already on its INT4 grid has
+    no error to factor; (2) with an identity covariance the factors are the best
+    rank-r approximation of the error (Eckart-Young: the residual norm is the
+    discarded singular values, and beats another rank-r candidate); (3) scaling the
+    covariance by a scales the factors' product by a (the product carries the
+    covariance's units, which is why the page's residual W - L1 L2 is not an
+    approximation of the quantization error)."""
+    rng = np.random.default_rng(12)
+    N, K, r = 24, 32, 4
+    step = np.exp(rng.uniform(-2, 1, (N, 1)))
+    q = rng.integers(-7, 8, (N, K)).astype(np.float64)   # |q| <= 7: the row amax is 7 steps
+    q[:, 0] = 7.0                                 # the row amax is 7 steps: the grid is exact
+    left, right, s = weight_prep.guide_step1_factors(q * step, np.eye(K), r)
+    # only the rounding of amax / 7 separates the weight from its grid
+    assert s[0] <= 1e-13 * np.abs(q * step).max() and np.abs(left @ right).max() <= 1e-13 * np.abs(q * step).max()
+    w = rng.standard_normal((N, K))
+    dw = w - weight_prep.int4_channel_estimate(w)
+    left, right, s = weight_prep.guide_step1_factors(w, np.eye(K), r)
+    err = np.linalg.norm(dw - left @ right)
+    assert math.isclose(err, math.sqrt(np.sum(s[r:] ** 2)), rel_tol=1e-9)
+    other = dw.copy()
+    other[:, r:] = 0.0                            # a different rank-r matrix
+    assert err < np.linalg.norm(dw - other)
+    l3, r3, _ = weight_prep.guide_step1_factors(w, 3.0 * np.eye(K), r)
+    assert np.allclose(l3 @ r3, 3.0 * (left @ right), rtol=1e-9, atol=1e-12)
+
+
+def test_guide_step1_split_reconstructs_the_weight():
+    d = weight_prep.attn_proj_calibrated(seed=5, M=32, K=128, N=96, calib=256)
+    g = weight_prep.guide_step1_split(d["x_cal"], d["wt"], 8)
+    w = F.bf16_to_f64(d["wt"])                                        # [N, K]
+    left, right, _ = weight_prep.guide_step1_factors(w, np.cov(F.bf16_to_f64(d["x_cal"]).T), 8)
+    exact = w - left @ right
+    r = F.bf16_to_f64(g["rt"])
+    assert np.all(np.abs(r - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)   # bf16 rounding only
+    assert np.array_equal(g["l1"], synth.to_bf16_bits(right.T))
+    assert np.array_equal(g["l2"], synth.to_bf16_bits(left.T))
