@@ -1,7 +1,11 @@
 // The C ABI of libq4lin (declared in include/q4lin.h): argument checks on the
-// host, then the launches, queued on the caller's stream.  No allocation, no
-// synchronization, no state.
+// host, then the launches, queued on the caller's stream.  No synchronization;
+// the only allocation is the NVFP4 scratch below.
 #include "q4lin.h"
+
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "q4_internal.h"
 
@@ -16,6 +20,31 @@ bool rank_ok(int32_t r) { return r == 0 || r == 16 || r == 32; }
 // Size limits of the kernels' 32-bit tile addressing and grid sizes.
 constexpr int64_t kMaxRows = int64_t(1) << 30;   // M, N
 constexpr int64_t kMaxK = int64_t(1) << 22;      // K, and ldx of the W4A16 activations
+constexpr int64_t kMaxLdx = int64_t(1) << 26;    // ldx of the quantizer's activations
+
+// The NVFP4 tensor-amax scratch (q4::kNvScratchWords words): one buffer per
+// (device, stream), allocated on the first NVFP4 quantization queued on that
+// stream and kept until the process ends.  Work queued on one stream runs in
+// order, so no two calls use one buffer at the same time; calls on different
+// streams get different buffers.  Null if the allocation fails.
+uint32_t* nv_stream_scratch(void* stream) {
+  static std::mutex mu;
+  static std::map<std::pair<int, void*>, uint32_t*> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, stream);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  void* p = nullptr;
+  if (hipMalloc(&p, sizeof(uint32_t) * q4::kNvScratchWords) != hipSuccess) return nullptr;
+  cache.emplace(key, static_cast<uint32_t*>(p));
+  return static_cast<uint32_t*>(p);
+}
+
+// K granularity of the W4A4 GEMMs: the block of MXFP4 (32) and NVFP4 (16); the
+// INT4 and MXFP8 kernels step K in tiles of 128.
+int64_t gemm_k_unit(q4_format fmt) { return fmt == Q4_MXFP4 ? 32 : (fmt == Q4_NVFP4 ? 16 : 128); }
 
 // Checks shared by the two W4A4 entry points.
 q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -24,7 +53,7 @@ q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_sca
                      q4_out out) {
   if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8) return Q4_ERR_FORMAT;
   if (out != Q4_OUT_BF16 && out != Q4_OUT_F32) return Q4_ERR_FORMAT;
-  if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || ldy < N) return Q4_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || (K % gemm_k_unit(fmt)) != 0 || ldy < N) return Q4_ERR_SHAPE;
   if (M > kMaxRows || N > kMaxRows || K > kMaxK) return Q4_ERR_SHAPE;
   if (!a_codes || !a_scales || !b_codes || !b_scales || !y) return Q4_ERR_NULL;
   if (fmt == Q4_NVFP4 && (!a_tscale || !b_tscale)) return Q4_ERR_NULL;
@@ -47,6 +76,7 @@ const char* q4_status_string(q4_status s) {
     case Q4_ERR_ALIGN: return "Q4_ERR_ALIGN";
     case Q4_ERR_FORMAT: return "Q4_ERR_FORMAT";
     case Q4_ERR_LAUNCH: return "Q4_ERR_LAUNCH";
+    case Q4_ERR_ALLOC: return "Q4_ERR_ALLOC";
   }
   return "unknown";
 }
@@ -56,8 +86,10 @@ q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, i
                        const uint16_t* l1t, int32_t r, float* t, void* stream) {
   if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8) return Q4_ERR_FORMAT;
   if ((fmt == Q4_INT4_SYM || fmt == Q4_MXFP8) && r != 0) return Q4_ERR_FORMAT;
-  if (M < 0 || K < 0 || (K % 32) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
-  if (M > kMaxRows) return Q4_ERR_SHAPE;
+  // NVFP4 blocks are 16 wide; with the fused t the pass reads 32 at a time
+  const int64_t unit = (fmt == Q4_NVFP4 && r == 0) ? 16 : 32;
+  if (M < 0 || K < 0 || (K % unit) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || K > kMaxK || ldx > kMaxLdx) return Q4_ERR_SHAPE;
   if (!x || !codes || !scales) return Q4_ERR_NULL;
   if (fmt == Q4_NVFP4 && !tensor_scale) return Q4_ERR_NULL;
   if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
@@ -66,13 +98,14 @@ q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, i
   if (fmt == Q4_NVFP4 && !aligned(tensor_scale, 4)) return Q4_ERR_ALIGN;
   if (r > 0 && (!aligned(l1t, 16) || !aligned(t, 16))) return Q4_ERR_ALIGN;
   if (M == 0) return Q4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (fmt == Q4_INT4_SYM)
-    return launched(q4::launch_int4_sym_rows(x, M, K, ldx, 1, codes, reinterpret_cast<float*>(scales),
-                                             static_cast<hipStream_t>(stream)));
-  if (fmt == Q4_MXFP8)
-    return launched(q4::launch_mxfp8_rows(x, M, K, ldx, 1, codes, scales, static_cast<hipStream_t>(stream)));
-  return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t,
-                                          (int)r, t, static_cast<hipStream_t>(stream)));
+    return launched(q4::launch_int4_sym_rows(x, M, K, ldx, 1, codes, reinterpret_cast<float*>(scales), s));
+  if (fmt == Q4_MXFP8) return launched(q4::launch_mxfp8_rows(x, M, K, ldx, 1, codes, scales, s));
+  uint32_t* scratch = nullptr;
+  if (fmt == Q4_NVFP4 && (scratch = nv_stream_scratch(stream)) == nullptr) return Q4_ERR_ALLOC;
+  return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t, (int)r,
+                                          t, s, scratch));
 }
 
 q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -80,7 +113,7 @@ q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64
                               const uint16_t* l1t, int32_t r, float* t, void* stream) {
   if (fmt != Q4_MXFP4) return Q4_ERR_FORMAT;
   if (M < 0 || K < 0 || (K % 32) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
-  if (M > kMaxRows) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || K > kMaxK || ldx > kMaxLdx) return Q4_ERR_SHAPE;
   if (!x || !inv_s || !codes || !scales) return Q4_ERR_NULL;
   if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
   if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(codes, 16) || !aligned(scales, 4) ||
@@ -89,7 +122,7 @@ q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64
   if (r > 0 && (!aligned(l1t, 16) || !aligned(t, 16))) return Q4_ERR_ALIGN;
   if (M == 0) return Q4_OK;
   return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, nullptr, l1t, (int)r,
-                                          t, static_cast<hipStream_t>(stream), inv_s));
+                                          t, static_cast<hipStream_t>(stream), nullptr, inv_s));
 }
 
 q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, int64_t stride_k,
@@ -97,7 +130,7 @@ q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, i
                        float* tensor_scale, void* stream) {
   if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_G64 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8)
     return Q4_ERR_FORMAT;
-  const int64_t blk = fmt == Q4_INT4_G64 ? 64 : 32;
+  const int64_t blk = fmt == Q4_INT4_G64 ? 64 : (fmt == Q4_NVFP4 ? 16 : 32);
   if (K < 0 || N < 0 || (K % blk) != 0 || stride_k < 1 || stride_n < 1) return Q4_ERR_SHAPE;
   if (!w || !codes || !scales) return Q4_ERR_NULL;
   if (fmt == Q4_INT4_G64 && !zeros) return Q4_ERR_NULL;
@@ -112,8 +145,10 @@ q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N, i
   if (fmt == Q4_MXFP8)
     return launched(q4::launch_mxfp8_rows(w, N, K, stride_n, stride_k, codes, static_cast<uint8_t*>(scales),
                                           static_cast<hipStream_t>(stream)));
+  uint32_t* scratch = nullptr;
+  if (fmt == Q4_NVFP4 && (scratch = nv_stream_scratch(stream)) == nullptr) return Q4_ERR_ALLOC;
   return launched(q4::launch_pack_weights((int)fmt, w, K, N, stride_k, stride_n, codes, scales, zeros,
-                                          tensor_scale, static_cast<hipStream_t>(stream)));
+                                          tensor_scale, static_cast<hipStream_t>(stream), scratch));
 }
 
 q4_status gemm_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -130,6 +165,9 @@ q4_status gemm_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_scal
     return launched(q4::launch_gemm_i4(a_codes, reinterpret_cast<const float*>(a_scales), b_codes,
                                        reinterpret_cast<const float*>(b_scales), M, N, K, ep, s));
   if (fmt == Q4_MXFP8) return launched(q4::launch_gemm_mx8(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
+  if (K % 128 != 0)
+    return launched(q4::launch_gemm_anyk((int)fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M,
+                                         N, K, ep, s));
   if (fmt == Q4_MXFP4) return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
   return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
 }
@@ -150,6 +188,9 @@ q4_status gemm_w4a4_lowrank(q4_format fmt, const uint8_t* a_codes, const uint8_t
   q4::EpilogueArgs ep{r > 0 ? t : nullptr, r > 0 ? l2t : nullptr, (int)r, bias, y, ldy,
                       out == Q4_OUT_F32 ? 1 : 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K % 128 != 0)
+    return launched(q4::launch_gemm_anyk((int)fmt, a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M,
+                                         N, K, ep, s));
   if (fmt == Q4_MXFP4) return launched(q4::launch_gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, ep, s));
   return launched(q4::launch_gemm_nv(a_codes, a_scales, a_tscale, b_codes, b_scales, b_tscale, M, N, K, ep, s));
 }

@@ -8,16 +8,6 @@
 
 namespace q4 {
 
-// Two E2M1 codes (byte B of a dword) times the block scale -> a bf16 pair.  The
-// products are exact bf16 values, so keeping the upper halves is exact; one byte
-// permute (bytes 2, 3 of lo, then of hi) packs them.
-template <int B>
-__device__ __forceinline__ uint32_t nv_dequant_pair(uint32_t codes, float s) {
-  const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B);
-  const uint32_t lo = __float_as_uint(v[0] * s), hi = __float_as_uint(v[1] * s);
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-}
-
 // 32 E2M1 codes (one 16-byte chunk) times their two block scales -> 4 chunks of bf16.
 __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x4* out4) {
   const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)(sc2 & 0xFFu), 0);

@@ -96,6 +96,17 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(u32x4 a, u32x4 b, v16f c) {
                                                  __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
+// Two E2M1 codes (byte B of a dword) times an NVFP4 block scale -> a bf16 pair.
+// Each product (two significant bits times the four of an E4M3 value) is an exact
+// bf16 value, so keeping the upper halves of the fp32 products is exact; one byte
+// permute (bytes 2, 3 of lo, then of hi) packs them.
+template <int B>
+__device__ __forceinline__ uint32_t nv_dequant_pair(uint32_t codes, float s) {
+  const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B);
+  const uint32_t lo = __float_as_uint(v[0] * s), hi = __float_as_uint(v[1] * s);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
 // Row index (within the 32x32 MFMA result) of accumulator register v of lane l.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 

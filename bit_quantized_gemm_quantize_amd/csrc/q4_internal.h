@@ -6,17 +6,23 @@
 
 namespace q4 {
 
+// Words of device scratch the NVFP4 tensor-amax launch needs (its partial maxima).
+constexpr int kNvScratchWords = 1024;
+
 // Activation quantizer (+ t = X L1 when r > 0).  fmt 0 = MXFP4, 1 = NVFP4.
-// NVFP4 queues: clear tensor_scale, tensor amax, encode, amax -> s_t.
+// NVFP4 queues the tensor-amax launch (partial maxima into nv_scratch, at least
+// kNvScratchWords words) and the encode launch; nv_scratch is unused otherwise.
+// inv_s (MXFP4, r > 0 only): the smoothing factors' reciprocals.
 hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                const uint16_t* l1t, int r, float* t, hipStream_t s,
-                               const float* inv_s = nullptr);
+                               uint32_t* nv_scratch, const float* inv_s = nullptr);
 
-// Weight packer over a strided logical [K, N] bf16 matrix.  fmt 0/1/2.
+// Weight packer over a strided logical [K, N] bf16 matrix.  fmt 0/1/2 (NVFP4 uses
+// nv_scratch as launch_quantize_act does).
 hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N, int64_t sk,
                                int64_t sn, uint8_t* codes, void* scales, uint16_t* zeros,
-                               float* tensor_scale, hipStream_t s);
+                               float* tensor_scale, hipStream_t s, uint32_t* nv_scratch);
 
 struct EpilogueArgs {
   const float* t;         // [M, r] fp32 or nullptr
@@ -67,5 +73,11 @@ hipError_t launch_gemm_nv(const uint8_t* ac, const uint8_t* as, const float* ats
 hipError_t launch_gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* wc,
                              const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                              int64_t K, const EpilogueArgs& ep, hipStream_t s);
+
+// The W4A4 GEMM for any K the formats allow (MXFP4: K % 32 == 0, NVFP4: K % 16 ==
+// 0), used when K is not a multiple of the tiled kernels' 128.  fmt 0 or 1.
+hipError_t launch_gemm_anyk(int fmt, const uint8_t* ac, const uint8_t* as, const float* ats,
+                            const uint8_t* bc, const uint8_t* bs, const float* bts, int64_t M,
+                            int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s);
 
 }  // namespace q4

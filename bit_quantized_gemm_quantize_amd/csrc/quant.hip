@@ -1,19 +1,14 @@
 // Activation quantizer (MXFP4 / NVFP4) fused with the low-rank down-projection,
 // and the offline weight packers.
 //
-// Activation pass (one read of X).  Without the low-rank term, MXFP4 and NVFP4 take
-// one thread per 32-element block instead (mx_rows_kernel, shared with MXFP8).  With
-// it:
-//   * a workgroup owns up to 32 rows (as many as spread M evenly over the CUs) and
-//     all of K; its 16 waves stride over K in pairs of 32-element blocks, so a lane
-//     (row l%32, half l/32) owns one whole block per step: 64 contiguous bytes of X
-//     in, 16 bytes of codes and its scale out.  The block maximum therefore needs
-//     no cross-lane exchange.
-//   * the same 64 bytes are the bf16 MFMA operand of t = X L1: the 32 block
-//     elements feed four 32x32x16 steps (K order permuted identically for X and L1,
-//     which a sum over K allows); L1^T rows are read 16 bytes at a time.
-//   * per-wave partial t tiles are summed through LDS in a fixed order, so t is
-//     deterministic.
+// Activation pass, one read of X per encode:
+//   * MXFP4 without the low-rank term: one thread per 32-element block
+//     (mx_rows_kernel, shared with MXFP8 and the weight packer).
+//   * with the low-rank term t = X L1 (or SmoothQuant factors): quant_act_kernel,
+//     rows on lanes, one whole block per lane, the same registers feeding the bf16
+//     MFMA of t.
+//   * NVFP4: a tensor-amax launch that leaves per-workgroup partial maxima in a
+//     small scratch array, then the encode launch (16-element blocks).
 #include <algorithm>
 
 #include "q4_device.h"
@@ -21,6 +16,8 @@
 
 namespace q4 {
 
+// partial maxima of the NVFP4 tensor-amax launch: the scratch it needs, 4 KB
+constexpr int kNvPartials = kNvScratchWords;
 constexpr int kQWaves = 16;
 constexpr int kQRows = 32;
 constexpr float kNvTensorDiv = 2688.0f;   // 6 (largest E2M1) * 448 (largest E4M3)
@@ -134,14 +131,13 @@ __device__ __forceinline__ int mx_encode_smoothed(const uint32_t* w, const float
 //   E4M3_RNE(x * 2**-E) saturated at +-448 (the product is exact in fp32; the clamp
 //   comes before the converter, which rounds to nearest even), 32 code bytes, one
 //   scale byte E + 127.
-//   MXFP4 and NVFP4 (the activation pass without the low-rank term): the encodes of
-//   the row-per-lane pass (one MX block and its scale byte, or two NVFP4 blocks of 16
-//   and their two E4M3 scale bytes), 16 code bytes.
-constexpr int kBlkMXFP4 = 0, kBlkNVFP4 = 1, kBlkMXFP8 = 2;
+//   MXFP4: E = floor(log2 amax) - 2, codes E2M1_RNE(x * 2**-E) by the hardware
+//   converter, 16 code bytes, one scale byte.
+constexpr int kBlkMXFP4 = 0, kBlkMXFP8 = 2;
 template <int KIND>
 __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t K, int64_t sr, int64_t sk,
                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                         int64_t nblk, int64_t q, float s_t, float d6) {
+                                         int64_t nblk, int64_t q) {
   const int64_t r = q / nblk, b = q % nblk;
   const uint16_t* src = x + r * sr + b * 32 * sk;
   uint32_t w[16];
@@ -154,13 +150,6 @@ __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) w[j] = (uint32_t)src[2 * j * sk] | ((uint32_t)src[(2 * j + 1) * sk] << 16);
-  }
-  if (KIND == kBlkNVFP4) {
-    u32x4 c;
-    const uint32_t sc = nv_encode32(w, s_t, d6, &c);
-    st16(codes + r * (K >> 1) + b * 16, c);
-    *reinterpret_cast<uint16_t*>(scales + r * (2 * nblk) + 2 * b) = (uint16_t)sc;
-    return;
   }
   const uint32_t amax = bf16_amax_bits<16>(w);
   if (KIND == kBlkMXFP4) {
@@ -194,34 +183,26 @@ __device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t
   scales[r * nblk + b] = (uint8_t)(E + 127);
 }
 
-// amax_t: NVFP4's tensor amax (the tensor scale is derived from it), else unused.
 template <int KIND>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                       int64_t K, int64_t sr, int64_t sk,
                                                       uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ amax_t) {
-  float s_t = 1.0f, d6 = 6.0f;
-  if (KIND == kBlkNVFP4) {
-    s_t = nv_tensor_scale(*amax_t);
-    d6 = 6.0f * s_t;
-  }
+                                                      uint8_t* __restrict__ scales) {
   const int64_t nblk = K >> 5, work = rows * nblk;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += (int64_t)gridDim.x * blockDim.x)
-    mx_block<KIND>(x, K, sr, sk, codes, scales, nblk, q, s_t, d6);
+    mx_block<KIND>(x, K, sr, sk, codes, scales, nblk, q);
 }
 
 // Launch of mx_rows_kernel: one thread per block, the grid capped (the threads
 // then stride over the blocks).
 template <int KIND>
 static hipError_t queue_mx_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t sr, int64_t sk,
-                                uint8_t* codes, uint8_t* scales, hipStream_t s,
-                                const float* amax_t = nullptr) {
+                                uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const int64_t work = rows * (K >> 5);
   if (work == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, int64_t(1) << 20);
   hipLaunchKernelGGL(mx_rows_kernel<KIND>, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, sr, sk, codes,
-                     scales, amax_t);
+                     scales);
   return hipGetLastError();
 }
 
@@ -230,7 +211,158 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t rows, int64_t K, int64_t
   return queue_mx_rows<kBlkMXFP8>(x, rows, K, sr, sk, codes, scales, s);
 }
 
-// ---------------------------------------------------------------------------- activation pass
+// ---------------------------------------------------------------------------- NVFP4 tensor amax
+// NVFP4 needs the tensor's largest magnitude before any block can be encoded, so
+// its pass is two launches: nv_amax_kernel reduces |x| per workgroup and stores
+// the partial maxima (fp32 bit patterns, an order-preserving integer for
+// non-negative values) in a scratch array of at most kNvPartials words; every
+// workgroup of the encode launch reduces that array itself, in the same order,
+// so each derives the same s_t, and workgroup 0 stores s_t.  No atomics, no
+// clearing, no single-thread launch.
+
+// Largest of the n partial maxima, reduced by the whole workgroup (256 threads).
+__device__ __forceinline__ uint32_t reduce_partials(const uint32_t* __restrict__ partials, int n,
+                                                    uint32_t* lds4) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += 256) m = max(m, partials[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]));
+  __syncthreads();
+  return m;
+}
+
+// Partial max of |x| over a strided [rows, cols] bf16 matrix (element (r, c) at
+// x[r * sr + c * sc]); workgroup b stores its maximum's bits in partials[b].
+// Rows of 16-byte aligned, contiguous chunks are read 16 bytes at a time, four
+// loads in flight per thread.
+__global__ __launch_bounds__(256) void nv_amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                      int64_t cols, int64_t sr, int64_t sc,
+                                                      uint32_t* __restrict__ partials) {
+  __shared__ uint32_t part[4];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (sc == 1 && (cols & 7) == 0 && (sr & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    const int64_t per_row = cols >> 3, nq = rows * per_row;      // 16-byte chunks
+    const bool flat = sr == cols;
+    for (int64_t q = tid; q < nq; q += 4 * stride) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t qu = q + u * stride;
+        const int64_t off = flat ? qu * 8 : (qu / per_row) * sr + (qu % per_row) * 8;
+        v[u] = qu < nq ? ld16(x + off) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v[u])));
+    }
+  } else {
+    for (int64_t q = tid; q < rows * cols; q += stride) {
+      const int64_t r = q / cols, c = q % cols;
+      m = max(m, (uint32_t)(x[r * sr + c * sc] & 0x7FFFu));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = max(max(part[0], part[1]), max(part[2], part[3])) << 16;
+}
+
+// Grid of the amax launch: at most kNvPartials workgroups.
+static int nv_amax_grid(int64_t elems) {
+  const int64_t want = (elems / 8 + 1023) / 1024;              // about four chunks per thread
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kNvPartials, want));
+}
+
+static hipError_t queue_nv_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t sr, int64_t sc,
+                                uint32_t* partials, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(nv_amax_kernel, dim3(grid), dim3(256), 0, s, x, rows, cols, sr, sc, partials);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- NVFP4 encode
+// One 16-element block per thread and step (two steps in flight), consecutive
+// threads on consecutive blocks of a row: 32 bytes of X in, 8 bytes of codes and
+// one E4M3 scale byte out.  Any K that is a multiple of 16.  x is [rows, K] with
+// row stride ldx (a multiple of 8, 16-byte aligned base).
+__device__ __forceinline__ void nv_block16(const uint16_t* __restrict__ x, int64_t K, int64_t ldx,
+                                           int64_t nb, int64_t q, float s_t, float d6,
+                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                           const u32x4& lo, const u32x4& hi) {
+  const int64_t r = q / nb, b = q % nb;
+  const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const float amax = __uint_as_float(bf16_amax_bits<8>(w) << 16);
+  const uint32_t code = e4m3_code(amax / d6);
+  uint32_t c[2];
+  nv_encode16(w, e4m3_value(code) * s_t, c);
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2*>(codes + r * (K >> 1) + b * 8) = u32x2{c[0], c[1]};
+  scales[r * nb + b] = (uint8_t)code;
+}
+
+__global__ __launch_bounds__(256) void nv_encode_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int64_t K, int64_t ldx, uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales,
+                                                        const uint32_t* __restrict__ partials, int nparts,
+                                                        float* __restrict__ tensor_scale) {
+  __shared__ uint32_t lds4[4];
+  const float s_t = nv_tensor_scale(__uint_as_float(reduce_partials(partials, nparts, lds4)));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  const float d6 = 6.0f * s_t;
+  const int64_t nb = K >> 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if ((nb & 1) == 0) {
+    // a pair of blocks per thread: 64 bytes of X in, 16 code bytes and 2 scale bytes out
+    const int64_t np = nb >> 1, work = rows * np;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += stride) {
+      const int64_t r = q / np, p = q % np;
+      const uint16_t* src = x + r * ldx + p * 32;
+      uint32_t w[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = ld16(src + 8 * c);
+        w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
+      }
+      u32x4 c;
+      const uint32_t sc = nv_encode32(w, s_t, d6, &c);
+      st16(codes + r * (K >> 1) + p * 16, c);
+      *reinterpret_cast<uint16_t*>(scales + r * nb + 2 * p) = (uint16_t)sc;
+    }
+    return;
+  }
+  const int64_t work = rows * nb;
+  auto src = [&](int64_t q) { return x + (q / nb) * ldx + (q % nb) * 16; };
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += 2 * stride) {
+    const int64_t q1 = q + stride;
+    const uint16_t* p0 = src(q);
+    const u32x4 a0 = ld16(p0), a1 = ld16(p0 + 8);
+    u32x4 b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+    if (q1 < work) {
+      const uint16_t* p1 = src(q1);
+      b0 = ld16(p1);
+      b1 = ld16(p1 + 8);
+    }
+    nv_block16(x, K, ldx, nb, q, s_t, d6, codes, scales, a0, a1);
+    if (q1 < work) nv_block16(x, K, ldx, nb, q1, s_t, d6, codes, scales, b0, b1);
+  }
+}
+
+static hipError_t queue_nv_encode(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
+                                  uint8_t* scales, uint32_t* partials, int nparts, float* tensor_scale,
+                                  hipStream_t s) {
+  // one thread per pair of blocks (even block count) or per two blocks
+  const int64_t work = rows * (K >> 5) + (((K >> 4) & 1) ? rows : 0);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, int64_t(1) << 20));
+  hipLaunchKernelGGL(nv_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ldx, codes, scales,
+                     partials, nparts, tensor_scale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- fused pass with t = X L1
 // One pair of 32-element blocks per lane half: the 64 bytes of X of block `blk` of
 // `row` (zeros past M or K).
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t row, int64_t ldx,
@@ -255,9 +387,11 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
 template <int FMT, int R, bool SMOOTH = false>
 __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int rows,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax_t,
-    const uint16_t* __restrict__ l1t, float* __restrict__ t, const float* __restrict__ inv_s) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const uint32_t* __restrict__ partials,
+    int nparts, float* __restrict__ tensor_scale, const uint16_t* __restrict__ l1t, float* __restrict__ t,
+    const float* __restrict__ inv_s) {
   __shared__ float red[R > 0 ? kQWaves * 32 * 32 : 1];
+  __shared__ uint32_t lds4[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.x * rows;
@@ -268,9 +402,20 @@ __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
   const int64_t sbytes = FMT == 0 ? nblk : 2 * nblk;   // scale bytes per row
 
   float s_t = 1.0f, d6 = 6.0f;
-  if (FMT == 1) {
-    s_t = nv_tensor_scale(*amax_t);
+  if constexpr (FMT == 1) {
+    // the tensor scale from the amax launch's partial maxima (the first 256 threads
+    // reduce them); workgroup 0 stores it
+    uint32_t m = 0;
+    if (threadIdx.x < 256) {
+      for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, partials[i]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+      if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = m;
+    }
+    __syncthreads();
+    s_t = nv_tensor_scale(__uint_as_float(max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]))));
     d6 = 6.0f * s_t;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
   }
   v16f acc = {};
 
@@ -336,72 +481,10 @@ __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------- tensor amax
-__global__ void clear_f32_kernel(float* p) { *p = 0.0f; }
-
-__global__ void nv_finalize_kernel(float* p) { *p = nv_tensor_scale(*p); }
-
-// Largest |x| over a strided [rows, cols] bf16 matrix (element (r, c) at
-// x[r * sr + c * sc]), reduced per workgroup (wave shuffles, then LDS) and then
-// folded into *amax with one integer atomic max on the fp32 bit pattern per
-// workgroup (valid for non-negative values).
-constexpr int kAmaxBlocks = 1024;
-__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                   int64_t cols, int64_t sr, int64_t sc,
-                                                   float* amax) {
-  __shared__ uint32_t part[4];
-  uint32_t m = 0;
-  const int64_t total = rows * cols;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  if (sc == 1 && (cols & 31) == 0 && (sr & 7) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-    // 64 bytes per thread per step, two steps (eight 16-byte loads) in flight
-    const int64_t per_row = cols >> 5, nq = rows * per_row;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += 2 * stride) {
-      u32x4 v[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t qu = q + u * stride;
-        const int64_t r = qu / per_row, c = qu % per_row;
-        const uint16_t* src = x + r * sr + c * 32;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[u][j] = qu < nq ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m = max(m, bf16_amax_bits<4>(reinterpret_cast<const uint32_t*>(&v[u][j])));
-    }
-  } else {
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
-      const int64_t r = q / cols, c = q % cols;
-      m = max(m, (uint32_t)(x[r * sr + c * sc] & 0x7FFFu));
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = max(max(part[0], part[1]), max(part[2], part[3]));
-    if (m != 0) atomicMax(reinterpret_cast<unsigned int*>(amax), m << 16);
-  }
-}
-
-static hipError_t queue_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t sr,
-                                    int64_t sc, float* amax, hipStream_t s) {
-  hipLaunchKernelGGL(clear_f32_kernel, dim3(1), dim3(1), 0, s, amax);
-  const int64_t work = (rows * cols + 31) / 32;
-  int64_t blocks = (work + 255) / 256;
-  if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, sr, sc, amax);
-  return hipGetLastError();
-}
-
 template <int FMT, int R, bool SMOOTH = false>
 static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
-                        uint8_t* scales, const float* amax, const uint16_t* l1t, float* t,
-                        hipStream_t s, const float* inv_s = nullptr) {
+                        uint8_t* scales, const uint32_t* partials, int nparts, float* tensor_scale,
+                        const uint16_t* l1t, float* t, hipStream_t s, const float* inv_s = nullptr) {
   // rows per workgroup: the fewest rounds of workgroups over the CUs with at most 32
   // rows each (M = 4608 on 256 CUs: 18 rows, one workgroup per CU)
   int cus = 256;
@@ -415,42 +498,34 @@ static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   const int rows = (int)std::max<int64_t>(1, (M + cus * waves - 1) / (cus * waves));
   const unsigned grid = (unsigned)((M + rows - 1) / rows);
   hipLaunchKernelGGL((quant_act_kernel<FMT, R, SMOOTH>), dim3(grid), dim3(kQWaves * 64), 0, s, x, M, K, ldx,
-                     rows, codes, scales, amax, l1t, t, inv_s);
+                     rows, codes, scales, partials, nparts, tensor_scale, l1t, t, inv_s);
 }
 
 hipError_t launch_quantize_act(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                const uint16_t* l1t, int r, float* t, hipStream_t s,
-                               const float* inv_s) {
+                               uint32_t* nv_scratch, const float* inv_s) {
   if (fmt == 0 && inv_s != nullptr) {
-    if (r == 0) queue_quant<0, 0, true>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s, inv_s);
-    else if (r == 16) queue_quant<0, 16, true>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s, inv_s);
-    else queue_quant<0, 32, true>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s, inv_s);
+    if (r == 0) queue_quant<0, 0, true>(x, M, K, ldx, codes, scales, nullptr, 0, nullptr, l1t, t, s, inv_s);
+    else if (r == 16) queue_quant<0, 16, true>(x, M, K, ldx, codes, scales, nullptr, 0, nullptr, l1t, t, s, inv_s);
+    else queue_quant<0, 32, true>(x, M, K, ldx, codes, scales, nullptr, 0, nullptr, l1t, t, s, inv_s);
     return hipGetLastError();
   }
-  if (fmt == 1) {
-    hipError_t e = queue_tensor_amax(x, M, K, ldx, 1, tensor_scale, s);
-    if (e != hipSuccess) return e;
-  }
   if (fmt == 0) {
-    // without the low-rank term, one thread per block: the row-per-lane layout only
-    // serves the MFMA of t = X L1
-    if (r == 0) {
-      const hipError_t e = queue_mx_rows<kBlkMXFP4>(x, M, K, ldx, 1, codes, scales, s);
-      if (e != hipSuccess) return e;
-    }
-    else if (r == 16) queue_quant<0, 16>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
-    else queue_quant<0, 32>(x, M, K, ldx, codes, scales, nullptr, l1t, t, s);
-  } else {
-    if (r == 0) {
-      const hipError_t e = queue_mx_rows<kBlkNVFP4>(x, M, K, ldx, 1, codes, scales, s, tensor_scale);
-      if (e != hipSuccess) return e;
-    } else if (r == 16) queue_quant<1, 16>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
-    else queue_quant<1, 32>(x, M, K, ldx, codes, scales, tensor_scale, l1t, t, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(nv_finalize_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
+    // without the low-rank term, one thread per block (no lane idles, every load
+    // instruction covers a contiguous 4 KB)
+    if (r == 0) return queue_mx_rows<kBlkMXFP4>(x, M, K, ldx, 1, codes, scales, s);
+    if (r == 16) queue_quant<0, 16>(x, M, K, ldx, codes, scales, nullptr, 0, nullptr, l1t, t, s);
+    else queue_quant<0, 32>(x, M, K, ldx, codes, scales, nullptr, 0, nullptr, l1t, t, s);
+    return hipGetLastError();
   }
+  // NVFP4: partial maxima into the scratch, then the encode launch
+  const int parts = nv_amax_grid(M * K);
+  const hipError_t e = queue_nv_amax(x, M, K, ldx, 1, nv_scratch, parts, s);
+  if (e != hipSuccess) return e;
+  if (r == 0) return queue_nv_encode(x, M, K, ldx, codes, scales, nv_scratch, parts, tensor_scale, s);
+  if (r == 16) queue_quant<1, 16>(x, M, K, ldx, codes, scales, nv_scratch, parts, tensor_scale, l1t, t, s);
+  else queue_quant<1, 32>(x, M, K, ldx, codes, scales, nv_scratch, parts, tensor_scale, l1t, t, s);
   return hipGetLastError();
 }
 
@@ -551,32 +626,44 @@ __device__ __forceinline__ void load_strided(const uint16_t* w, int64_t k0, int6
   }
 }
 
+// MXFP4: one thread per (column n, 32-element block).  NVFP4: one thread per
+// (column n, 16-element block), the tensor scale from the partial maxima of the
+// amax launch (reduced by every workgroup; workgroup 0 stores s_t).
 template <int FMT>
 __global__ __launch_bounds__(256) void pack_fp4_kernel(const uint16_t* __restrict__ w, int64_t K,
                                                        int64_t N, int64_t sk, int64_t sn,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
-                                                       const float* __restrict__ amax_t) {
+                                                       const uint32_t* __restrict__ partials, int nparts,
+                                                       float* __restrict__ tensor_scale) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nblk = K >> 5;
-  if (q >= N * nblk) return;
-  const int64_t n = q % N, blk = q / N;
-  uint32_t v[16];
-  load_strided(w, blk * 32, n, sk, sn, 32, v);
-  u32x4 c;
   if (FMT == 0) {
+    const int64_t nblk = K >> 5;
+    if (q >= N * nblk) return;
+    const int64_t n = q % N, blk = q / N;
+    uint32_t v[16];
+    load_strided(w, blk * 32, n, sk, sn, 32, v);
     const int E = mx_block_exponent(bf16_amax_bits<16>(v));
     const float sc = exp2i(E);
-    c = u32x4{fp4_encode8_pow2(v, sc), fp4_encode8_pow2(v + 4, sc), fp4_encode8_pow2(v + 8, sc),
-              fp4_encode8_pow2(v + 12, sc)};
+    st16(codes + n * (K >> 1) + blk * 16, u32x4{fp4_encode8_pow2(v, sc), fp4_encode8_pow2(v + 4, sc),
+                                                 fp4_encode8_pow2(v + 8, sc), fp4_encode8_pow2(v + 12, sc)});
     scales[n * nblk + blk] = (uint8_t)(E + 127);
-  } else {
-    const float s_t = nv_tensor_scale(*amax_t);
-    const uint32_t sc = nv_encode32(v, s_t, 6.0f * s_t, &c);
-    scales[n * 2 * nblk + 2 * blk] = (uint8_t)(sc & 0xFF);
-    scales[n * 2 * nblk + 2 * blk + 1] = (uint8_t)(sc >> 8);
+    return;
   }
-  st16(codes + n * (K >> 1) + blk * 16, c);
+  __shared__ uint32_t lds4[4];
+  const float s_t = nv_tensor_scale(__uint_as_float(reduce_partials(partials, nparts, lds4)));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  const int64_t nb = K >> 4;
+  if (q >= N * nb) return;
+  const int64_t n = q % N, blk = q / N;
+  uint32_t v[8];
+  load_strided(w, blk * 16, n, sk, sn, 16, v);
+  const uint32_t code = e4m3_code(__uint_as_float(bf16_amax_bits<8>(v) << 16) / (6.0f * s_t));
+  uint32_t c[2];
+  nv_encode16(v, e4m3_value(code) * s_t, c);
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2*>(codes + n * (K >> 1) + blk * 8) = u32x2{c[0], c[1]};
+  scales[n * nb + blk] = (uint8_t)code;
 }
 
 // Asymmetric int4, group 64: s = bf16(fp32(hi - lo) / 15) (1 if 0),
@@ -658,13 +745,13 @@ __global__ __launch_bounds__(256) void pack_int4_rows_kernel(const uint16_t* __r
 
 hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N, int64_t sk,
                                int64_t sn, uint8_t* codes, void* scales, uint16_t* zeros,
-                               float* tensor_scale, hipStream_t s) {
+                               float* tensor_scale, hipStream_t s, uint32_t* nv_scratch) {
   // K-contiguous rows with 16-byte alignment: the rows of W^T are quantized exactly
   // like activation rows (same blocks along K, same encoders), with vector loads
   const bool rows = sk == 1 && sn % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0;
   if (rows && fmt != 2)
     return launch_quantize_act(fmt, w, N, K, sn, codes, static_cast<uint8_t*>(scales), tensor_scale,
-                               nullptr, 0, nullptr, s);
+                               nullptr, 0, nullptr, s, nv_scratch);
   if (rows) {
     const int64_t work = N * (K >> 6);
     hipLaunchKernelGGL(pack_int4_rows_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, w,
@@ -677,21 +764,20 @@ hipError_t launch_pack_weights(int fmt, const uint16_t* w, int64_t K, int64_t N,
                        N, sk, sn, codes, static_cast<uint16_t*>(scales), zeros);
     return hipGetLastError();
   }
-  const int64_t work = N * (K >> 5);
-  const unsigned grid = (unsigned)((work + 255) / 256);
   if (fmt == 0) {
-    hipLaunchKernelGGL(pack_fp4_kernel<0>, dim3(grid), dim3(256), 0, s, w, K, N, sk, sn, codes,
-                       static_cast<uint8_t*>(scales), nullptr);
+    const int64_t work = N * (K >> 5);
+    hipLaunchKernelGGL(pack_fp4_kernel<0>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, w, K, N,
+                       sk, sn, codes, static_cast<uint8_t*>(scales), nullptr, 0, nullptr);
     return hipGetLastError();
   }
-  // logical [K, N]: rows k (stride sk), columns n (stride sn)
-  hipError_t e = queue_tensor_amax(w, K, N, sk, sn, tensor_scale, s);
+  // NVFP4, logical [K, N]: rows k (stride sk), columns n (stride sn)
+  const int parts = nv_amax_grid(K * N);
+  const hipError_t e = queue_nv_amax(w, K, N, sk, sn, nv_scratch, parts, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pack_fp4_kernel<1>, dim3(grid), dim3(256), 0, s, w, K, N, sk, sn, codes,
-                     static_cast<uint8_t*>(scales), tensor_scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nv_finalize_kernel, dim3(1), dim3(1), 0, s, tensor_scale);
+  const int64_t work = N * (K >> 4);
+  hipLaunchKernelGGL(pack_fp4_kernel<1>, dim3((unsigned)std::max<int64_t>(1, (work + 255) / 256)), dim3(256),
+                     0, s, w, K, N, sk, sn, codes, static_cast<uint8_t*>(scales), nv_scratch, parts,
+                     tensor_scale);
   return hipGetLastError();
 }
 

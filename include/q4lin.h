@@ -54,7 +54,8 @@ typedef enum q4_status {
   Q4_ERR_SHAPE = 2,   /* negative size, K not a multiple of the block, bad rank/stride */
   Q4_ERR_ALIGN = 3,   /* a pointer or leading dimension breaks the stated alignment   */
   Q4_ERR_FORMAT = 4,  /* format not valid for this call                              */
-  Q4_ERR_LAUNCH = 5   /* the HIP runtime rejected a kernel launch                    */
+  Q4_ERR_LAUNCH = 5,  /* the HIP runtime rejected a kernel launch                    */
+  Q4_ERR_ALLOC = 6    /* the library's one scratch allocation (NVFP4, see below) failed */
 } q4_status;
 
 typedef enum q4_format {

@@ -205,25 +205,41 @@ INT4_QMAX, INT4_QMIN = 7, -8
 INT4_SCALE_FLOOR = np.float32(1e-8)
 
 
+def _nearest_int_half_even(v):
+    """Nearest integer to each fp32 value, ties to the even integer, written out from
+    the definition: the integer below, plus one when the fraction is over a half or
+    exactly a half above an odd integer.  fp32 values of magnitude 2**23 and more are
+    integers already."""
+    v = np.asarray(v, dtype=np.float64)                               # exact copy of fp32
+    lo = np.floor(v)
+    frac = v - lo                                                     # exact: |v| < 2**53
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(lo, 2.0) == 1.0))
+    return lo + up
+
+
 def int4_sym_quantize(bits):
-    """Signed int4, symmetric, one fp32 scale per row (per output channel for a
-    weight stored [N, K], per token for an activation), the per-channel quantizer of
-    the SVDQuant Guide's "Step 1: Low-Rank Outlier Decomposition in PyTorch":
+    """Signed int4 with one fp32 step per row (the Q4_INT4_SYM format; the
+    per-channel quantizer of the SVDQuant Guide, "Step 1: Low-Rank Outlier
+    Decomposition in PyTorch", taken per row for both operands).
 
-        scale = max(fp32(amax / 7), 1e-8)                   amax over the row's K values
-        q     = clamp(RNE(fp32(x / scale)), -8, 7)          RNE: half to even (torch.round)
-
-    Each step is taken in fp32 (the bf16 inputs are exact there).  Codes are the
-    two's-complement low 4 bits, packed two per byte with the even k in the low
-    nibble.  Returns (codes uint8 [rows, K/2], scales float32 [rows]).
+    A row is represented as q * step with integer codes q in [-8, 7].  The step
+    maps the row's largest magnitude onto the largest positive code:
+    step = fp32(amax / 7), and no smaller than 1e-8 (an all-zero row gets the floor).
+    Each element's code is the integer nearest to the fp32 quotient fp32(x / step),
+    ties to even, limited to the code range; since |x| <= amax = 7 step, only -7 ..
+    7 occur.  Codes are stored as two's-complement nibbles, two per byte, even k in
+    the low nibble.  Returns (codes uint8 [rows, K/2], steps float32 [rows]).
     """
     bits = _rows(bits, 2)
     x = bf16_to_f32(bits)
     check_finite(x, "activation/weight")
-    amax = np.abs(x).max(axis=1)                                      # fp32, exact
-    scale = np.maximum(amax / np.float32(INT4_QMAX), INT4_SCALE_FLOOR)  # fp32 division
-    q = np.clip(np.rint(x / scale[:, None]), INT4_QMIN, INT4_QMAX)    # fp32 division, RNE
-    return pack_nibbles((q.astype(np.int64) & 0xF).astype(np.uint8)), scale.astype(np.float32)
+    amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    step = (amax / np.float32(INT4_QMAX)).astype(np.float32)          # fp32 division
+    step = np.where(step < INT4_SCALE_FLOOR, INT4_SCALE_FLOOR, step).astype(np.float32)
+    quot = (x / step[:, None]).astype(np.float32)                     # fp32 division
+    q = _nearest_int_half_even(quot)
+    q = np.minimum(np.maximum(q, INT4_QMIN), INT4_QMAX).astype(np.int64)
+    return pack_nibbles((q & 0xF).astype(np.uint8)), step
 
 
 def int4_sym_dequantize(codes, scales):

@@ -50,7 +50,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib()
-    names = ["Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN", "Q4_ERR_FORMAT", "Q4_ERR_LAUNCH"]
+    names = ["Q4_OK", "Q4_ERR_NULL", "Q4_ERR_SHAPE", "Q4_ERR_ALIGN", "Q4_ERR_FORMAT", "Q4_ERR_LAUNCH",
+             "Q4_ERR_ALLOC"]
     for i, n in enumerate(names):
         assert B.status_string(i) == n
     assert B.status_string(77) == "unknown"
@@ -72,6 +73,10 @@ def test_quantize_act_rejections():
     assert qa(fmt=1, ts=None) == B.Q4_ERR_NULL          # NVFP4 needs the tensor scale
     assert qa(r=32, l1t=OK16, t=None) == B.Q4_ERR_NULL
     assert qa(K=48, ldx=48) == B.Q4_ERR_SHAPE            # K not a multiple of 32
+    assert qa(fmt=1, ts=OK16, K=40, ldx=40) == B.Q4_ERR_SHAPE   # NVFP4: K not a multiple of 16
+    # NVFP4 with the fused t reads 32 elements at a time
+    assert qa(fmt=1, ts=OK16, K=48, ldx=48, r=16, l1t=OK16, t=OK16) == B.Q4_ERR_SHAPE
+    assert qa(ldx=(1 << 26) + 8) == B.Q4_ERR_SHAPE       # past the quantizer's 32-bit row offsets
     assert qa(M=-1) == B.Q4_ERR_SHAPE
     assert qa(ldx=128) == B.Q4_ERR_SHAPE                 # ldx < K
     assert qa(r=8, l1t=OK16, t=OK16) == B.Q4_ERR_SHAPE   # rank not 0/16/32
@@ -192,7 +197,9 @@ def test_gemm_w4a4_rejections():
     assert gw(ac=None) == B.Q4_ERR_NULL
     assert gw(y=None) == B.Q4_ERR_NULL
     assert gw(fmt=1) == B.Q4_ERR_NULL                    # NVFP4 without tensor scales
-    assert gw(K=96) == B.Q4_ERR_SHAPE                    # K not a multiple of 128
+    assert gw(K=80) == B.Q4_ERR_SHAPE                    # MXFP4: K not a multiple of 32
+    assert gw(fmt=1, ats=OK16, bts=OK16, K=24) == B.Q4_ERR_SHAPE   # NVFP4: K not a multiple of 16
+    assert gw(fmt=3, asc=OK16, bsc=OK16, K=96) == B.Q4_ERR_SHAPE  # INT4: K not a multiple of 128
     assert gw(N=-2) == B.Q4_ERR_SHAPE
     assert gw(ldy=100) == B.Q4_ERR_SHAPE
     assert gw(K=(1 << 22) + 128) == B.Q4_ERR_SHAPE        # past the 32-bit tile offsets
@@ -216,6 +223,7 @@ def test_gemm_w4a4_lowrank_rejections():
                                    a["K"], t, l2t, r, None, OK16, 256, 0, None)
 
     assert call(r=24) == B.Q4_ERR_SHAPE
+    assert call(K=80) == B.Q4_ERR_SHAPE
     assert call(t=None) == B.Q4_ERR_NULL
     assert call(l2t=ODD) == B.Q4_ERR_ALIGN
     assert call(fmt=9) == B.Q4_ERR_FORMAT
@@ -247,4 +255,6 @@ def test_gemm_w4a16_and_pack_rejections():
     assert pw(sk=0) == B.Q4_ERR_SHAPE
     assert pw(K=-32) == B.Q4_ERR_SHAPE
     assert pw(fmt=4, K=48) == B.Q4_ERR_SHAPE
+    assert pw(fmt=1, ts=OK16, K=40) == B.Q4_ERR_SHAPE    # NVFP4: K not a multiple of 16
+    assert pw(fmt=0, K=48) == B.Q4_ERR_SHAPE             # MXFP4: K not a multiple of 32
     assert pw(fmt=4, sk=0) == B.Q4_ERR_SHAPE

@@ -119,14 +119,19 @@ def test_quantize_nv_wide_dynamic_range():
     assert np.array_equal(u8(g["codes"]), codes)
 
 
-def test_quantize_nv_full_qkv_sampled_rows():
+@pytest.mark.parametrize("step", range(8))
+def test_quantize_nv_full_qkv_sampled_rows(step):
+    """The fused-QKV activations at 2048^2 for each of the 8 denoising steps, each
+    with its own outlier channel set: the tensor scale and the sampled rows' codes
+    and block scales bit-exact."""
     dev = device()
-    d = synth.qkv_nvfp4(step=3)
+    d = synth.qkv_nvfp4(step=step)
     x = d["x"]
-    say("quantize_act nvfp4 16896x3072 (QKV activations, one denoising step)")
+    say(f"quantize_act nvfp4 16896x3072 (QKV activations, denoising step {step})")
     g = quantize("nvfp4", x, dev)
     amax_t = np.abs(F.bf16_to_f32(x)).max()
-    rows = np.unique(np.concatenate([[0, x.shape[0] - 1], np.random.default_rng(2).choice(x.shape[0], 254)]))
+    rows = np.unique(np.concatenate([[0, x.shape[0] - 1],
+                                     np.random.default_rng(2 + step).choice(x.shape[0], 126)]))
     codes, sb, st = Q.nv_quantize(x[rows], amax_t=amax_t)
     assert float(g["ts"].item()) == float(st)
     assert np.array_equal(u8(g["scales"])[rows], sb)
