@@ -28,6 +28,7 @@ _I64 = _c.c_int64
 _I32 = _c.c_int32
 SIGNATURES = {
     "quantize_act": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P]),
+    "quantize_act_noalloc": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P]),
     "quantize_act_smooth": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _P]),
     "pack_weights": (_c.c_int, [_c.c_int, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "gemm_w4a4": (_c.c_int, [_c.c_int, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I64,
@@ -186,6 +187,24 @@ def quantize_act(fmt, x, codes, scales, tensor_scale=None, l1t=None, t=None, str
     st = load().quantize_act(_fmt(fmt), _ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(scales),
                              _ptr(tensor_scale), _ptr(l1t), r, _ptr(t), _stream(stream))
     _check("quantize_act", st)
+
+
+def quantize_act_noalloc(fmt, x, codes, scales, tensor_scale=None, l1t=None, t=None, stream=None):
+    """quantize_act through the entry point that allocates nothing (its NVFP4 scratch
+    is a static device array shared by every call on the GPU)."""
+    _rowmajor(x, "x")
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    f = _fmt(fmt)
+    dev = _device(x, "x")
+    _strided(x, "x", (torch.bfloat16,), M, K, dev)
+    _operand(f, codes, scales, tensor_scale, M, K, dev, "x")
+    if r:
+        _packed(l1t, "l1t", torch.bfloat16, r, K, dev)
+        _packed(t, "t", torch.float32, M, r, dev)
+    st = load().quantize_act_noalloc(f, _ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(scales),
+                                     _ptr(tensor_scale), _ptr(l1t), r, _ptr(t), _stream(stream))
+    _check("quantize_act_noalloc", st)
 
 
 def quantize_act_smooth(fmt, x, inv_s, codes, scales, l1t=None, t=None, stream=None):

@@ -9,6 +9,12 @@
 
 #include "q4_internal.h"
 
+// Scratch of quantize_act_noalloc: the NVFP4 partial maxima in a static device
+// array, q4::kNvScratchWords words (4 KB) on every GPU the library runs on, held
+// until the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device memory: only the address static_scratch() looks up is passed on.
+static __device__ __align__(256) uint32_t scratch[q4::kNvScratchWords];
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -42,6 +48,22 @@ uint32_t* nv_stream_scratch(void* stream) {
   return static_cast<uint32_t*>(p);
 }
 
+// The array's device address on the current device, looked up once per device
+// (with that device current) on its first call there.  Null if the lookup fails.
+uint32_t* static_scratch() {
+  static std::mutex mu;
+  static std::map<int, uint32_t*> addr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = addr.find(dev);
+  if (it != addr.end()) return it->second;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  addr.emplace(dev, static_cast<uint32_t*>(p));
+  return static_cast<uint32_t*>(p);
+}
+
 // K granularity of the W4A4 GEMMs: the block of MXFP4 (32) and NVFP4 (16); the
 // INT4 and MXFP8 kernels step K in tiles of 128.
 int64_t gemm_k_unit(q4_format fmt) { return fmt == Q4_MXFP4 ? 32 : (fmt == Q4_NVFP4 ? 16 : 128); }
@@ -64,6 +86,40 @@ q4_status check_w4a4(q4_format fmt, const uint8_t* a_codes, const uint8_t* a_sca
   return Q4_OK;
 }
 
+// quantize_act and quantize_act_noalloc: the same checks and launches; they differ
+// only in where the NVFP4 partial maxima live.
+q4_status quantize_act_impl(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            uint8_t* codes, uint8_t* scales, float* tensor_scale, const uint16_t* l1t,
+                            int32_t r, float* t, void* stream, bool noalloc) {
+  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8) return Q4_ERR_FORMAT;
+  if ((fmt == Q4_INT4_SYM || fmt == Q4_MXFP8) && r != 0) return Q4_ERR_FORMAT;
+  // NVFP4 blocks are 16 wide; with the fused t the pass reads 32 at a time
+  const int64_t unit = (fmt == Q4_NVFP4 && r == 0) ? 16 : 32;
+  if (M < 0 || K < 0 || (K % unit) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
+  if (M > kMaxRows || K > kMaxK || ldx > kMaxLdx) return Q4_ERR_SHAPE;
+  if (!x || !codes || !scales) return Q4_ERR_NULL;
+  if (fmt == Q4_NVFP4 && !tensor_scale) return Q4_ERR_NULL;
+  if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
+  if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(codes, 16) || !aligned(scales, 4))
+    return Q4_ERR_ALIGN;
+  if (fmt == Q4_NVFP4 && !aligned(tensor_scale, 4)) return Q4_ERR_ALIGN;
+  if (r > 0 && (!aligned(l1t, 16) || !aligned(t, 16))) return Q4_ERR_ALIGN;
+  if (M == 0) return Q4_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt == Q4_INT4_SYM)
+    return launched(q4::launch_int4_sym_rows(x, M, K, ldx, 1, codes, reinterpret_cast<float*>(scales), s));
+  if (fmt == Q4_MXFP8) return launched(q4::launch_mxfp8_rows(x, M, K, ldx, 1, codes, scales, s));
+  uint32_t* scr = nullptr;
+  if (fmt == Q4_NVFP4) {
+    // the amax launch never has more workgroups than the scratch has words, so
+    // every size fits either scratch
+    scr = noalloc ? static_scratch() : nv_stream_scratch(stream);
+    if (scr == nullptr) return noalloc ? Q4_ERR_LAUNCH : Q4_ERR_ALLOC;
+  }
+  return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t, (int)r,
+                                          t, s, scr));
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,28 +140,13 @@ const char* q4_status_string(q4_status s) {
 q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                        uint8_t* codes, uint8_t* scales, float* tensor_scale,
                        const uint16_t* l1t, int32_t r, float* t, void* stream) {
-  if (fmt != Q4_MXFP4 && fmt != Q4_NVFP4 && fmt != Q4_INT4_SYM && fmt != Q4_MXFP8) return Q4_ERR_FORMAT;
-  if ((fmt == Q4_INT4_SYM || fmt == Q4_MXFP8) && r != 0) return Q4_ERR_FORMAT;
-  // NVFP4 blocks are 16 wide; with the fused t the pass reads 32 at a time
-  const int64_t unit = (fmt == Q4_NVFP4 && r == 0) ? 16 : 32;
-  if (M < 0 || K < 0 || (K % unit) != 0 || ldx < K || !rank_ok(r)) return Q4_ERR_SHAPE;
-  if (M > kMaxRows || K > kMaxK || ldx > kMaxLdx) return Q4_ERR_SHAPE;
-  if (!x || !codes || !scales) return Q4_ERR_NULL;
-  if (fmt == Q4_NVFP4 && !tensor_scale) return Q4_ERR_NULL;
-  if (r > 0 && (!l1t || !t)) return Q4_ERR_NULL;
-  if (!aligned(x, 16) || (ldx % 8) != 0 || !aligned(codes, 16) || !aligned(scales, 4))
-    return Q4_ERR_ALIGN;
-  if (fmt == Q4_NVFP4 && !aligned(tensor_scale, 4)) return Q4_ERR_ALIGN;
-  if (r > 0 && (!aligned(l1t, 16) || !aligned(t, 16))) return Q4_ERR_ALIGN;
-  if (M == 0) return Q4_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fmt == Q4_INT4_SYM)
-    return launched(q4::launch_int4_sym_rows(x, M, K, ldx, 1, codes, reinterpret_cast<float*>(scales), s));
-  if (fmt == Q4_MXFP8) return launched(q4::launch_mxfp8_rows(x, M, K, ldx, 1, codes, scales, s));
-  uint32_t* scratch = nullptr;
-  if (fmt == Q4_NVFP4 && (scratch = nv_stream_scratch(stream)) == nullptr) return Q4_ERR_ALLOC;
-  return launched(q4::launch_quantize_act((int)fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t, (int)r,
-                                          t, s, scratch));
+  return quantize_act_impl(fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t, r, t, stream, false);
+}
+
+q4_status quantize_act_noalloc(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                               const uint16_t* l1t, int32_t r, float* t, void* stream) {
+  return quantize_act_impl(fmt, x, M, K, ldx, codes, scales, tensor_scale, l1t, r, t, stream, true);
 }
 
 q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

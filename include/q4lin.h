@@ -131,6 +131,25 @@ Q4_API q4_status quantize_act(q4_format fmt, const uint16_t* x, int64_t M, int64
                        const uint16_t* l1t, int32_t r, float* t, void* stream);
 
 /*
+ * quantize_act_noalloc -- quantize_act for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results, checks and status codes are those of
+ * quantize_act, and it allocates nothing.  The only scratch quantize_act uses --
+ * NVFP4's 1024 per-workgroup partial maxima of the tensor amax, 4 KB -- lives
+ * here in a static device array of that size on each GPU the library runs on,
+ * held until the process ends; every input size fits it (the amax launch never
+ * uses more workgroups than it has words), so no size is rejected for it.  Its
+ * device address is looked up once per device on the first call there
+ * (Q4_ERR_LAUNCH if that lookup fails).  All calls on one GPU share the array:
+ * NVFP4 calls that overlap on one GPU (different streams, no ordering) race and
+ * must be ordered by the caller.  MXFP4, INT4_SYM and MXFP8 use no scratch.
+ */
+Q4_API q4_status quantize_act_noalloc(q4_format fmt, const uint16_t* x, int64_t M, int64_t K,
+                                      int64_t ldx, uint8_t* codes, uint8_t* scales,
+                                      float* tensor_scale, const uint16_t* l1t, int32_t r, float* t,
+                                      void* stream);
+
+/*
  * quantize_act_smooth -- quantize_act with SmoothQuant pre-conditioning of the
  * activation: each element is divided by its channel's smoothing factor s_j
  * before quantization (SVDQuant Guide, "2. SmoothQuant Pre-Conditioning for DiTs":

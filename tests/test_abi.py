@@ -65,6 +65,22 @@ def qa(**kw):
                               a["ts"], a["l1t"], a["r"], a["t"], None)
 
 
+def test_quantize_act_noalloc_checks_like_quantize_act():
+    """The allocation-free entry point runs the same host checks (nothing here
+    reaches the device)."""
+    L = lib()
+    cases = [dict(fmt=7), dict(x=None), dict(fmt=1, ts=None), dict(K=48, ldx=48),
+             dict(fmt=1, ts=OK16, K=40, ldx=40), dict(ldx=128), dict(r=8, l1t=OK16, t=OK16),
+             dict(x=ODD), dict(M=0), dict(fmt=1, ts=OK16, M=0)]
+    for kw in cases:
+        a = dict(fmt=0, x=OK16, M=64, K=256, ldx=256, codes=OK16, scales=OK16, ts=None, l1t=None, r=0,
+                 t=None)
+        a.update(kw)
+        args = (a["fmt"], a["x"], a["M"], a["K"], a["ldx"], a["codes"], a["scales"], a["ts"], a["l1t"],
+                a["r"], a["t"], None)
+        assert L.quantize_act_noalloc(*args) == L.quantize_act(*args), kw
+
+
 def test_quantize_act_rejections():
     assert qa(fmt=2) == B.Q4_ERR_FORMAT
     assert qa(fmt=7) == B.Q4_ERR_FORMAT
