@@ -5,7 +5,8 @@
 // are few, half tiles of 256 x 128 (128 x 64 per wave, F = 2 weight sub-tiles
 // instead of 4).  K advances in tiles of 64
 // elements: each operand tile is 256 rows x 64 bf16 (128 bytes per row) in LDS,
-// 16-byte chunks XOR-swizzled by row, two stages, one barrier per K-tile.
+// 16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ lds_swz<8>(r), for the
+// 64-bank LDS), two stages, one barrier per K-tile.
 //
 // A loader policy turns global data into bf16 LDS rows:
 //   Loader::issue_regs(kt)            issue the global reads of K-tile kt that land
@@ -34,7 +35,7 @@ constexpr int kBf16TileBytes = kBf16BM * kBf16RowBytes;      // one operand tile
 constexpr int kBf16MainLds = 4 * kBf16TileBytes;             // [A0][A1][B0][B1]
 
 __device__ __forceinline__ int lds_chunk_off(int row, int chunk) {
-  return row * kBf16RowBytes + ((chunk ^ (row & 7)) << 4);
+  return row * kBf16RowBytes + ((chunk ^ lds_swz<8>(row)) << 4);
 }
 
 template <int F>
@@ -43,13 +44,13 @@ struct Bf16Frags {
 };
 
 // fragments of MFMA step s (16 K) of the tile at la / lb into buffer BUF.  Rows
-// 32 g + r32 all have row & 7 == lane & 7, so one swizzled chunk offset per step
-// serves every sub-tile; the sub-tiles are 4 KB apart.
+// 32 g + r32 all have the swizzle lds_swz<8>(r32), so one swizzled chunk offset per
+// step serves every sub-tile; the sub-tiles are 4 KB apart.
 template <int BUF, int F>
 __device__ __forceinline__ void bf16_read_frags(Bf16Frags<F>& fr, const uint8_t* la, const uint8_t* lb,
                                                 int s, int wx, int wy, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
-  const int chunk = ((2 * s + h) ^ (lane & 7)) << 4;
+  const int chunk = ((2 * s + h) ^ lds_swz<8>(r32)) << 4;
   const uint8_t* pa = la + (wx * 128 + r32) * kBf16RowBytes + chunk;
   const uint8_t* pb = lb + (wy * 32 * F + r32) * kBf16RowBytes + chunk;
 #pragma unroll

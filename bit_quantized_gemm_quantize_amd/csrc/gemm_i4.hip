@@ -75,20 +75,25 @@ __device__ __forceinline__ void i4_tile(uint8_t* lds_raw, const uint8_t* __restr
 
   // K-tile kt -> stage: each wave moves 64 activation and kRowsB weight rows, 8 rows
   // of 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding
-  // global chunk (i % 8) ^ (row & 7)); rows and blocks past the matrix read as zero
+  // global chunk (i % 8) ^ lds_swz<8>(row)); rows and blocks past the matrix read as zero
   const int lr = lane >> 3, lp = lane & 7;
   auto load_ktile = [&](int kt, int stage) {
-    const uint32_t blk = (uint32_t)kt * 8 + (lp ^ lr);
-    const uint32_t koff = blk < nblk ? blk * 16 : kOOB;
+    // row = 16 q + 8 (j % 2) + lr: its swizzle lds_swz<8>(row) is 4 (j % 2) + lr / 2
+    uint32_t koff[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t blk = (uint32_t)kt * 8 + (lp ^ (4 * jp + (lr >> 1)));
+      koff[jp] = blk < nblk ? blk * 16 : kOOB;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t row = 64 * wave + 8 * j + lr;
-      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kI4KTB], row * kbytes + koff);
+      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kI4KTB], row * kbytes + koff[j & 1]);
     }
 #pragma unroll
     for (int j = 0; j < kRowsB / 8; ++j) {
       const uint32_t row = kRowsB * wave + 8 * j + lr;
-      buf_ld16_lds(rc_b, &lds[1][stage][(kRowsB * wave + 8 * j) * kI4KTB], row * kbytes + koff);
+      buf_ld16_lds(rc_b, &lds[1][stage][(kRowsB * wave + 8 * j) * kI4KTB], row * kbytes + koff[j & 1]);
     }
   };
   // raw 16-byte fragments (32 codes), double-buffered across MFMA steps; widened to
@@ -98,12 +103,12 @@ __device__ __forceinline__ void i4_tile(uint8_t* lds_raw, const uint8_t* __restr
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int row = wm * 128 + 32 * g + r32;
-      fa[buf][g] = ld16(&lds[0][stage][row * kI4KTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+      fa[buf][g] = ld16(&lds[0][stage][row * kI4KTB + (((4 * h + s) ^ lds_swz<8>(row)) << 4)]);
     }
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int row = wn * 32 * F + 32 * f + r32;
-      fb[buf][f] = ld16(&lds[1][stage][row * kI4KTB + (((4 * h + s) ^ (row & 7)) << 4)]);
+      fb[buf][f] = ld16(&lds[1][stage][row * kI4KTB + (((4 * h + s) ^ lds_swz<8>(row)) << 4)]);
     }
   };
 

@@ -23,7 +23,7 @@
 // gemm_mx_kernel).
 //
 // LDS: the two operand tiles (256 rows x 128 bytes each) are stored with 16-byte
-// chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)), so the 16-byte
+// chunks XOR-swizzled by row (chunk c of row r at c ^ lds_swz<8>(r)), so the 16-byte
 // fragment reads are free of bank conflicts.  Tiles go from HBM/L2 straight into
 // LDS (buffer loads with the LDS destination, no staging registers; rows and
 // K blocks past the matrix read as zero).  Two LDS stages, one barrier per K-tile;
@@ -72,7 +72,7 @@ struct MxLoads {
   static constexpr int kRowsA = kBM / kWaves, kRowsB = kTN / kWaves;   // rows each wave loads
   // codes, global -> LDS: each wave moves 8 rows x 128 bytes per instruction straight
   // into LDS (lane i -> row i/8, stored position i%8, which holds global chunk
-  // (i%8) ^ (row & 7), the swizzle).  Wave w covers activation rows kRowsA w ..
+  // (i%8) ^ lds_swz<8>(row), the swizzle).  Wave w covers activation rows kRowsA w ..
   // +kRowsA-1 and weight rows kRowsB w .. +kRowsB-1: kNL instructions per K-tile,
   // issued in three parts (instructions [begin(p), begin(p+1))).
   static constexpr int kNA = kRowsA / 8, kNL = kNA + kRowsB / 8;

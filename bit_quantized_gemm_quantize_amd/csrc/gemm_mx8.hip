@@ -9,7 +9,7 @@
 // 128 x 128 as 4 x 4 MFMA tiles with fp32 accumulators in the matrix registers.
 // K advances in tiles of 128 elements (128 bytes per row, 4 scale bytes per row),
 // loaded straight into two LDS stages with the 16-byte chunks XOR-swizzled by row
-// (chunk c of row r at c ^ (r & 7)).  An MFMA step consumes 64 K elements, and
+// (chunk c of row r at c ^ lds_swz<8>(r), for the 64-bank LDS).  An MFMA step consumes 64 K elements, and
 // with 8-bit operands the instruction splits each 32-element block over the two
 // lane halves (measured on gfx950: lane half h holds K [16h, 16h+16) of the step
 // in its first 16 bytes and K [32+16h, 32+16h+16) in its last 16, and block b is
@@ -73,20 +73,25 @@ __device__ __forceinline__ void mx8_tile(
 
   // K-tile kt -> stage: each wave moves 64 activation and kRowsB weight rows, 8 rows
   // of 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding
-  // global chunk (i % 8) ^ (row & 7)); rows past the matrix read as zero
+  // global chunk (i % 8) ^ lds_swz<8>(row)); rows past the matrix read as zero
   const int lr = lane >> 3, lp = lane & 7;
   auto load_ktile = [&](int kt, int stage) {
-    const uint32_t chunk = (uint32_t)kt * 8 + (lp ^ lr);
-    const uint32_t koff = chunk < nchunk ? chunk * 16 : kOOB;
+    // row = 16 q + 8 (j % 2) + lr: its swizzle lds_swz<8>(row) is 4 (j % 2) + lr / 2
+    uint32_t koff[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t chunk = (uint32_t)kt * 8 + (lp ^ (4 * jp + (lr >> 1)));
+      koff[jp] = chunk < nchunk ? chunk * 16 : kOOB;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t row = 64 * wave + 8 * j + lr;
-      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff);
+      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kX8KTB], row * kbytes + koff[j & 1]);
     }
 #pragma unroll
     for (int j = 0; j < kRowsB / 8; ++j) {
       const uint32_t row = kRowsB * wave + 8 * j + lr;
-      buf_ld16_lds(rc_b, &lds[1][stage][(kRowsB * wave + 8 * j) * kX8KTB], row * kbytes + koff);
+      buf_ld16_lds(rc_b, &lds[1][stage][(kRowsB * wave + 8 * j) * kX8KTB], row * kbytes + koff[j & 1]);
     }
   };
   // the lane's scale dwords of K-tile kt (rows past the matrix, and K-tiles past K,
@@ -104,7 +109,7 @@ __device__ __forceinline__ void mx8_tile(
   auto frag = [&](int op, int stage, int row, int s) {
     const uint8_t* base = &lds[op][stage][row * kX8KTB];
     const int c = 4 * s + h;
-    const u32x4 lo = ld16(base + ((c ^ (row & 7)) << 4)), hi = ld16(base + (((c + 2) ^ (row & 7)) << 4));
+    const u32x4 lo = ld16(base + ((c ^ lds_swz<8>(row)) << 4)), hi = ld16(base + (((c + 2) ^ lds_swz<8>(row)) << 4));
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto read_frags = [&](int buf, int stage, int s) {

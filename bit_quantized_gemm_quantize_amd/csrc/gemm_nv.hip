@@ -65,17 +65,17 @@ struct NvLoader {
   // half P: both operands' chunks of row group P
   template <int P>
   __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb) {
-    // row (tid >> 1) + 128 P: row & 7 does not depend on P
+    // row (tid >> 1) + 128 P: its swizzle does not depend on P
     const int c = tid & 1, r = tid >> 1;
     const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
     u32x4 o[4];
     nv_dequant_chunk(ca[P], sa[P], o);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st16(la + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
+    for (int d = 0; d < 4; ++d) st16(la + off + (((4 * c + d) ^ lds_swz<8>(r)) << 4), o[d]);
     if (P < TN / 128) {
       nv_dequant_chunk(cb[P], sb[P], o);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ (r & 7)) << 4), o[d]);
+      for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ lds_swz<8>(r)) << 4), o[d]);
     }
   }
 };

@@ -28,7 +28,7 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
 // Per K-tile (one quantization group of 64 K): the activation tile (256 rows x 128
 // bytes of bf16) goes straight into LDS, each wave moving rows 64 w .. 64 w + 63 as
 // 8 rows x 128 bytes per instruction (lane i -> row i/8, stored position i%8, which
-// holds global chunk (i%8) ^ (row & 7)); the weight tile is TN rows x 2 chunks of
+// holds global chunk (i%8) ^ lds_swz<8>(row)); the weight tile is TN rows x 2 chunks of
 // 32 codes, thread tid owning chunk tid & 1 of rows tid/2 (and tid/2 + 128), with
 // each row's (s, z).  Reads past M / N / K return zeros.
 template <int TN>
@@ -59,8 +59,9 @@ struct W4A16Loader {
     const uint32_t lr = lane >> 3, lp = lane & 7;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t row = 64 * wave + 8 * j + lr;         // row & 7 == lr
-      const uint32_t off = in_range_or_oob(row * ldxb + (uint32_t)kt * 128 + ((lp ^ lr) << 4), (uint32_t)kt, ngrp);
+      const uint32_t row = 64 * wave + 8 * j + lr;         // lds_swz<8>(row) == 4 (j % 2) + lr / 2
+      const uint32_t off = in_range_or_oob(row * ldxb + (uint32_t)kt * 128 + ((lp ^ (4 * (j & 1) + (lr >> 1))) << 4),
+                                           (uint32_t)kt, ngrp);
       buf_ld16_lds(rx, la + (64 * wave + 8 * j) * kBf16RowBytes, off);
     }
   }
@@ -86,7 +87,7 @@ struct W4A16Loader {
     u32x4 o[4];
     int4_dequant_chunk(cb[P], sc, zs, o);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * cw + d) ^ (r & 7)) << 4), o[d]);
+    for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * cw + d) ^ lds_swz<8>(r)) << 4), o[d]);
   }
 };
 
