@@ -43,9 +43,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mx_traffic.json")
 KERNEL_SOURCES = ["gemm_mx.hip", "q4_epilogue.h", "q4_device.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "bit_quantized_gemm_quantize_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -92,6 +92,8 @@ def cpu_baseline(d, budget_s=12.0):
 
 
 GEMM_KERNEL_PREFIX = "void q4::gemm_mx_kernel<32, false, 0>"
+QUANT_KERNEL_PREFIX = "void q4::quant_act_kernel<0, 32, false>"
+QUANT_SOURCES = ["quant.hip", "q4_device.h"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 CAL_BYTES = 256 * 2 ** 20          # the calibration copy below: 64 Mi fp32 in, 64 Mi fp32 out
 
@@ -112,12 +114,13 @@ def timed_region_avg_ns(trace_csv, steps):
 
 
 def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None, steps=None,
-                       bench_log=None):
+                       bench_log=None, util_csv=None):
     """Turns the rocprofv3 outputs of a bench run (one --kernel-trace --stats run,
-    one --pmc FETCH_SIZE run, one --pmc WRITE_SIZE run) into the committed text
-    summary and the traffic record read by measured_traffic().  HBM bytes of the
-    GEMM are the counters' per-dispatch KiB, each scaled by the ratio of the bytes
-    the calibration copy really moves to what the same counter reports for it."""
+    one --pmc FETCH_SIZE run, one --pmc WRITE_SIZE run, and optionally one --pmc run
+    of the SQ/GRBM utilisation counters) into the committed text summary and the
+    traffic record read by measured_traffic().  HBM bytes of a kernel are the
+    counters' per-dispatch KiB, each scaled by the ratio of the bytes the
+    calibration copy really moves to what the same counter reports for it."""
     lines = [f"# rocprofv3 summary: MXFP4 W4A4 GEMM + low-rank epilogue, M={M} K={K} N={N} r={RANK}",
              "", "commands (R = the repository root; each run after `cd /tmp && export TMPDIR=/tmp`):", ""]
     lines += ["    " + c for c in command]
@@ -132,19 +135,21 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None,
         if name.startswith(GEMM_KERNEL_PREFIX):
             gemm_avg_ns = float(r["AverageNs"])
 
-    def per_dispatch(path, counter):
+    def per_dispatch(path, counter, prefix=GEMM_KERNEL_PREFIX):
         vals = {}
         for r in _csv_rows(path):
             if r["Counter_Name"] != counter:
                 continue
             vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
             vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        gemm = [v for k, d in vals.items() if k.startswith(GEMM_KERNEL_PREFIX) for v in d.values()]
+        kern = [v for k, d in vals.items() if k.startswith(prefix) for v in d.values()]
         cal = [v for k, d in vals.items() if k.startswith(COPY_KERNEL) for v in d.values()]
-        return float(np.mean(gemm)), float(np.max(cal))
+        return float(np.mean(kern)), float(np.max(cal))
 
     fetch_kib, cal_fetch_kib = per_dispatch(fetch_csv, "FETCH_SIZE")
     write_kib, cal_write_kib = per_dispatch(write_csv, "WRITE_SIZE")
+    q_fetch_kib, _ = per_dispatch(fetch_csv, "FETCH_SIZE", QUANT_KERNEL_PREFIX)
+    q_write_kib, _ = per_dispatch(write_csv, "WRITE_SIZE", QUANT_KERNEL_PREFIX)
     f_scale = CAL_BYTES / (cal_fetch_kib * 1024.0)
     w_scale = CAL_BYTES / (cal_write_kib * 1024.0)
     fetch_b, write_b = fetch_kib * 1024.0 * f_scale, write_kib * 1024.0 * w_scale
@@ -158,6 +163,48 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None,
               f"algorithmic bytes per launch: read {alg_in / 1e6:.2f} MB (A, B codes + scales, t, L2^T), "
               f"write {alg_out / 1e6:.2f} MB (Y bf16); measured / algorithmic = "
               f"{(fetch_b + write_b) / (alg_in + alg_out):.3f}"]
+    # the fused quantizer of the same step: reads X (bf16) and L1^T, writes codes,
+    # scales and t (fp32)
+    q_fetch_b, q_write_b = q_fetch_kib * 1024.0 * f_scale, q_write_kib * 1024.0 * w_scale
+    q_alg_in = M * K * 2 + K * RANK * 2
+    q_alg_out = M * K // 2 + M * K // 32 + M * RANK * 4
+    lines += ["", "## HBM traffic of the fused quantizer (same two --pmc runs)", "",
+              f"`{QUANT_KERNEL_PREFIX[5:]}` per dispatch: FETCH_SIZE {q_fetch_kib:.0f} KiB -> "
+              f"{q_fetch_b / 1e6:.2f} MB; WRITE_SIZE {q_write_kib:.0f} KiB -> {q_write_b / 1e6:.2f} MB", "",
+              f"algorithmic bytes per launch: read {q_alg_in / 1e6:.2f} MB (X bf16, L1^T), write "
+              f"{q_alg_out / 1e6:.2f} MB (codes, scales, t fp32); measured / algorithmic = "
+              f"{(q_fetch_b + q_write_b) / (q_alg_in + q_alg_out):.3f}"]
+    util = None
+    if util_csv:
+        # per dispatch: counters summed over the chip's instances.  SQ_BUSY_CYCLES sums
+        # over the 32 shader engines, SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs and
+        # GRBM_GUI_ACTIVE over the 8 XCDs (its window also spans the dispatch set-up).
+        acc = {}
+        for r in _csv_rows(util_csv):
+            if not r["Kernel_Name"].startswith(GEMM_KERNEL_PREFIX):
+                continue
+            d = acc.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        disp = [acc[k] for k in sorted(acc, key=int)][-max(1, len(acc) // 4):]
+        mean = {c: float(np.mean([d[c] for d in disp])) for c in disp[0]}
+        se_cycles = mean["SQ_BUSY_CYCLES"] / 32.0
+        mfma_simd = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0
+        grbm_xcd = mean["GRBM_GUI_ACTIVE"] / 8.0
+        util = {"mfma_busy_per_simd": mfma_simd, "sq_busy_cycles_per_se": se_cycles,
+                "grbm_gui_active_per_xcd": grbm_xcd,
+                "mfma_util_vs_sq_busy": mfma_simd / se_cycles,
+                "mfma_util_vs_grbm": mfma_simd / grbm_xcd,
+                "wait_any_frac": mean["SQ_WAIT_ANY"] / mean["SQ_WAVE_CYCLES"],
+                "lds_bank_conflict_per_active": mean["SQ_LDS_BANK_CONFLICT"] / max(mean["SQ_LDS_IDX_ACTIVE"], 1.0)}
+        lines += ["", "## MFMA utilisation of the GEMM (--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+                      "GRBM_GUI_ACTIVE SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT)", "",
+                  f"last {len(disp)} dispatches of {len(acc)}: MFMA busy {mfma_simd:.0f} cycles per SIMD "
+                  f"(SQ_VALU_MFMA_BUSY_CYCLES / 1024); shader-engine busy {se_cycles:.0f} cycles "
+                  f"(SQ_BUSY_CYCLES / 32); GPU busy {grbm_xcd:.0f} cycles (GRBM_GUI_ACTIVE / 8)", "",
+                  f"MFMA busy / SQ busy = {100 * util['mfma_util_vs_sq_busy']:.1f}%; "
+                  f"MFMA busy / GPU busy = {100 * util['mfma_util_vs_grbm']:.1f}%; "
+                  f"SQ_WAIT_ANY / SQ_WAVE_CYCLES = {100 * util['wait_any_frac']:.1f}%; "
+                  f"LDS bank-conflict cycles per LDS-active cycle = {util['lds_bank_conflict_per_active']:.3f}"]
     if trace_csv and steps:
         timed_ns = timed_region_avg_ns(trace_csv, steps)
         if timed_ns:
@@ -182,7 +229,9 @@ def summarize_profiles(stats_csv, fetch_csv, write_csv, command, trace_csv=None,
                       f"of {MXFP4_PEAK_TFLOPS:.0f})"]
     rec = {"kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": round(fetch_b + write_b),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
-           "fetch_scale": f_scale, "write_scale": w_scale, "gemm_avg_us": gemm_avg_ns and gemm_avg_ns / 1e3}
+           "fetch_scale": f_scale, "write_scale": w_scale, "gemm_avg_us": gemm_avg_ns and gemm_avg_ns / 1e3,
+           "quant_source_hash": kernel_source_hash(QUANT_SOURCES),
+           "quant_hbm_bytes_per_launch": round(q_fetch_b + q_write_b), "gemm_util": util}
     return "\n".join(lines) + "\n", rec
 
 
@@ -524,6 +573,9 @@ def main():
     # (~65 ms) and the timed region 200 steps (~32 ms), both well inside a second.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
+    # a floor on the warmup's GPU time: when W steps take less (a faster kernel, a
+    # smaller --warmup), whole batches of 50 more untimed steps run until it is met
+    ap.add_argument("--min-warmup-ms", type=float, default=80.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true",
                     help="time every other step of the path, one JSON line per row")
@@ -535,13 +587,16 @@ def main():
                     help="with --summarize: a command line that produced the inputs")
     ap.add_argument("--bench-log", metavar="LOG",
                     help="with --summarize: the output of the profiled bench.py run")
+    ap.add_argument("--util", metavar="UTIL_CSV",
+                    help="with --summarize: the counter_collection CSV of the --pmc SQ/GRBM "
+                         "utilisation run")
     ap.add_argument("--trace", metavar="TRACE_CSV",
                     help="with --summarize: the kernel trace of the stats run; the GEMM average "
                          "over its last --steps dispatches is added")
     a = ap.parse_args()
     if a.summarize:
         text, rec = summarize_profiles(*a.summarize, a.command, trace_csv=a.trace, steps=a.steps,
-                                       bench_log=a.bench_log)
+                                       bench_log=a.bench_log, util_csv=a.util)
         with open(os.path.join(ROOT, "profiles", "gemm_mx_mlp_up_4608x3072x12288.md"), "w") as f:
             f.write(text)
         with open(TRAFFIC_FILE, "w") as f:
@@ -617,8 +672,18 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
-    for i in range(a.warmup):
-        step(i)
+    t_w = time.perf_counter()
+    n_warm = 0
+    for _ in range(a.warmup):
+        step(n_warm)
+        n_warm += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t_w) * 1e3 < a.min_warmup_ms:
+        for _ in range(50):
+            step(n_warm)
+            n_warm += 1
+        torch.cuda.synchronize()
+    warmup_ms = (time.perf_counter() - t_w) * 1e3
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(a.steps)]
     torch.cuda.synchronize()
@@ -627,7 +692,10 @@ def main():
         step(i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gemm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in events]))
+    ev_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    gemm_ms = float(np.mean(ev_ms))
+    # the last quarter of the timed steps: the clocks have settled longest there
+    gemm_ms_lq = float(np.mean(ev_ms[-max(1, a.steps // 4):]))
     ms_per_step = wall * 1e3 / a.steps
 
     flops = 2.0 * M * N * K
@@ -640,6 +708,8 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "warmup_steps_run": n_warm,
+        "warmup_ms": round(warmup_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -654,6 +724,7 @@ def main():
                      "achieved": round(gemm_tflops, 2), "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(), "avg_launch_ms": round(gemm_ms, 5),
+                     "avg_launch_ms_last_quarter": round(gemm_ms_lq, 5),
                      "algorithmic_flop_per_launch": flops},
     }
     if not a.no_cpu_baseline:
