@@ -17,6 +17,10 @@ What it computes, in plain NumPy (fp64 unless the step is defined in fp32):
   with a per-tensor fp32 scale, asymmetric int4 group-64) and their dequantizers.
 * ``layer``   -- the linear layer: dequantized fp64 GEMM, the low-rank branch
   evaluated right to left, bias, and the per-element error bound.
+* ``attention`` -- FP8 attention (NVIDIA Technical Blog summary, second
+  optimization layer): MXFP8 Q, K (along head_dim) and V (along the keys), the
+  blocked online softmax with P quantized to MXFP8, and per element the most that
+  codes decided differently in fp32 could move the result.
 
 Sources.  The pages define the layer's structure: the SVDQuant Guide (aifetchly),
 "The Three Pillars of SVDQuant", 1. Mathematical Outlier Factorization (forward
@@ -36,4 +40,4 @@ Parity status: every function here is pinned by the CPU tests
 exact special cases.  None is "parity unpinned".
 """
 
-from . import formats, quant, layer  # noqa: F401
+from . import formats, quant, layer, attention  # noqa: F401

@@ -1,0 +1,175 @@
+"""Pins of the FP8 attention oracle (oracle/attention.py) to things other than
+itself: a library softmax, closed forms (uniform and one-hot attention), an
+invariance of the blocked recurrence, and the already pinned MXFP8 quantizer."""
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from bit_quantized_gemm_quantize_amd import synth
+from oracle import attention as A
+from oracle.formats import bf16_to_f64
+from oracle.quant import mxfp8_dequantize, mxfp8_quantize
+
+
+def _bits(x):
+    return synth.to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _qkv(seed, batch, seq, heads, d=128, sd=1.0):
+    rng = np.random.default_rng(seed)
+    shape = (batch * seq, heads * d)
+    return tuple(_bits(sd * rng.standard_normal(shape)) for _ in range(3))
+
+
+@pytest.mark.parametrize("seq,key_block", [(150, 64), (64, 64), (37, 64), (200, 32)])
+def test_unquantized_recurrence_is_softmax_attention(seq, key_block):
+    """quantize=False: the blocked online recurrence (steps 3, 4, 6) must equal
+    softmax(c Q K^T) V computed with scipy's softmax, per batch item and head,
+    including a ragged last block."""
+    batch, heads, d = 2, 2, 128
+    q, k, v = _qkv(1, batch, seq, heads, sd=2.0)
+    r = A.attention_fp8(q, k, v, batch, seq, heads, d, key_block=key_block, quantize=False)
+    c = 1.0 / np.sqrt(d)
+    qf = bf16_to_f64(q).reshape(batch, seq, heads, d)
+    kf = bf16_to_f64(k).reshape(batch, seq, heads, d)
+    vf = bf16_to_f64(v).reshape(batch, seq, heads, d)
+    for b in range(batch):
+        for h in range(heads):
+            p = softmax(c * qf[b, :, h] @ kf[b, :, h].T, axis=1)
+            ref = p @ vf[b, :, h]
+            got = r["o"].reshape(batch, seq, heads, d)[b, :, h]
+            np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_uniform_scores_average_the_quantized_values():
+    """K = 0: every logit is 0, every probability exp(0) = 1 (an exact MXFP8 value),
+    so O is the plain mean of the MXFP8-dequantized V over the seq keys (a ragged
+    seq: the masked keys of the last block must not count)."""
+    batch, seq, heads, d = 1, 100, 2, 128
+    q, _, v = _qkv(2, batch, seq, heads)
+    k = np.zeros_like(q)
+    r = A.attention_fp8(q, k, v, batch, seq, heads, d)
+    vt = np.zeros((heads * d, 128), dtype=np.uint16)                           # keys padded to 128
+    vt[:, :seq] = v.reshape(seq, heads * d).T
+    vhat = mxfp8_dequantize(*mxfp8_quantize(vt))[:, :seq]                      # [heads*d, seq]
+    expect = np.broadcast_to(vhat.mean(axis=1), (seq, heads * d))
+    np.testing.assert_allclose(r["o"], expect, rtol=1e-12, atol=1e-15)
+    assert np.all(r["ambiguity"] == 0)
+    assert np.all(r["l"] == seq)
+
+
+def test_one_hot_scores_select_one_value_row():
+    """Query i scores a * e_{pi(i)} against keys e_j (one-hot, exact in MXFP8): one
+    logit per row is a c = 64 larger than the rest, so every other probability is
+    below e^-64 and O row i is row pi(i) of the dequantized V.  pi puts the
+    maximum in every key block, so the running maximum grows mid-sequence and the
+    rescaling of earlier blocks is exercised."""
+    batch, seq, heads, d = 1, 128, 1, 128
+    rng = np.random.default_rng(3)
+    pi = rng.permutation(seq)
+    a = 64.0 * np.sqrt(d)                      # c * a = 64
+    qf = np.zeros((seq, d))
+    qf[np.arange(seq), pi] = a
+    kf = np.eye(seq, d)
+    _, _, v = _qkv(4, batch, seq, heads)
+    r = A.attention_fp8(_bits(qf), _bits(kf), v, batch, seq, heads, d)
+    vc, vs = mxfp8_quantize(np.ascontiguousarray(v.T))
+    vhat = mxfp8_dequantize(vc, vs).T                                          # [seq, d]
+    np.testing.assert_allclose(r["o"], vhat[pi], rtol=1e-20, atol=1e-24)
+
+
+def test_blocking_is_invisible_while_the_maximum_stays_put():
+    """When every row's maximum logit sits in the first key block, the running
+    maximum never changes, P is quantized against the final maximum in every
+    block, and key blocks of 64 give the same O as one block over all keys (the
+    MX chunks of 32 keys are the same either way)."""
+    batch, seq, heads, d = 1, 192, 2, 128
+    rng = np.random.default_rng(5)
+    qf = np.abs(rng.standard_normal((seq, heads * d)))     # positive queries
+    kf = rng.standard_normal((seq, heads * d))
+    kf[3] = 4.0                                            # key 3 wins every row
+    q, k = _bits(qf), _bits(kf)
+    _, _, v = _qkv(6, batch, seq, heads)
+    r64 = A.attention_fp8(q, k, v, batch, seq, heads, d, key_block=64)
+    r1 = A.attention_fp8(q, k, v, batch, seq, heads, d, key_block=seq)
+    np.testing.assert_allclose(r64["o"], r1["o"], rtol=1e-12, atol=1e-15)
+    # and the maximum really moves when it does not sit first: the results differ
+    kf2 = kf.copy()
+    kf2[3] = kf[4]
+    kf2[150] = 4.0
+    r64b = A.attention_fp8(q, _bits(kf2), v, batch, seq, heads, d, key_block=64)
+    r1b = A.attention_fp8(q, _bits(kf2), v, batch, seq, heads, d, key_block=seq)
+    assert np.abs(r64b["o"] - r1b["o"]).max() > 0
+
+
+def test_real_valued_mx8_matches_the_pinned_mxfp8_quantizer():
+    """mx8_real (used for P) and quant.mxfp8_quantize (pinned against the golden
+    blocks) give the same values on bf16 inputs, including zero blocks, values
+    that saturate, and signed values."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 256)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    x[5] = 0.0
+    x[6, :32] = 0.0
+    bits = _bits(x)
+    codes, scales = mxfp8_quantize(bits)
+    vals, step, und = A.mx8_real(bf16_to_f64(bits))
+    np.testing.assert_array_equal(vals, mxfp8_dequantize(codes, scales))
+    assert np.all(step > 0)
+
+
+def test_fp8_error_against_exact_attention_is_a_few_percent():
+    """Gaussian Q, K, V: the FP8 result stays within the error FP8 allows (E4M3
+    keeps 3 mantissa bits: a few percent relative RMS), and is not exact."""
+    batch, seq, heads, d = 1, 160, 2, 128
+    q, k, v = _qkv(8, batch, seq, heads)
+    r = A.attention_fp8(q, k, v, batch, seq, heads, d)
+    e = A.attention_fp8(q, k, v, batch, seq, heads, d, quantize=False)
+    rel = np.sqrt(np.mean((r["o"] - e["o"]) ** 2) / np.mean(e["o"] ** 2))
+    assert 1e-3 < rel < 0.1
+    assert np.all(r["ambiguity"] >= 0)
+    assert (r["ambiguity"] > 0).mean() < 0.2
+
+
+def test_quantize_v_layout():
+    """V is quantized along the keys per (batch, head, channel), padded to 32 keys."""
+    batch, seq, heads, d = 2, 40, 2, 128
+    _, _, v = _qkv(9, batch, seq, heads)
+    codes, scales = A.quantize_v(v, batch, seq, heads, d)
+    assert codes.shape == (batch, heads * d, 64) and scales.shape == (batch, heads * d, 2)
+    vb = v.reshape(batch, seq, heads * d)
+    for b in range(batch):
+        c, s = mxfp8_quantize(np.ascontiguousarray(vb[b, :32].T))
+        np.testing.assert_array_equal(codes[b, :, :32], c)
+        np.testing.assert_array_equal(scales[b, :, :1], s)
+    assert np.all(codes[:, :, seq:] == 0)
+
+
+@pytest.mark.parametrize("seq,second", [(64, 40), (128, 100)])
+def test_two_live_keys_worked_by_hand(seq, second):
+    """A worked example whose codes are derived by hand.  Query 0 is 14 e_0 (14 =
+    1.75 * 2**3 is exact in E4M3, so its MXFP8 form is exact); key 0 is e_0, key
+    `second` is 0 and every other key is -64 e_0.  With c = 1/sqrt(128):
+      logits 14 c = 1.2374..., 0, and -79.2 (probabilities below e^-80: zero codes);
+      row maximum 14 c -> p = 1 for key 0, p = exp(-14 c) = 0.290110... for key
+      `second`, sum l = 1.290110... (the -79 keys add < 1e-33);
+      chunk of key 0: amax 1, E = 0 - 8, code of 1 * 2**8 = 256 exact;
+      chunk of key `second`: amax 0.2901, E = floor(log2 0.2901) - 8 = -10,
+      0.2901 * 2**10 = 297.07 lies in [256, 512) where E4M3 steps by 32, so it
+      rounds to 288: p^ = 288 / 1024 = 0.28125.
+    V rows 0 and `second` are exact in MXFP8 along the keys (values 1 and 2 in
+    channel d, all other keys 0), so O[0, d] = (1 * 1 + 0.28125 * 2) / l."""
+    batch, heads, d = 1, 1, 128
+    qf = np.zeros((seq, d))
+    qf[0, 0] = 14.0
+    kf = np.zeros((seq, d))
+    kf[:, 0] = -64.0
+    kf[0, 0] = 1.0
+    kf[second, 0] = 0.0
+    vf = np.zeros((seq, d))
+    vf[0, :] = 1.0
+    vf[second, :] = 2.0
+    r = A.attention_fp8(_bits(qf), _bits(kf), _bits(vf), batch, seq, heads, d)
+    l = 1.0 + np.exp(-14.0 / np.sqrt(128.0))
+    np.testing.assert_allclose(r["o"][0], (1.0 + 0.28125 * 2.0) / l, rtol=1e-14)
+    np.testing.assert_allclose(r["l"][0, 0, 0], l, rtol=1e-14)
