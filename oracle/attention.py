@@ -45,28 +45,36 @@ from .quant import MX_BLOCK, mxfp8_dequantize, mxfp8_quantize
 
 KEY_BLOCK = 64
 E4M3_EMAX = 8
-# a code whose fp64 input lies this close (relative) to a rounding boundary, or a
-# block whose amax lies this close to a power of two, counts as undecided
+# default margin of mx8_real: a code whose input lies this close (relative) to a
+# rounding boundary, or a block whose amax lies this close to a power of two,
+# counts as undecided
 AMBIGUOUS_REL = 1e-5
 FP32_TINY = 2.0 ** -126
 
 
-def mx8_real(x):
+def mx8_real(x, rel=AMBIGUOUS_REL, force_chunk=None):
     """MXFP8 of real (fp64) values along the last axis, whose length is a multiple
     of 32, by the same rule as ``quant.mxfp8_quantize`` (E = floor(log2 amax) - 8,
     E4M3 round to nearest even of x * 2**-E, saturating at 448).
 
+    rel: the relative error (scalar, or per element) with which another evaluation
+    of the same values may see them.  force_chunk (optional, bool per block of 32):
+    blocks whose exponent is to be counted as undecided whatever their amax.
+
     Returns (dequantized fp64 values, step, undecided):
     * step: the spacing of the E4M3 grid at each element times 2**E (the most a
-      one-code change of that element moves its value),
-    * undecided: elements whose code an fp32 evaluation of the same rule might
-      decide differently (the value within AMBIGUOUS_REL of a rounding boundary,
-      or the block's amax within AMBIGUOUS_REL of a power of two).
+      one-code change of that element moves its value), doubled where the block
+      exponent is undecided (the grid then halves or doubles),
+    * undecided: elements whose code such an evaluation might decide differently
+      (the value within rel of a rounding boundary, or the block's amax within rel
+      of a power of two, or a forced block).
     """
     x = np.asarray(x, dtype=np.float64)
     check_finite(x, "attention operand")
     shape = x.shape
-    blocks = x.reshape(shape[:-1] + (shape[-1] // MX_BLOCK, MX_BLOCK))
+    bshape = shape[:-1] + (shape[-1] // MX_BLOCK, MX_BLOCK)
+    blocks = x.reshape(bshape)
+    relb = np.broadcast_to(np.asarray(rel, dtype=np.float64), shape).reshape(bshape)
     amax = np.abs(blocks).max(axis=-1)
     pos = amax > 0
     lg = floor_log2(np.where(pos, amax, 1.0))
@@ -83,16 +91,19 @@ def mx8_real(x):
     # distance to the nearest rounding boundary (midpoints between grid values)
     # (a power of two is a grid value, not a boundary; u >= 448 saturates)
     frac = u / spacing - np.floor(u / spacing)
-    near_mid = np.abs(frac - 0.5) * spacing <= AMBIGUOUS_REL * np.maximum(u, spacing)
+    near_mid = np.abs(frac - 0.5) * spacing <= relb * np.maximum(u, spacing)
     undecided = near_mid & (u < E4M3_MAX)
-    # amax within AMBIGUOUS_REL of a power of two, from either side.  amax = 1 exactly
-    # is decided: it is the chunk holding the row's running maximum, whose
-    # probability exp(0) both sides compute as exactly 1
+    # amax within rel of a power of two, from either side.  amax = 1 exactly is
+    # decided here: it is the chunk holding the row's running maximum, whose
+    # probability exp(0) is exactly 1 in any evaluation (a near tie for that
+    # maximum is the caller's to force)
+    relc = relb.max(axis=-1)
     lo = np.ldexp(1.0, lg)
     dist = np.minimum(amax - lo, 2.0 * lo - amax)
-    amb_scale = pos & (amax != 1.0) & (dist <= AMBIGUOUS_REL * np.where(pos, amax, 1.0))
+    amb_scale = pos & (amax != 1.0) & (dist <= relc * np.where(pos, amax, 1.0))
+    if force_chunk is not None:
+        amb_scale = amb_scale | np.asarray(force_chunk, dtype=bool)
     undecided = undecided | amb_scale[..., None]
-    # a changed block exponent halves or doubles the grid: allow twice the spacing
     step = spacing * scale * np.where(amb_scale[..., None], 2.0, 1.0)
     return vals.reshape(shape), step.reshape(shape), undecided.reshape(shape)
 
@@ -124,20 +135,32 @@ def quantize_v(v_bits, batch, seq, heads, head_dim):
 
 
 def attention_fp8(q_bits, k_bits, v_bits, batch, seq, heads, head_dim=128, scale=None,
-                  key_block=KEY_BLOCK, quantize=True):
+                  key_block=KEY_BLOCK, quantize=True, query_rows=None, score_err=0.0, sum_err=0.0):
     """FP8 attention (steps 1-6 above) of Q, K, V given as bf16 bits
     [batch * seq, heads * head_dim] (token-major, head h in columns
     h * head_dim .. +head_dim, as the QKV projection writes them).
 
     Returns dict(out_bits uint16 [batch * seq, heads * head_dim] (bf16 RNE of o),
-    o fp64 (before rounding), ambiguity fp64 (per element: the most that codes of P
-    left undecided in fp64 can move o), l fp64 [batch, heads, seq]).
+    o fp64 (before rounding), l fp64 [batch, heads, seq], and two per-element
+    bounds for comparing another evaluation of the same steps in finite precision:
+    * ambiguity: the most that codes or exponents of P it may decide the other way
+      can move o (values within its error of a decision boundary),
+    * error_bound: the most its rounding can move o otherwise: the errors of the
+      probabilities (through l and the rescaling factors) and of the P V sums.
+    score_err is that evaluation's error bound on a score, relative to
+    sum_d |q^_d k^_d| (its matrix unit's accumulation error), and sum_err the same
+    for the sums of P^ V^ (relative to sum |p^ v^|); its fp32 exp2 and logit
+    arithmetic add a relative 2**-20 (1 + |c s| + |c m|) to each probability.
+    Neither bound changes o.
 
     quantize=False skips every quantization (steps 1, 2 and 5 become identities):
     the recurrence then computes exact softmax attention, which the tests use to pin
     steps 3, 4 and 6.
+
+    query_rows (optional, indices into the seq queries of every batch item): only
+    those queries are computed (every query is independent of the others); the
+    returned arrays then hold batch * len(query_rows) rows, batch-major.
     """
-    n = batch * seq
     width = heads * head_dim
     c = 1.0 / np.sqrt(head_dim) if scale is None else float(scale)
     if quantize:
@@ -154,18 +177,26 @@ def attention_fp8(q_bits, k_bits, v_bits, batch, seq, heads, head_dim=128, scale
         vt = np.transpose(v, (0, 2, 1))
     q = q.reshape(batch, seq, heads, head_dim)
     k = k.reshape(batch, seq, heads, head_dim)
-    o = np.zeros((batch, seq, heads, head_dim))
+    rows = np.arange(seq) if query_rows is None else np.asarray(query_rows, dtype=np.int64)
+    q = q[:, rows]
+    nq = len(rows)
+    o = np.zeros((batch, nq, heads, head_dim))
     amb = np.zeros_like(o)
-    lsum = np.zeros((batch, heads, seq))
+    lsum = np.zeros((batch, heads, nq))
+    err = np.zeros_like(o)
     nblocks = -(-seq // key_block)
     for b in range(batch):
         for h in range(heads):
-            s_all = q[b, :, h, :] @ k[b, :, h, :].T                    # [seq, seq]
+            qh, kh = q[b, :, h, :], k[b, :, h, :]
+            s_all = qh @ kh.T                                          # [queries, seq]
+            ds = score_err * (np.abs(qh) @ np.abs(kh).T)               # score error bounds
+            dsmax = ds.max(axis=1)
             v_h = vt[b, h * head_dim:(h + 1) * head_dim, :seq].T       # [seq keys, head_dim]
-            m = np.full(seq, -np.inf)
-            l = np.zeros(seq)
-            acc = np.zeros((seq, head_dim))
-            bnd = np.zeros((seq, head_dim))
+            m = np.full(nq, -np.inf)
+            l = np.zeros(nq)
+            acc = np.zeros((nq, head_dim))
+            acc_abs = np.zeros((nq, head_dim))                         # sum of |p^ v^|, rescaled
+            bnd = np.zeros((nq, head_dim))
             for blk in range(nblocks):
                 j0 = blk * key_block
                 j1 = min(j0 + key_block, seq)
@@ -180,19 +211,41 @@ def attention_fp8(q_bits, k_bits, v_bits, batch, seq, heads, head_dim=128, scale
                 l = alpha * l + p.sum(axis=1)
                 if quantize:
                     width_pad = -(-(j1 - j0) // MX_BLOCK) * MX_BLOCK
-                    pp = np.zeros((seq, width_pad))
+                    pp = np.zeros((nq, width_pad))
                     pp[:, :j1 - j0] = p
-                    ph, step, und = mx8_real(pp)
+                    # relative error of each probability as the other evaluation sees
+                    # it: its score's and the maximum's errors, and fp32's exp2
+                    rel = np.full((nq, width_pad), 1.0)
+                    rel[:, :j1 - j0] = (c * (ds[:, j0:j1] + dsmax[:, None])
+                                        + 2.0 ** -20 * (1 + np.abs(c * s) + np.abs(c * m_new)[:, None]))
+                    # the chunk holding the row maximum (amax exactly 1) loses it when
+                    # a rival score (in another chunk, or an earlier block's maximum)
+                    # lies within the two scores' errors: its exponent is undecided
+                    # then.  Rounding the logits to fp32 keeps their order, so exact
+                    # scores (score_err = 0) never trade places.
+                    cmax = pp.reshape(nq, -1, MX_BLOCK).max(axis=2)
+                    top = cmax == 1.0
+                    rival = np.maximum(np.where(top, 0.0, cmax).max(axis=1), alpha)
+                    tie = (score_err > 0) & (rival >= np.exp(-2.0 * c * dsmax))
+                    ph, step, und = mx8_real(pp, rel, force_chunk=top & tie[:, None])
                     ph, step, und = ph[:, :j1 - j0], step[:, :j1 - j0], und[:, :j1 - j0]
                     flips = np.where(und, step, 0.0) @ np.abs(v_h[j0:j1])
                 else:
                     ph = p
                     flips = 0.0
                 acc = alpha[:, None] * acc + ph @ v_h[j0:j1]
+                acc_abs = alpha[:, None] * acc_abs + np.abs(ph) @ np.abs(v_h[j0:j1])
                 bnd = alpha[:, None] * bnd + flips
                 m = m_new
             o[b, :, h, :] = acc / l[:, None]
             amb[b, :, h, :] = bnd / l[:, None]
+            # e bounds the relative error of every probability, of every rescaling
+            # factor and of l: O' = sum A' p^ v / sum A' p' moves by at most
+            # (2 e + sum_err) sum |p^ v^| / l + 4 e |O|
+            e = c * 2.0 * dsmax + 2.0 ** -20 * (1 + 2.0 * np.abs(c * s_all).max(axis=1))
+            err[b, :, h, :] = ((2.0 * e + sum_err)[:, None] * acc_abs / l[:, None]
+                               + 4.0 * e[:, None] * np.abs(o[b, :, h, :]))
             lsum[b, h] = l
-    o = o.reshape(n, width)
-    return dict(out_bits=f32_to_bf16_rne(o), o=o, ambiguity=amb.reshape(n, width), l=lsum)
+    o = o.reshape(batch * nq, width)
+    return dict(out_bits=f32_to_bf16_rne(o), o=o, ambiguity=amb.reshape(batch * nq, width),
+                error_bound=err.reshape(batch * nq, width), l=lsum)

@@ -127,8 +127,10 @@ def test_fp8_error_against_exact_attention_is_a_few_percent():
     e = A.attention_fp8(q, k, v, batch, seq, heads, d, quantize=False)
     rel = np.sqrt(np.mean((r["o"] - e["o"]) ** 2) / np.mean(e["o"] ** 2))
     assert 1e-3 < rel < 0.1
+    # the allowance for codes an fp32 evaluation may decide the other way stays a
+    # small fraction of the result
     assert np.all(r["ambiguity"] >= 0)
-    assert (r["ambiguity"] > 0).mean() < 0.2
+    assert r["ambiguity"].mean() < 0.01 * np.sqrt(np.mean(r["o"] ** 2))
 
 
 def test_quantize_v_layout():
