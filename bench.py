@@ -464,6 +464,24 @@ def bench_rows(reps=50):
               flush=True)
     del y8, x8, w8
 
+    # ---- f4: FP8 attention at the FLUX-class joint attention of a 1024x1024 image
+    # (4096 image + 512 text tokens, 24 heads of 128), Gaussian Q, K, V
+    Sa, Ha = 4608, 24
+    rng_a = np.random.default_rng(7)
+    qa, ka, va = (bf16_dev(synth.to_bf16_bits(rng_a.standard_normal((Sa, Ha * 128)).astype(np.float32)))
+                  for _ in range(3))
+    ab = B.attn_buffers(1, Sa, Ha, dev)
+    oa = torch.empty((Sa, Ha * 128), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda i: B.attention_fp8_quantize(qa, ka, va, 1, Sa, Ha, ab, stream=stream), 1)
+    emit(f"attention_fp8_quantize {Sa} tokens x {Ha} heads x 128", ms,
+         bytes_=3 * Sa * Ha * 128 * 2 + 3 * Sa * Ha * (128 + 4),
+         note="Q, K MXFP8 along head_dim, V MXFP8 along the keys (transposed)")
+    ms = timed(lambda i: B.attention_fp8(ab, 1, Sa, Ha, oa, stream=stream), 1)
+    emit(f"attention_fp8 {Sa} tokens x {Ha} heads x 128", ms, flops=4.0 * Sa * Sa * 128 * Ha, peak=5000.0,
+         note="Q K^T and P V on the E4M3 block-scaled MFMA, online softmax over 64-key blocks; "
+              "peak = dense FP8 5.0 PFLOP/s")
+    del qa, ka, va, ab, oa
+
     # ---- comparison: the vendor MXFP4 GEMM (hipBLASLt through torch._scaled_mm) on
     # the same codes and E8M0 scales, row-major scale layout
     y = torch.empty((Mq, Np), dtype=torch.bfloat16, device=dev)

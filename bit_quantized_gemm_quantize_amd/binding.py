@@ -43,6 +43,9 @@ SIGNATURES = {
                                               _I32, _P, _P, _P, _I64, _P]),
     "gemm_w4a16": (_c.c_int, [_P, _I64, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _P, _I64, _c.c_int,
                               _P]),
+    "attention_fp8_quantize": (_c.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                          _P, _P, _P, _P]),
+    "attention_fp8": (_c.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _c.c_float, _P, _I64, _P]),
     "q4_status_string": (_c.c_char_p, [_c.c_int]),
 }
 
@@ -356,7 +359,57 @@ def gemm_w4a16(x, w_codes, w_scales, w_zeros, N, y, bias=None, group=64, out=OUT
     _check("gemm_w4a16", st)
 
 
+HEAD_DIM = 128
+
+
+def _attn_bufs_check(bufs, batch, seq, heads, dev):
+    tokens, width = batch * seq, heads * HEAD_DIM
+    seq64 = -(-seq // 64) * 64
+    _packed(bufs["qc"], "qc", torch.uint8, tokens, width, dev)
+    _packed(bufs["kc"], "kc", torch.uint8, tokens, width, dev)
+    _packed(bufs["qs"], "qs", torch.uint8, tokens, heads * 4, dev)
+    _packed(bufs["ks"], "ks", torch.uint8, tokens, heads * 4, dev)
+    _packed(bufs["vc"], "vc", torch.uint8, batch * width, seq64, dev)
+    _packed(bufs["vs"], "vs", torch.uint8, batch * heads * (seq64 // 64), 256, dev)
+
+
+def attention_fp8_quantize(q, k, v, batch, seq, heads, bufs, stream=None):
+    """q, k, v bf16 [batch*seq, heads*128] (contiguous rows, any row stride) -> the
+    MXFP8 operands of attention_fp8 in bufs (from attn_buffers)."""
+    dev = _device(q, "q")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _strided(t, name, (torch.bfloat16,), batch * seq, heads * HEAD_DIM, dev)
+    _attn_bufs_check(bufs, batch, seq, heads, dev)
+    st = load().attention_fp8_quantize(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), batch,
+                                       seq, heads, HEAD_DIM, _ptr(bufs["qc"]), _ptr(bufs["qs"]), _ptr(bufs["kc"]),
+                                       _ptr(bufs["ks"]), _ptr(bufs["vc"]), _ptr(bufs["vs"]), _stream(stream))
+    _check("attention_fp8_quantize", st)
+
+
+def attention_fp8(bufs, batch, seq, heads, out, softmax_scale=None, stream=None):
+    """FP8 attention of the operands in bufs -> out bf16 [batch*seq, heads*128]."""
+    dev = _device(out, "out")
+    _strided(out, "out", (torch.bfloat16,), batch * seq, heads * HEAD_DIM, dev)
+    _attn_bufs_check(bufs, batch, seq, heads, dev)
+    c = HEAD_DIM ** -0.5 if softmax_scale is None else float(softmax_scale)
+    st = load().attention_fp8(_ptr(bufs["qc"]), _ptr(bufs["qs"]), _ptr(bufs["kc"]), _ptr(bufs["ks"]),
+                              _ptr(bufs["vc"]), _ptr(bufs["vs"]), batch, seq, heads, HEAD_DIM, c, _ptr(out),
+                              out.stride(0), _stream(stream))
+    _check("attention_fp8", st)
+
+
 # ----------------------------------------------------------------------------- buffers
+def attn_buffers(batch, seq, heads, device="cuda"):
+    """Output buffers of attention_fp8_quantize (the MXFP8 Q, K, V), as a dict."""
+    tokens, width = batch * seq, heads * HEAD_DIM
+    seq64 = -(-seq // 64) * 64
+    u8 = dict(dtype=torch.uint8, device=device)
+    return dict(qc=torch.empty((tokens, width), **u8), qs=torch.empty((tokens, heads * 4), **u8),
+                kc=torch.empty((tokens, width), **u8), ks=torch.empty((tokens, heads * 4), **u8),
+                vc=torch.empty((batch * width, seq64), **u8),
+                vs=torch.empty((batch * heads * (seq64 // 64), 256), **u8))
+
+
 def empty_quant(fmt, rows, K, device="cuda"):
     """Output buffers for quantize_act / pack_weights: (codes, scales, tensor_scale|zeros)."""
     fmt = _fmt(fmt)

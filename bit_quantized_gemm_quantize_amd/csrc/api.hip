@@ -27,6 +27,9 @@ bool rank_ok(int32_t r) { return r == 0 || r == 16 || r == 32; }
 constexpr int64_t kMaxRows = int64_t(1) << 30;   // M, N
 constexpr int64_t kMaxK = int64_t(1) << 22;      // K, and ldx of the W4A16 activations
 constexpr int64_t kMaxLdx = int64_t(1) << 26;    // ldx of the quantizer's activations
+// FP8 attention: the code tensors (batch * seq * heads * 128 bytes) stay below 2^31,
+// the reach of the kernels' 32-bit buffer offsets
+constexpr int64_t kMaxAttnElems = int64_t(1) << 31;
 
 // The NVFP4 tensor-amax scratch (q4::kNvScratchWords words): one buffer per
 // (device, stream), allocated on the first NVFP4 quantization queued on that
@@ -327,6 +330,43 @@ q4_status gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* w_codes,
   q4::EpilogueArgs ep{nullptr, nullptr, 0, bias, y, ldy, out == Q4_OUT_F32 ? 1 : 0};
   return launched(q4::launch_gemm_w4a16(x, ldx, w_codes, w_scales, w_zeros, M, N, K, ep,
                                         static_cast<hipStream_t>(stream)));
+}
+
+q4_status attention_fp8_quantize(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk,
+                                 const uint16_t* v, int64_t ldv, int64_t batch, int64_t seq, int64_t heads,
+                                 int64_t head_dim, uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes,
+                                 uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales, void* stream) {
+  if (head_dim != 128 || batch < 0 || seq < 0 || heads < 0) return Q4_ERR_SHAPE;
+  if (batch * seq * heads > kMaxAttnElems / 128) return Q4_ERR_SHAPE;
+  const int64_t width = heads * 128;
+  if (ldq < width || ldk < width || ldv < width || ldq > kMaxLdx || ldk > kMaxLdx || ldv > kMaxLdx)
+    return Q4_ERR_SHAPE;
+  if (batch == 0 || seq == 0 || heads == 0) return Q4_OK;   // empty: the pointers are not looked at
+  if (!q || !k || !v || !q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales)
+    return Q4_ERR_NULL;
+  if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 4) || (ldv % 2) != 0 || !aligned(q_codes, 16) ||
+      !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scales, 4) || !aligned(k_scales, 4) ||
+      !aligned(v_scales, 4))
+    return Q4_ERR_ALIGN;
+  return launched(q4::launch_attn_quantize(q, ldq, k, ldk, v, ldv, batch, seq, heads, q_codes, q_scales, k_codes,
+                                           k_scales, v_codes, v_scales, static_cast<hipStream_t>(stream)));
+}
+
+q4_status attention_fp8(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                        const uint8_t* k_scales, const uint8_t* v_codes, const uint8_t* v_scales, int64_t batch,
+                        int64_t seq, int64_t heads, int64_t head_dim, float softmax_scale, uint16_t* out,
+                        int64_t ldo, void* stream) {
+  if (head_dim != 128 || batch < 0 || seq < 0 || heads < 0) return Q4_ERR_SHAPE;
+  if (batch * seq * heads > kMaxAttnElems / 128) return Q4_ERR_SHAPE;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 3.0e38f)) return Q4_ERR_SHAPE;
+  if (ldo < heads * 128 || ldo > kMaxLdx) return Q4_ERR_SHAPE;
+  if (batch == 0 || seq == 0 || heads == 0) return Q4_OK;   // empty: the pointers are not looked at
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out) return Q4_ERR_NULL;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scales, 4) ||
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(out, 8) || (ldo % 4) != 0)
+    return Q4_ERR_ALIGN;
+  return launched(q4::launch_attn_fp8(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, batch, seq, heads,
+                                      softmax_scale, out, ldo, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -80,4 +80,15 @@ hipError_t launch_gemm_anyk(int fmt, const uint8_t* ac, const uint8_t* as, const
                             const uint8_t* bc, const uint8_t* bs, const float* bts, int64_t M,
                             int64_t N, int64_t K, const EpilogueArgs& ep, hipStream_t s);
 
+// FP8 attention (head_dim 128): the MXFP8 quantization of Q, K (rows) and V
+// (transposed, along the keys), and the attention kernel.  Layouts as declared in
+// q4lin.h.
+hipError_t launch_attn_quantize(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk,
+                                const uint16_t* v, int64_t ldv, int64_t batch, int64_t seq, int64_t heads,
+                                uint8_t* qc, uint8_t* qs, uint8_t* kc, uint8_t* ks, uint8_t* vc,
+                                uint8_t* vs, hipStream_t s);
+hipError_t launch_attn_fp8(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                           const uint8_t* vc, const uint8_t* vs, int64_t batch, int64_t seq, int64_t heads,
+                           float softmax_scale, uint16_t* out, int64_t ldo, hipStream_t s);
+
 }  // namespace q4

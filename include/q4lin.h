@@ -337,6 +337,60 @@ Q4_API q4_status gemm_w4a16(const uint16_t* x, int64_t ldx,
                      int64_t M, int64_t N, int64_t K, int32_t group,
                      const uint16_t* bias, void* y, int64_t ldy, q4_out out, void* stream);
 
+/*
+ * attention_fp8_quantize -- the first half of FP8 attention (NVIDIA Technical Blog
+ * summary, second optimization layer: attention quantized to FP8): Q and K to
+ * MXFP8 along head_dim, V to MXFP8 along the keys, transposed.
+ *
+ *   q, k, v   bf16 [batch * seq, heads * 128], row strides ldq, ldk, ldv (elements,
+ *             at least heads * 128): token-major, head h in columns h*128 .. +128,
+ *             as gemm_w4a4_lowrank_qkv_rope writes them.  v and ldv: 4-byte
+ *             aligned / even.
+ *   head_dim  128 (the only value supported).
+ *   q_codes, k_codes    uint8 [batch * seq, heads * 128] E4M3 codes, 16-byte aligned.
+ *   q_scales, k_scales  uint8 [batch * seq, heads * 4] E8M0 scale bytes (one per
+ *                       32 channels), 4-byte aligned.
+ *   v_codes   uint8 [batch, heads * 128, seq64], seq64 = seq rounded up to 64: row
+ *             h*128 + d holds channel d of head h over the keys (zero past seq);
+ *             16-byte aligned.
+ *   v_scales  uint8 [batch, heads, seq64 / 64, 256]: for key block kb (keys
+ *             64 kb .. +63), byte c*128 + (d % 32)*4 + d / 32 is the E8M0 scale of
+ *             channel d over keys 64 kb + 32 c .. +31 (0 for keys past seq).
+ * Element and scale rule as quantize_act with Q4_MXFP8: E = floor(log2 amax) - 8
+ * clamped to [-127, 127], codes E4M3 round-to-nearest-even of x 2**-E saturated
+ * at +-448.  batch, seq, heads >= 0; batch * seq * heads * 128 below 2^31.  An
+ * empty problem (batch, seq or heads 0) returns Q4_OK without looking at the
+ * pointers.
+ */
+Q4_API q4_status attention_fp8_quantize(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk,
+                                        const uint16_t* v, int64_t ldv, int64_t batch, int64_t seq,
+                                        int64_t heads, int64_t head_dim, uint8_t* q_codes,
+                                        uint8_t* q_scales, uint8_t* k_codes, uint8_t* k_scales,
+                                        uint8_t* v_codes, uint8_t* v_scales, void* stream);
+
+/*
+ * attention_fp8 -- the second half: softmax(c Q K^T) V per (batch item, head) on
+ * the operands attention_fp8_quantize wrote, with the FP8 reading of the NVIDIA
+ * Technical Blog summary's quantized attention:
+ *   scores s = q^ . k^ on the block-scaled MFMA (fp32 accumulation);
+ *   online softmax over blocks of 64 keys in key order: per block m' = max(m,
+ *   max c s), p = exp(c s - m'), l' = l exp(m - m') + sum p;
+ *   P quantized to MXFP8 along the keys per 32-key chunk (the rule above) and
+ *   O' = O exp(m - m') + P^ V^ on the block-scaled MFMA;
+ *   out = O / l, bf16 round-to-nearest-even.
+ * Every query attends to the seq keys of its own batch item (no mask otherwise).
+ *
+ *   softmax_scale  c > 0, finite (1/sqrt(128) for standard attention).
+ *   out            bf16 [batch * seq, heads * 128], row stride ldo (multiple of 4,
+ *                  at least heads * 128), 8-byte aligned.
+ * Other arguments as attention_fp8_quantize.  The repair budget the page gives
+ * (rho = 0.005) is not applied: every query runs in FP8.
+ */
+Q4_API q4_status attention_fp8(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                               const uint8_t* k_scales, const uint8_t* v_codes, const uint8_t* v_scales,
+                               int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                               float softmax_scale, uint16_t* out, int64_t ldo, void* stream);
+
 /* Static, NUL-terminated name of a status ("Q4_OK", ...); "unknown" otherwise. */
 Q4_API const char* q4_status_string(q4_status s);
 

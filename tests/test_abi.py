@@ -30,7 +30,7 @@ def header_functions():
     return re.findall(r"Q4_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_every_call():
     names = header_functions()
     for n in ["quantize_act", "pack_weights", "gemm_w4a4", "gemm_w4a4_lowrank", "gemm_w4a16",
               "q4_status_string"]:
@@ -274,3 +274,48 @@ def test_gemm_w4a16_and_pack_rejections():
     assert pw(fmt=1, ts=OK16, K=40) == B.Q4_ERR_SHAPE    # NVFP4: K not a multiple of 16
     assert pw(fmt=0, K=48) == B.Q4_ERR_SHAPE             # MXFP4: K not a multiple of 32
     assert pw(fmt=4, sk=0) == B.Q4_ERR_SHAPE
+
+
+def aq(**kw):
+    a = dict(q=OK16, ldq=256, k=OK16, ldk=256, v=OK16, ldv=256, batch=1, seq=100, heads=2, hd=128, qc=OK16,
+             qs=OK16, kc=OK16, ks=OK16, vc=OK16, vs=OK16)
+    a.update(kw)
+    return lib().attention_fp8_quantize(a["q"], a["ldq"], a["k"], a["ldk"], a["v"], a["ldv"], a["batch"],
+                                        a["seq"], a["heads"], a["hd"], a["qc"], a["qs"], a["kc"], a["ks"],
+                                        a["vc"], a["vs"], None)
+
+
+def test_attention_fp8_quantize_rejections():
+    assert aq(hd=64) == B.Q4_ERR_SHAPE                   # head_dim 128 only
+    assert aq(seq=-1) == B.Q4_ERR_SHAPE
+    assert aq(ldv=200) == B.Q4_ERR_SHAPE                 # row stride below heads * 128
+    assert aq(batch=1 << 10, seq=1 << 14, heads=8) == B.Q4_ERR_SHAPE   # 2^31 code bytes
+    assert aq(v=None) == B.Q4_ERR_NULL
+    assert aq(vs=None) == B.Q4_ERR_NULL
+    assert aq(v=ODD) == B.Q4_ERR_ALIGN                   # V read a dword (two channels) at a time
+    assert aq(ldv=257) == B.Q4_ERR_ALIGN
+    assert aq(kc=P((1 << 20) + 4)) == B.Q4_ERR_ALIGN
+    assert aq(seq=0) == B.Q4_OK and aq(heads=0) == B.Q4_OK and aq(batch=0) == B.Q4_OK
+    assert aq(seq=0, q=None, vc=None) == B.Q4_OK           # empty: pointers not looked at
+
+
+def af(**kw):
+    a = dict(qc=OK16, qs=OK16, kc=OK16, ks=OK16, vc=OK16, vs=OK16, batch=1, seq=100, heads=2, hd=128,
+             c=0.088, out=OK16, ldo=256)
+    a.update(kw)
+    return lib().attention_fp8(a["qc"], a["qs"], a["kc"], a["ks"], a["vc"], a["vs"], a["batch"], a["seq"],
+                               a["heads"], a["hd"], a["c"], a["out"], a["ldo"], None)
+
+
+def test_attention_fp8_rejections():
+    assert af(hd=96) == B.Q4_ERR_SHAPE
+    assert af(c=0.0) == B.Q4_ERR_SHAPE                   # softmax scale must be positive
+    assert af(c=float("inf")) == B.Q4_ERR_SHAPE
+    assert af(c=float("nan")) == B.Q4_ERR_SHAPE
+    assert af(ldo=128) == B.Q4_ERR_SHAPE                 # below heads * 128
+    assert af(out=None) == B.Q4_ERR_NULL
+    assert af(vc=None) == B.Q4_ERR_NULL
+    assert af(out=P((1 << 20) + 4)) == B.Q4_ERR_ALIGN    # 8-byte stores
+    assert af(ldo=258) == B.Q4_ERR_ALIGN
+    assert af(seq=0) == B.Q4_OK and af(batch=0) == B.Q4_OK
+    assert af(seq=0, out=None) == B.Q4_OK
