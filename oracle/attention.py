@@ -14,28 +14,33 @@ rest of the oracle uses (OCP MX v1.0, E4M3 with emax 8):
    straddles two heads).
 2. V: MXFP8 along the key axis, per (batch, head, channel): blocks of 32
    consecutive keys; a last block of fewer than 32 keys is padded with zeros.
-3. Scores s = q^ . k^ (exact products, fp64 sums), logits c * s with c the softmax
-   scale (1 / sqrt(head_dim) by default).  The maximum of each block is taken over
-   the logits, so that the probability of a row's largest logit is exp(0) = 1
-   exactly.
-4. Softmax online over blocks of KEY_BLOCK keys, in key order (the flash-attention
-   recurrence): m' = max(m, max of the block's s), alpha = exp(c (m - m')),
-   p = exp(c (s - m')), l' = alpha l + sum p.  Keys past the sequence end are
-   masked (p = 0).
-5. P is quantized to MXFP8 along the keys, per query and 32-key chunk of the block,
-   before the product with V: O' = alpha O + P^ V^.  Since P is quantized against
-   the running maximum of its block, the block size is part of the result.
-6. Output O / l rounded to bf16.
+3. Scores s = q^ . k^ (exact products, fp64 sums); logits in base 2,
+   t = log2(e) c s, with c the softmax scale (1 / sqrt(head_dim) by default).
+4. Softmax numerators shifted by a power of two: per query, M = ceil(max t) and
+   p = 2**(t - M), in (0, 1], over the seq keys of the query's batch item.
+5. P quantized to MXFP8 along the keys, per query and 32-key chunk (keys 32 j ..
+   32 j + 31, the last chunk padded with zeros): P^.
+6. O = P^ V^ / l with l = sum P^ (the weights actually used, so O is a weighted
+   mean of the V^ rows: one-hot scores return one row exactly), rounded to bf16.
+
+MX quantization commutes with scaling by a power of two (the block exponent moves,
+the codes stay), so in steps 4-5 any integer M at or above the maximum gives the
+same P^ 2**M: P^ is the MXFP8 form of exp(c s) itself, up to the range limits of
+E8M0 and fp32, and does not depend on how an implementation walks the keys (its
+key blocks, their order, or the running maximum it keeps).  The integer shift is
+this reading's choice: quantizing against the exact maximum (p = exp(c (s - m)))
+would make the result depend on where a blocked evaluation sees the maximum.
 
 Readings of the pages' open points are listed in the design notes (attention
-section): the quantization granularities, the key block, the order of the steps,
-and the repair budget, which this function leaves at rho = 0.
+section): the quantization granularities, the shift, the order of the steps, and
+the repair budget, which this function leaves at rho = 0.
 
 Every step that decides a code (an E4M3 rounding, an E8M0 exponent) is taken in
-fp64 here; the kernel takes it in fp32 after its own exp2, so a value within a
-few fp32 ulps of a rounding boundary may round the other way there.  ``attention_fp8``
-therefore also returns, per output element, the largest change such flips could
-make (``ambiguity``), for the parity test to allow.
+fp64 here; a device takes it in fp32, from scores its matrix unit accumulates, so
+a value near a rounding boundary may round the other way there.
+``attention_fp8`` therefore also returns per output element the largest change
+such flips could make (``ambiguity``) and a bound on the rest of the device's
+rounding (``error_bound``), for the parity test to allow.
 """
 
 import numpy as np
@@ -43,8 +48,8 @@ import numpy as np
 from .formats import E4M3_MAX, bf16_to_f64, check_finite, e4m3_decode, e4m3_encode, f32_to_bf16_rne, floor_log2
 from .quant import MX_BLOCK, mxfp8_dequantize, mxfp8_quantize
 
-KEY_BLOCK = 64
 E4M3_EMAX = 8
+LOG2E = 1.4426950408889634
 # default margin of mx8_real: a code whose input lies this close (relative) to a
 # rounding boundary, or a block whose amax lies this close to a power of two,
 # counts as undecided
@@ -52,14 +57,13 @@ AMBIGUOUS_REL = 1e-5
 FP32_TINY = 2.0 ** -126
 
 
-def mx8_real(x, rel=AMBIGUOUS_REL, force_chunk=None):
+def mx8_real(x, rel=AMBIGUOUS_REL):
     """MXFP8 of real (fp64) values along the last axis, whose length is a multiple
     of 32, by the same rule as ``quant.mxfp8_quantize`` (E = floor(log2 amax) - 8,
     E4M3 round to nearest even of x * 2**-E, saturating at 448).
 
     rel: the relative error (scalar, or per element) with which another evaluation
-    of the same values may see them.  force_chunk (optional, bool per block of 32):
-    blocks whose exponent is to be counted as undecided whatever their amax.
+    of the same values may see them (0: it sees them exactly).
 
     Returns (dequantized fp64 values, step, undecided):
     * step: the spacing of the E4M3 grid at each element times 2**E (the most a
@@ -67,7 +71,7 @@ def mx8_real(x, rel=AMBIGUOUS_REL, force_chunk=None):
       exponent is undecided (the grid then halves or doubles),
     * undecided: elements whose code such an evaluation might decide differently
       (the value within rel of a rounding boundary, or the block's amax within rel
-      of a power of two, or a forced block).
+      of a power of two).
     """
     x = np.asarray(x, dtype=np.float64)
     check_finite(x, "attention operand")
@@ -93,16 +97,12 @@ def mx8_real(x, rel=AMBIGUOUS_REL, force_chunk=None):
     frac = u / spacing - np.floor(u / spacing)
     near_mid = np.abs(frac - 0.5) * spacing <= relb * np.maximum(u, spacing)
     undecided = near_mid & (u < E4M3_MAX)
-    # amax within rel of a power of two, from either side.  amax = 1 exactly is
-    # decided here: it is the chunk holding the row's running maximum, whose
-    # probability exp(0) is exactly 1 in any evaluation (a near tie for that
-    # maximum is the caller's to force)
+    # amax within rel of a power of two, from either side (an amax exactly on one
+    # is undecided too unless it carries no error)
     relc = relb.max(axis=-1)
     lo = np.ldexp(1.0, lg)
     dist = np.minimum(amax - lo, 2.0 * lo - amax)
-    amb_scale = pos & (amax != 1.0) & (dist <= relc * np.where(pos, amax, 1.0))
-    if force_chunk is not None:
-        amb_scale = amb_scale | np.asarray(force_chunk, dtype=bool)
+    amb_scale = pos & (dist <= relc * np.where(pos, amax, 1.0)) & (relc > 0)
     undecided = undecided | amb_scale[..., None]
     step = spacing * scale * np.where(amb_scale[..., None], 2.0, 1.0)
     return vals.reshape(shape), step.reshape(shape), undecided.reshape(shape)
@@ -135,31 +135,30 @@ def quantize_v(v_bits, batch, seq, heads, head_dim):
 
 
 def attention_fp8(q_bits, k_bits, v_bits, batch, seq, heads, head_dim=128, scale=None,
-                  key_block=KEY_BLOCK, quantize=True, query_rows=None, score_err=0.0, sum_err=0.0):
+                  quantize=True, query_rows=None, score_err=0.0, sum_err=0.0, shift=0):
     """FP8 attention (steps 1-6 above) of Q, K, V given as bf16 bits
     [batch * seq, heads * head_dim] (token-major, head h in columns
     h * head_dim .. +head_dim, as the QKV projection writes them).
 
     Returns dict(out_bits uint16 [batch * seq, heads * head_dim] (bf16 RNE of o),
-    o fp64 (before rounding), l fp64 [batch, heads, seq], and two per-element
-    bounds for comparing another evaluation of the same steps in finite precision:
+    o fp64 (before rounding), l fp64 [batch, heads, seq] (sum P^, relative to
+    2**M), and two per-element bounds for comparing another evaluation of the same
+    steps in finite precision:
     * ambiguity: the most that codes or exponents of P it may decide the other way
       can move o (values within its error of a decision boundary),
-    * error_bound: the most its rounding can move o otherwise: the errors of the
-      probabilities (through l and the rescaling factors) and of the P V sums.
+    * error_bound: the most the rounding of its sums of P^ V^ and of P^ can move o.
     score_err is that evaluation's error bound on a score, relative to
     sum_d |q^_d k^_d| (its matrix unit's accumulation error), and sum_err the same
-    for the sums of P^ V^ (relative to sum |p^ v^|); its fp32 exp2 and logit
-    arithmetic add a relative 2**-20 (1 + |c s| + |c m|) to each probability.
-    Neither bound changes o.
+    for the sums of P^ V^ and of P^ (relative to the sums of magnitudes); its fp32
+    exp2 of an fp32 exponent adds a relative 2**-20 (|t - M| + 1) to each
+    probability (nothing for an integer exponent).  Neither bound changes o.
 
     quantize=False skips every quantization (steps 1, 2 and 5 become identities):
-    the recurrence then computes exact softmax attention, which the tests use to pin
-    steps 3, 4 and 6.
-
-    query_rows (optional, indices into the seq queries of every batch item): only
-    those queries are computed (every query is independent of the others); the
-    returned arrays then hold batch * len(query_rows) rows, batch-major.
+    the result is then exact softmax attention, which the tests use to pin steps 3,
+    4 and 6.  query_rows (optional, indices into the seq queries of every batch
+    item): only those queries are computed (every query is independent of the
+    others); the returned arrays then hold batch * len(query_rows) rows,
+    batch-major.  shift: an integer added to every M (the result does not change).
     """
     width = heads * head_dim
     c = 1.0 / np.sqrt(head_dim) if scale is None else float(scale)
@@ -180,72 +179,48 @@ def attention_fp8(q_bits, k_bits, v_bits, batch, seq, heads, head_dim=128, scale
     rows = np.arange(seq) if query_rows is None else np.asarray(query_rows, dtype=np.int64)
     q = q[:, rows]
     nq = len(rows)
+    seq32 = -(-seq // MX_BLOCK) * MX_BLOCK
     o = np.zeros((batch, nq, heads, head_dim))
     amb = np.zeros_like(o)
-    lsum = np.zeros((batch, heads, nq))
     err = np.zeros_like(o)
-    nblocks = -(-seq // key_block)
+    lsum = np.zeros((batch, heads, nq))
     for b in range(batch):
         for h in range(heads):
             qh, kh = q[b, :, h, :], k[b, :, h, :]
-            s_all = qh @ kh.T                                          # [queries, seq]
-            ds = score_err * (np.abs(qh) @ np.abs(kh).T)               # score error bounds
-            dsmax = ds.max(axis=1)
             v_h = vt[b, h * head_dim:(h + 1) * head_dim, :seq].T       # [seq keys, head_dim]
-            m = np.full(nq, -np.inf)
-            l = np.zeros(nq)
-            acc = np.zeros((nq, head_dim))
-            acc_abs = np.zeros((nq, head_dim))                         # sum of |p^ v^|, rescaled
-            bnd = np.zeros((nq, head_dim))
-            for blk in range(nblocks):
-                j0 = blk * key_block
-                j1 = min(j0 + key_block, seq)
-                s = s_all[:, j0:j1]
-                m_new = np.maximum(m, s.max(axis=1))
-                alpha = np.where(np.isfinite(m), np.exp(c * (m - m_new)), 0.0)
-                p = np.exp(c * (s - m_new[:, None]))
-                if quantize:
-                    # below fp32's normal range a probability counts as zero: it moves
-                    # o by less than 2**-126 |v|
-                    p = np.where(p < FP32_TINY, 0.0, p)
-                l = alpha * l + p.sum(axis=1)
-                if quantize:
-                    width_pad = -(-(j1 - j0) // MX_BLOCK) * MX_BLOCK
-                    pp = np.zeros((nq, width_pad))
-                    pp[:, :j1 - j0] = p
-                    # relative error of each probability as the other evaluation sees
-                    # it: its score's and the maximum's errors, and fp32's exp2
-                    rel = np.full((nq, width_pad), 1.0)
-                    rel[:, :j1 - j0] = (c * (ds[:, j0:j1] + dsmax[:, None])
-                                        + 2.0 ** -20 * (1 + np.abs(c * s) + np.abs(c * m_new)[:, None]))
-                    # the chunk holding the row maximum (amax exactly 1) loses it when
-                    # a rival score (in another chunk, or an earlier block's maximum)
-                    # lies within the two scores' errors: its exponent is undecided
-                    # then.  Rounding the logits to fp32 keeps their order, so exact
-                    # scores (score_err = 0) never trade places.
-                    cmax = pp.reshape(nq, -1, MX_BLOCK).max(axis=2)
-                    top = cmax == 1.0
-                    rival = np.maximum(np.where(top, 0.0, cmax).max(axis=1), alpha)
-                    tie = (score_err > 0) & (rival >= np.exp(-2.0 * c * dsmax))
-                    ph, step, und = mx8_real(pp, rel, force_chunk=top & tie[:, None])
-                    ph, step, und = ph[:, :j1 - j0], step[:, :j1 - j0], und[:, :j1 - j0]
-                    flips = np.where(und, step, 0.0) @ np.abs(v_h[j0:j1])
-                else:
-                    ph = p
-                    flips = 0.0
-                acc = alpha[:, None] * acc + ph @ v_h[j0:j1]
-                acc_abs = alpha[:, None] * acc_abs + np.abs(ph) @ np.abs(v_h[j0:j1])
-                bnd = alpha[:, None] * bnd + flips
-                m = m_new
-            o[b, :, h, :] = acc / l[:, None]
-            amb[b, :, h, :] = bnd / l[:, None]
-            # e bounds the relative error of every probability, of every rescaling
-            # factor and of l: O' = sum A' p^ v / sum A' p' moves by at most
-            # (2 e + sum_err) sum |p^ v^| / l + 4 e |O|
-            e = c * 2.0 * dsmax + 2.0 ** -20 * (1 + 2.0 * np.abs(c * s_all).max(axis=1))
-            err[b, :, h, :] = ((2.0 * e + sum_err)[:, None] * acc_abs / l[:, None]
-                               + 4.0 * e[:, None] * np.abs(o[b, :, h, :]))
+            t = LOG2E * c * (qh @ kh.T)                                # [queries, seq]
+            M = np.ceil(t.max(axis=1)) + shift
+            p = np.exp2(t - M[:, None])
+            if quantize:
+                # below fp32's normal range a probability counts as zero: it moves
+                # o by less than 2**-126 |v|
+                p = np.where(p < FP32_TINY, 0.0, p)
+            if quantize:
+                # relative error of each probability as another evaluation sees it:
+                # its score's error, and fp32's rounding of the exponent t - M (an
+                # integer exponent, as for scores of 0, is exact)
+                tm = t - M[:, None]
+                rel = (c * score_err * (np.abs(qh) @ np.abs(kh).T)
+                       + 2.0 ** -20 * (np.abs(tm) + (tm != np.round(tm))))
+                pp = np.zeros((nq, seq32))
+                pp[:, :seq] = p
+                relp = np.zeros((nq, seq32))
+                relp[:, :seq] = rel
+                ph, step, und = mx8_real(pp, relp)
+                ph, step, und = ph[:, :seq], step[:, :seq], und[:, :seq]
+            else:
+                ph, step, und = p, np.zeros_like(p), np.zeros(p.shape, dtype=bool)
+            l = ph.sum(axis=1)
+            acc = ph @ v_h
+            o_h = acc / l[:, None]
+            o[b, :, h, :] = o_h
             lsum[b, h] = l
+            # a code decided the other way moves p^_j by at most step_j, so O = sum p^ v
+            # / sum p^ by at most step_j (|v_j| + |O|) / l; the sums of p^ v^ and of p^
+            # (the matrix unit's) move O by sum_err (sum |p^ v^| / l + |O|)
+            amb[b, :, h, :] = (np.where(und, step, 0.0) @ np.abs(v_h)
+                               + np.where(und, step, 0.0).sum(axis=1)[:, None] * np.abs(o_h)) / l[:, None]
+            err[b, :, h, :] = sum_err * ((np.abs(ph) @ np.abs(v_h)) / l[:, None] + np.abs(o_h))
     o = o.reshape(batch * nq, width)
     return dict(out_bits=f32_to_bf16_rne(o), o=o, ambiguity=amb.reshape(batch * nq, width),
                 error_bound=err.reshape(batch * nq, width), l=lsum)

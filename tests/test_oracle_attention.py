@@ -22,14 +22,14 @@ def _qkv(seed, batch, seq, heads, d=128, sd=1.0):
     return tuple(_bits(sd * rng.standard_normal(shape)) for _ in range(3))
 
 
-@pytest.mark.parametrize("seq,key_block", [(150, 64), (64, 64), (37, 64), (200, 32)])
-def test_unquantized_recurrence_is_softmax_attention(seq, key_block):
-    """quantize=False: the blocked online recurrence (steps 3, 4, 6) must equal
-    softmax(c Q K^T) V computed with scipy's softmax, per batch item and head,
-    including a ragged last block."""
+@pytest.mark.parametrize("seq", [150, 64, 37, 1])
+def test_unquantized_is_softmax_attention(seq):
+    """quantize=False: steps 3, 4 and 6 (base-2 logits, the power-of-two shift, the
+    normalization) must equal softmax(c Q K^T) V computed with scipy's softmax, per
+    batch item and head."""
     batch, heads, d = 2, 2, 128
     q, k, v = _qkv(1, batch, seq, heads, sd=2.0)
-    r = A.attention_fp8(q, k, v, batch, seq, heads, d, key_block=key_block, quantize=False)
+    r = A.attention_fp8(q, k, v, batch, seq, heads, d, quantize=False)
     c = 1.0 / np.sqrt(d)
     qf = bf16_to_f64(q).reshape(batch, seq, heads, d)
     kf = bf16_to_f64(k).reshape(batch, seq, heads, d)
@@ -56,15 +56,14 @@ def test_uniform_scores_average_the_quantized_values():
     expect = np.broadcast_to(vhat.mean(axis=1), (seq, heads * d))
     np.testing.assert_allclose(r["o"], expect, rtol=1e-12, atol=1e-15)
     assert np.all(r["ambiguity"] == 0)
-    assert np.all(r["l"] == seq)
+    assert np.all(r["l"] == seq)            # M = 0, every p^ = 1
 
 
 def test_one_hot_scores_select_one_value_row():
     """Query i scores a * e_{pi(i)} against keys e_j (one-hot, exact in MXFP8): one
     logit per row is a c = 64 larger than the rest, so every other probability is
-    below e^-64 and O row i is row pi(i) of the dequantized V.  pi puts the
-    maximum in every key block, so the running maximum grows mid-sequence and the
-    rescaling of earlier blocks is exercised."""
+    below e^-64 and, l being the sum of the quantized weights, O row i is row pi(i)
+    of the dequantized V, whatever the quantization error of that weight."""
     batch, seq, heads, d = 1, 128, 1, 128
     rng = np.random.default_rng(3)
     pi = rng.permutation(seq)
@@ -79,28 +78,17 @@ def test_one_hot_scores_select_one_value_row():
     np.testing.assert_allclose(r["o"], vhat[pi], rtol=1e-20, atol=1e-24)
 
 
-def test_blocking_is_invisible_while_the_maximum_stays_put():
-    """When every row's maximum logit sits in the first key block, the running
-    maximum never changes, P is quantized against the final maximum in every
-    block, and key blocks of 64 give the same O as one block over all keys (the
-    MX chunks of 32 keys are the same either way)."""
-    batch, seq, heads, d = 1, 192, 2, 128
-    rng = np.random.default_rng(5)
-    qf = np.abs(rng.standard_normal((seq, heads * d)))     # positive queries
-    kf = rng.standard_normal((seq, heads * d))
-    kf[3] = 4.0                                            # key 3 wins every row
-    q, k = _bits(qf), _bits(kf)
-    _, _, v = _qkv(6, batch, seq, heads)
-    r64 = A.attention_fp8(q, k, v, batch, seq, heads, d, key_block=64)
-    r1 = A.attention_fp8(q, k, v, batch, seq, heads, d, key_block=seq)
-    np.testing.assert_allclose(r64["o"], r1["o"], rtol=1e-12, atol=1e-15)
-    # and the maximum really moves when it does not sit first: the results differ
-    kf2 = kf.copy()
-    kf2[3] = kf[4]
-    kf2[150] = 4.0
-    r64b = A.attention_fp8(q, _bits(kf2), v, batch, seq, heads, d, key_block=64)
-    r1b = A.attention_fp8(q, _bits(kf2), v, batch, seq, heads, d, key_block=seq)
-    assert np.abs(r64b["o"] - r1b["o"]).max() > 0
+@pytest.mark.parametrize("shift", [1, 7, -3])
+def test_power_of_two_shift_changes_nothing(shift):
+    """MX quantization commutes with powers of two, so shifting M by an integer
+    leaves P^ 2**M, l 2**M and O unchanged, bit for bit (the property that makes
+    the result independent of how an implementation walks the keys)."""
+    batch, seq, heads, d = 2, 100, 2, 128
+    q, k, v = _qkv(5, batch, seq, heads, sd=2.0)
+    r0 = A.attention_fp8(q, k, v, batch, seq, heads, d)
+    r1 = A.attention_fp8(q, k, v, batch, seq, heads, d, shift=shift)
+    np.testing.assert_array_equal(r0["o"], r1["o"])
+    np.testing.assert_array_equal(r0["l"], r1["l"] * 2.0 ** shift)
 
 
 def test_real_valued_mx8_matches_the_pinned_mxfp8_quantizer():
@@ -152,15 +140,16 @@ def test_two_live_keys_worked_by_hand(seq, second):
     """A worked example whose codes are derived by hand.  Query 0 is 14 e_0 (14 =
     1.75 * 2**3 is exact in E4M3, so its MXFP8 form is exact); key 0 is e_0, key
     `second` is 0 and every other key is -64 e_0.  With c = 1/sqrt(128):
-      logits 14 c = 1.2374..., 0, and -79.2 (probabilities below e^-80: zero codes);
-      row maximum 14 c -> p = 1 for key 0, p = exp(-14 c) = 0.290110... for key
-      `second`, sum l = 1.290110... (the -79 keys add < 1e-33);
-      chunk of key 0: amax 1, E = 0 - 8, code of 1 * 2**8 = 256 exact;
-      chunk of key `second`: amax 0.2901, E = floor(log2 0.2901) - 8 = -10,
-      0.2901 * 2**10 = 297.07 lies in [256, 512) where E4M3 steps by 32, so it
-      rounds to 288: p^ = 288 / 1024 = 0.28125.
+      base-2 logits t = log2(e) c s: 14 c log2(e) = 1.78525..., 0, and -114.3;
+      M = ceil(1.785) = 2, so p = 2**-0.21475 = 0.861763 for key 0, 2**-2 = 0.25
+      for key `second`, below 2**-116 for the rest (zero codes);
+      chunk of key 0: amax 0.8618, E = floor(log2 0.8618) - 8 = -9, 0.8618 * 2**9 =
+      441.2 lies in [256, 512) where E4M3 steps by 32, so it rounds to 448 (the
+      midpoint is 432): p^ = 448 / 512 = 0.875;
+      chunk of key `second`: 0.25 = 2**-2, E = -10, code 256 exact: p^ = 0.25;
+      l = 0.875 + 0.25 = 1.125.
     V rows 0 and `second` are exact in MXFP8 along the keys (values 1 and 2 in
-    channel d, all other keys 0), so O[0, d] = (1 * 1 + 0.28125 * 2) / l."""
+    channel d, all other keys 0), so O[0, d] = (0.875 * 1 + 0.25 * 2) / 1.125 = 11/9."""
     batch, heads, d = 1, 1, 128
     qf = np.zeros((seq, d))
     qf[0, 0] = 14.0
@@ -172,6 +161,5 @@ def test_two_live_keys_worked_by_hand(seq, second):
     vf[0, :] = 1.0
     vf[second, :] = 2.0
     r = A.attention_fp8(_bits(qf), _bits(kf), _bits(vf), batch, seq, heads, d)
-    l = 1.0 + np.exp(-14.0 / np.sqrt(128.0))
-    np.testing.assert_allclose(r["o"][0], (1.0 + 0.28125 * 2.0) / l, rtol=1e-14)
-    np.testing.assert_allclose(r["l"][0, 0, 0], l, rtol=1e-14)
+    np.testing.assert_allclose(r["o"][0], 11.0 / 9.0, rtol=1e-14)
+    np.testing.assert_allclose(r["l"][0, 0, 0], 1.125, rtol=1e-14)
