@@ -3,8 +3,13 @@
 // writes them (bf16, token-major, head h in columns h*128 .. +128) and are
 // quantized to MXFP8 (E4M3 elements, one E8M0 scale per 32): Q and K along
 // head_dim, V along the keys, transposed.  The attention kernel then runs both
-// products on the block-scaled MFMA with an online softmax over blocks of 64 keys,
-// the probabilities quantized to MXFP8 per 32-key chunk in registers.
+// products on the block-scaled MFMA: per query, base-2 logits t = c log2(e) s, the
+// probabilities 2**(t - M) for an integer shift M at or above the logits, MXFP8
+// along the keys per 32-key chunk (P^), and O = P^ V^ / sum P^.  Because MX
+// quantization commutes with powers of two, any such M gives the same P^ up to
+// 2**M, so the kernel walks the keys in blocks of 64 with a running integer M and
+// folds the shift between blocks into the E8M0 scales it hands the MFMA: no
+// rescaling of O between blocks.
 //
 // Layouts (bytes):
 //   Q, K codes [tokens, heads*128], scales [tokens, heads*4] (the MXFP8 row layout);
@@ -23,11 +28,14 @@
 // 8-bit MFMA wants in lane half h of its B operand for a 64-element K step.  So the
 // probabilities, encoded to E4M3 in place, are the B operand of O^T = V^T P^T with
 // no trip through LDS; lane half h supplies the scale of key chunk h (= tile h).
-// K blocks (64 keys x 128 bytes) and V^T blocks (128 channels x 64 bytes) are
-// loaded straight into two LDS stages, 16-byte chunks XOR-swizzled per row so the
-// fragment reads spread over the 64 banks.
+// The sum of P^ comes from one more MFMA against a tile of ones.  K blocks (64 keys
+// x 128 bytes) and V^T blocks (128 channels x 64 bytes) are loaded straight into
+// two LDS stages, 16-byte chunks XOR-swizzled per row so the fragment reads spread
+// over the 64 banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "q4_device.h"
 #include "q4_internal.h"
@@ -59,16 +67,11 @@ __device__ __forceinline__ int tile_key(int t, int i) {
   return 32 * t + 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
 }
 
-// max and sum of x over the lane pair (l, l ^ 32).  The swap leaves x of one lane
-// of the pair in each of its two results, so the pair's combination is symmetric
-// in them.
+// max of x over the lane pair (l, l ^ 32).  The swap leaves x of one lane of the
+// pair in each of its two results, so their max is the pair's.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // E8M0 exponent of a block whose largest magnitude is pmax (fp32, >= 0), for E4M3
@@ -162,13 +165,19 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) voff[hf] = kKBytes + i * 64 + (((2 * hf + h) ^ swz_v(i)) << 4);
 
-  v16f o[4];
+  // O^T and l = sum of the quantized probabilities, both relative to 2**mref: the
+  // exponent shift of the first block (kept until a far larger maximum comes)
+  v16f o[4], lt = v16f{};
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = v16f{};
-  float m = -__builtin_inff(), l = 0.0f;
+  float mcur = -__builtin_inff(), mref = -__builtin_inff();
   const int rem = a.seq - (nkb - 1) * kKB;          // keys of the last block
+  // the A operand of the l tile: every element E4M3 1.0 (0x38), scale 2**0
+  const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                       0x38383838, 0x38383838, 0x38383838, 0x38383838};
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto block = [&](int kb, auto mask_c) {
+    constexpr bool kMask = decltype(mask_c)::value;
     const int st = kb & 1;
     // block kb has landed (this wave's part), and every wave is done with block kb-1
     wait_vmem();
@@ -196,49 +205,54 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
     Q4_ATTN_SCORE_STEP(1)
 #undef Q4_ATTN_SCORE_STEP
 
-    // ---- online softmax in the log2 domain: t = c2 s; element k of tile t is key
-    // 32 t + 16 h + k of the block
-    float t0[16], t1[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      t0[k] = s0[k] * a.c2;
-      t1[k] = s1[k] * a.c2;
-    }
-    if (kb == nkb - 1 && rem < kKB) {
+    // ---- probabilities.  Element k of tile t is key 32 t + 16 h + k of the block;
+    // tile t is 32-key chunk t.  Keys past the sequence (last block only) get -inf.
+    if constexpr (kMask) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        if (16 * h + k >= rem) t0[k] = -__builtin_inff();
-        if (32 + 16 * h + k >= rem) t1[k] = -__builtin_inff();
+        if (16 * h + k >= rem) s0[k] = -__builtin_inff();
+        if (32 + 16 * h + k >= rem) s1[k] = -__builtin_inff();
       }
     }
-    float mx0 = t0[0], mx1 = t1[0];
+    float mx0 = s0[0], mx1 = s1[0];
 #pragma unroll
     for (int k = 1; k < 16; ++k) {
-      mx0 = fmaxf(mx0, t0[k]);
-      mx1 = fmaxf(mx1, t1[k]);
+      mx0 = fmaxf(mx0, s0[k]);
+      mx1 = fmaxf(mx1, s1[k]);
     }
     mx0 = pair_max(mx0);
     mx1 = pair_max(mx1);
-    const float m_new = fmaxf(m, fmaxf(mx0, mx1));
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    // the E8M0 scales of the two 32-key chunks (tile t = chunk t), from their
-    // largest probabilities
-    const int e0 = mx8_exponent(__builtin_amdgcn_exp2f(mx0 - m_new));
-    const int e1 = mx8_exponent(__builtin_amdgcn_exp2f(mx1 - m_new));
-    const float down0 = exp2i(-e0), down1 = exp2i(-e1);
-    float psum = 0.0f;
+    // the integer exponent shift M >= the base-2 logits seen so far (any integer
+    // gives the same quantized weights up to a power of two, which the MFMA's
+    // scale absorbs)
+    mcur = fmaxf(mcur, __builtin_ceilf(fmaxf(mx0, mx1) * a.c2));
+    if (mref == -__builtin_inff()) mref = mcur;
+    if (__builtin_amdgcn_ballot_w64(mcur - mref > 100.0f)) {
+      // keep the scale bytes below 255: move O and l to the new shift (exactly).
+      // Rare: the empty asm keeps it a branch, not multiplies on every block.
+      asm volatile("" ::: "memory");
+      const float f = mcur - mref > 100.0f ? exp2i((int)(mref - mcur)) : 1.0f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[dt][k] *= f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lt[k] *= f;
+      mref = mcur - mref > 100.0f ? mcur : mref;
+    }
+    // the chunks' E8M0 exponents from their largest probabilities, and the codes:
+    // p * 2**-E = 2**(c2 s - (M + E)) (M + E is an integer: one rounding, in the fma)
+    const int e0 = mx8_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(mx0, a.c2, -mcur)));
+    const int e1 = mx8_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(mx1, a.c2, -mcur)));
+    const float sh0 = -(mcur + (float)e0), sh1 = -(mcur + (float)e1);
     uint32_t pw[8];
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
       float v0[4], v1[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(t0[4 * wd + j] - m_new);
-        const float p1 = __builtin_amdgcn_exp2f(t1[4 * wd + j] - m_new);
-        psum += p0 + p1;
-        v0[j] = fminf(p0 * down0, 448.0f);
-        v1[j] = fminf(p1 * down1, 448.0f);
+        v0[j] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[4 * wd + j], a.c2, sh0)), 448.0f);
+        v1[j] = fminf(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[4 * wd + j], a.c2, sh1)), 448.0f);
       }
       int x0 = __builtin_amdgcn_cvt_pk_fp8_f32(v0[0], v0[1], 0, false);
       x0 = __builtin_amdgcn_cvt_pk_fp8_f32(v0[2], v0[3], x0, true);
@@ -247,16 +261,14 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
       pw[wd] = (uint32_t)x0;
       pw[4 + wd] = (uint32_t)x1;
     }
-    l = l * alpha + psum;
     const v8i pf = v8i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-    const int psc = (h ? e1 : e0) + 127;
+    // lane half h supplies the scale of chunk h, relative to 2**mref
+    const int psc = (h ? e1 : e0) + (int)(mcur - mref) + 127;
 
-    // ---- O^T = alpha O^T + V^T P^T, four 32-channel tiles
+    // ---- O^T += V^T P^T (four 32-channel tiles) and l += sum P^ (the ones tile)
     const uint32_t vsc = *reinterpret_cast<const uint32_t*>(sb + kVsOff + 4 * (32 * h + i));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) o[dt][k] *= alpha;
       const u32x4 a0 = ld16(sb + voff[0] + dt * 2048), a1 = ld16(sb + voff[1] + dt * 2048);
       const v8i vf = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
       switch (dt) {   // the byte of the scale dword is an immediate
@@ -266,12 +278,17 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
         default: o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[3], kFmtE4M3, kFmtE4M3, 3, (int)vsc, 0, psc); break;
       }
     }
-  }
+    lt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lt, kFmtE4M3, kFmtE4M3, 0, 127, 0, psc);
+  };
+
+  for (int kb = 0; kb + 1 < nkb; ++kb) block(kb, std::false_type{});
+  if (rem < kKB) block(nkb - 1, std::true_type{});
+  else block(nkb - 1, std::false_type{});
 
   // ---- O / l in bf16: lane (i, h) holds channels 32 dt + 8 q + 4 h + r of query i
   const int query = q0 + kQW * wave + i;
   if (query >= a.seq) return;
-  const float inv = 1.0f / pair_sum(l);
+  const float inv = 1.0f / lt[0];
   uint16_t* dst = a.out + (tok0 + query) * a.ldo + hd * kHD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)

@@ -7,11 +7,12 @@ sampled queries.
 
 The bound.  The kernel decides every E4M3 code and E8M0 exponent of P itself, in
 fp32, from scores its matrix unit accumulates: the block-scaled FP8 MFMA sums its
-products with an error of up to 4e-5 of sum |terms| (measured on gfx950 over
-2^18 dot products of 128; the median is 1e-6), not fp32's 1e-7.  The oracle
-(score_err, sum_err = KAPPA = 1e-4) turns that into, per element, the codes that
-may round the other way (ambiguity) and the rounding of everything else
-(error_bound).  Two kinds of case:
+products with an error well above fp32's (measured on gfx950: up to 7.3e-5 of
+sum |terms| over 2^19 dot products of 128 to 512 Gaussian and wide-range operands,
+median ~5e-6; up to 1.1e-4 in this kernel's P V sums).  The oracle takes
+score_err = sum_err = KAPPA = 2^-12 (twice the largest seen) and turns it into,
+per element, the codes that may round the other way (ambiguity) and the rounding
+of everything else (error_bound).  Two kinds of case:
 * exact scores: Q and K hold integers (each 32-block an 8 and values in -7..7,
   exact in MXFP8), whose products and sums the MFMA forms exactly, so only fp32's
   exp2 and the P V sums are inexact: a tight bound.
@@ -33,7 +34,7 @@ from _gpu import bf16_dev, bits16, device, say, u8
 pytestmark = pytest.mark.gpu
 
 D = 128
-KAPPA = 1e-4     # error bound of the FP8 MFMA's sums, relative to sum |terms|
+KAPPA = 2.0 ** -12   # error bound of the FP8 MFMA's sums, relative to sum |terms|
 
 
 def exact_qk_bits(seed, batch, seq, heads):
