@@ -15,7 +15,8 @@
  *
  * Conventions shared by every call:
  *   - Every pointer argument is a DEVICE pointer on the current HIP device, owned
- *     by the caller.  The library never allocates and keeps no state.
+ *     by the caller.  The library's one allocation is NVFP4's 4 KB scratch (see
+ *     quantize_act); nothing else is allocated, and nothing is kept between calls.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - 4-bit codes are packed two per byte along K: element 2j in the low nibble,
  *     element 2j+1 in the high nibble; a row of K elements is K/2 bytes.  FP4 codes
@@ -113,13 +114,19 @@ typedef enum q4_out {
  *                 (else Q4_ERR_FORMAT).
  *   x             bf16 [M, K], row stride ldx elements.  16-byte aligned, ldx a
  *                 multiple of 8, ldx >= K.
- *   M, K          0 <= M <= 2^30; K >= 0 and a multiple of 32.
+ *   M, K          0 <= M <= 2^30; K >= 0 and a multiple of 32 (NVFP4 with r = 0:
+ *                 of 16, its block).
  *   codes  (out)  uint8 [M, K/2] (MXFP8: [M, K]).  16-byte aligned.
  *   scales (out)  MXFP4, MXFP8: uint8 E8M0 [M, K/32]; NVFP4: uint8 E4M3 [M, K/16];
  *                 INT4_SYM: float [M] (passed through this pointer).
  *                 4-byte aligned.
- *   tensor_scale  NVFP4: float[1], written with s_t (also used as the amax
- *                 accumulator while the call runs).  MXFP4: ignored, may be NULL.
+ *   tensor_scale  NVFP4: float[1], written with s_t.  Other formats: ignored, may
+ *                 be NULL.  NVFP4 runs two launches: the tensor amax as one partial
+ *                 maximum per workgroup into a 4 KB scratch, then the encode pass
+ *                 (with the fused t when r > 0), which reduces them first.  The
+ *                 scratch is allocated once per (device, stream) on the first
+ *                 NVFP4 call (this one or pack_weights) on that stream and kept
+ *                 until the process ends; Q4_ERR_ALLOC if that fails.
  *   l1t           r > 0: bf16 L1^T [r, K] (the down-projection stored
  *                 in-features-contiguous, nn.Linear layout), 16-byte aligned.
  *                 r = 0: ignored.
@@ -181,12 +188,14 @@ Q4_API q4_status quantize_act_smooth(q4_format fmt, const uint16_t* x, int64_t M
  *                     stride_k = N, stride_n = 1 for row-major [K, N]).  Strides >= 1.
  *                     w 2-byte aligned; with stride_k = 1, stride_n a multiple of 8
  *                     and w 16-byte aligned the rows are read 16 bytes at a time.
- *   K, N              K a multiple of 32 (MXFP4, NVFP4) or 64 (INT4_G64).
+ *   K, N              K a multiple of 32 (MXFP4, INT4_SYM, MXFP8), 16 (NVFP4) or
+ *                     64 (INT4_G64).
  *   codes  (out)      uint8 [N, K/2] (MXFP8: [N, K]), 16-byte aligned.
  *   scales (out)      MXFP4, MXFP8: uint8 [N, K/32]; NVFP4: uint8 E4M3 [N, K/16];
  *                     INT4_G64: bf16 [N, K/64]; INT4_SYM: float [N].  4-byte aligned.
  *   zeros  (out)      INT4_G64: bf16 [N, K/64] (integers 0..15); else ignored.
- *   tensor_scale(out) NVFP4: float[1] (s_t of the weight); else ignored.
+ *   tensor_scale(out) NVFP4: float[1] (s_t of the weight); else ignored.  NVFP4
+ *                     uses the stream's 4 KB scratch, as quantize_act does.
  */
 Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64_t N,
                        int64_t stride_k, int64_t stride_n, uint8_t* codes, void* scales,
