@@ -46,8 +46,39 @@ __device__ __forceinline__ uint32_t nv_encode_pair(uint32_t r, uint32_t pair, fl
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v0, v1, 1.0f, SEL);
 }
 
-// Encode 16 bf16 values (8 dwords) of one NVFP4 block.
+// The correctly rounded quotient x / den from y = RN(1/den) (Markstein: with y the
+// correctly rounded reciprocal and q = RN(x y) within an ulp of x / den, the
+// residual r = x - den q is exact in one fma and RN(q + r y) is RN(x / den); den,
+// y and the quotients that decide a code are normal fp32 numbers here).
+__device__ __forceinline__ float nv_quotient(float x, float den, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-den, q, x);
+  return __builtin_fmaf(r, y, q);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t nv_encode_pair_rcp(uint32_t r, uint32_t pair, float den, float y) {
+  const float v0 = nv_quotient(bf16_lo(pair), den, y), v1 = nv_quotient(bf16_hi(pair), den, y);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v0, v1, 1.0f, SEL);
+}
+
+// Encode 16 bf16 values (8 dwords) of one NVFP4 block: x / den for each, rounded
+// to E2M1.  With den in [2^-100, 2^100] the quotients go through the reciprocal
+// (one IEEE division per block); otherwise, and for den = 0 (signed zero codes),
+// through the IEEE division per element.
 __device__ __forceinline__ void nv_encode16(const uint32_t* w, float den, uint32_t* out2) {
+  if (den >= 0x1p-100f && den <= 0x1p100f) {
+    const float y = 1.0f / den;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      uint32_t r = 0;
+      r = nv_encode_pair_rcp<0>(r, w[4 * d + 0], den, y);
+      r = nv_encode_pair_rcp<1>(r, w[4 * d + 1], den, y);
+      r = nv_encode_pair_rcp<2>(r, w[4 * d + 2], den, y);
+      r = nv_encode_pair_rcp<3>(r, w[4 * d + 3], den, y);
+      out2[d] = r;
+    }
+    return;
+  }
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
     uint32_t r = 0;
