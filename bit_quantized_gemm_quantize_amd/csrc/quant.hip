@@ -595,13 +595,24 @@ __global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __re
     return scale;
   };
   uint8_t* out = codes + r * (K >> 1);
-  auto encode8 = [&](int64_t c, const uint32_t* w, float scale) {
+  // x / scale is the IEEE quotient either way: through the row's reciprocal
+  // (nv_quotient) for scale in [2^-100, 2^100], else by division
+  auto encode8 = [&](int64_t c, const uint32_t* w, float scale, float y) {
     uint32_t packed = 0;
+    if (scale >= 0x1p-100f && scale <= 0x1p100f) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
-      const float q = fminf(fmaxf(__builtin_rintf(v / scale), -8.0f), 7.0f);
-      packed |= ((uint32_t)(int)q & 0xFu) << (4 * j);
+      for (int j = 0; j < 8; ++j) {
+        const float v = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+        const float q = fminf(fmaxf(__builtin_rintf(nv_quotient(v, scale, y)), -8.0f), 7.0f);
+        packed |= ((uint32_t)(int)q & 0xFu) << (4 * j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+        const float q = fminf(fmaxf(__builtin_rintf(v / scale), -8.0f), 7.0f);
+        packed |= ((uint32_t)(int)q & 0xFu) << (4 * j);
+      }
     }
     *reinterpret_cast<uint32_t*>(out + 4 * c) = packed;
   };
@@ -618,10 +629,10 @@ __global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __re
     }
 #pragma unroll
     for (int i = 0; i < kRegChunks; ++i) m = max(m, bf16_amax_bits<4>(w[i]));
-    const float scale = wave_scale(m);
+    const float scale = wave_scale(m), y = 1.0f / scale;
 #pragma unroll
     for (int i = 0; i < kRegChunks; ++i)
-      if (lane + 64 * i < chunks) encode8(lane + 64 * i, w[i], scale);
+      if (lane + 64 * i < chunks) encode8(lane + 64 * i, w[i], scale, y);
     return;
   }
   uint32_t m = 0;
@@ -630,11 +641,11 @@ __global__ __launch_bounds__(256) void int4_sym_rows_kernel(const uint16_t* __re
     load8(c, w);
     m = max(m, bf16_amax_bits<4>(w));
   }
-  const float scale = wave_scale(m);
+  const float scale = wave_scale(m), y = 1.0f / scale;
   for (int64_t c = lane; c < chunks; c += 64) {
     uint32_t w[4];
     load8(c, w);
-    encode8(c, w, scale);
+    encode8(c, w, scale, y);
   }
 }
 
