@@ -729,14 +729,21 @@ __device__ __forceinline__ void int4_encode_group(const uint32_t* v, int64_t n, 
   if (s == 0.0f) { s = 1.0f; sstore = 0x3F80u; }
   const float z = fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f);
   uint32_t out[8];
+  // w / s is the IEEE quotient either way: through the group's reciprocal
+  // (nv_quotient) for s in [2^-100, 2^100], else by division
+  const bool rcp = s >= 0x1p-100f && s <= 0x1p100f;
+  const float y = 1.0f / s;
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     uint32_t r = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t pair = v[4 * d + j];
-      const float q0 = fminf(fmaxf(rintf(bf16_lo(pair) / s) + z, 0.0f), 15.0f);
-      const float q1 = fminf(fmaxf(rintf(bf16_hi(pair) / s) + z, 0.0f), 15.0f);
+      const float a = bf16_lo(pair), b = bf16_hi(pair);
+      const float qa = rcp ? nv_quotient(a, s, y) : a / s;
+      const float qb = rcp ? nv_quotient(b, s, y) : b / s;
+      const float q0 = fminf(fmaxf(rintf(qa) + z, 0.0f), 15.0f);
+      const float q1 = fminf(fmaxf(rintf(qb) + z, 0.0f), 15.0f);
       r |= ((uint32_t)q0 | ((uint32_t)q1 << 4)) << (8 * j);
     }
     out[d] = r;

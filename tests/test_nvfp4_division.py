@@ -1,6 +1,6 @@
-"""The NVFP4 encoders divide every element by its block's scale product den, and
-the symmetric INT4 quantizer by its row scale, in fp32 (IEEE division, round to
-nearest even).  The kernels form that quotient from
+"""The NVFP4 encoders divide every element by its block's scale product den, the
+symmetric INT4 quantizer by its row scale and the asymmetric INT4 packer by its
+group scale, in fp32 (IEEE division, round to nearest even).  The kernels form that quotient from
 one correctly rounded reciprocal per block, y = RN(1/den), as RN(q + r y) with
 q = RN(x y) and r = RN(x - den q) (Markstein's correction, two fmas).  This checks
 on the CPU, with exact rational arithmetic for the final fma, that the result
@@ -33,7 +33,7 @@ def rn32(v):
 def test_reciprocal_quotient_is_the_ieee_quotient():
     rng = np.random.default_rng(7)
     f32 = np.float32
-    mags = (np.arange(0x3E00, 0x4108, 3, dtype=np.uint32) << 16).view(np.float32)   # 0.125 .. 8.5
+    mags = (np.arange(0x3E00, 0x4184, 3, dtype=np.uint32) << 16).view(np.float32)   # 0.125 .. 16.5
     checked = 0
     for trial in range(40):
         if trial % 4 == 0:        # significands all ones, and exact powers of two
