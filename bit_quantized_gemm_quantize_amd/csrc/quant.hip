@@ -18,7 +18,6 @@ namespace q4 {
 
 // partial maxima of the NVFP4 tensor-amax launch: the scratch it needs, 4 KB
 constexpr int kNvPartials = kNvScratchWords;
-constexpr int kQWaves = 16;
 constexpr int kQRows = 32;
 constexpr float kNvTensorDiv = 2688.0f;   // 6 (largest E2M1) * 448 (largest E4M3)
 
@@ -394,43 +393,46 @@ static hipError_t queue_nv_encode(const uint16_t* x, int64_t rows, int64_t K, in
 }
 
 // ---------------------------------------------------------------------------- fused pass with t = X L1
-// One pair of 32-element blocks per lane half: the 64 bytes of X of block `blk` of
-// `row` (zeros past M or K).
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t row, int64_t ldx,
-                                           int64_t blk, bool ok, uint32_t* w) {
-  if (ok) {
-    const uint16_t* src = x + row * ldx + blk * 32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 v = ld16(src + 8 * q);
-      w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) w[q] = 0;
-  }
-}
+// A workgroup owns `rows` (<= 32) consecutive rows and walks K in chunks of 256
+// elements.  Each chunk of its rows of X and of L1^T (r rows) goes straight into
+// LDS, one contiguous KB per wave instruction (two rows of 512 bytes; the 16-byte
+// chunks XOR-swizzled by row & 15 so that the MFMA's column reads of 32 rows hit 16
+// distinct bank groups per pass).  From LDS, one lane per (row, 32-element block)
+// encodes the block, and wave w runs the MFMAs of K steps 2w, 2w+1 of the chunk
+// (32 x 32 x 16 bf16: rows of X against the rows of L1^T), accumulating its own
+// partial t, reduced across the waves at the end.  A ring of four stages, one
+// barrier per chunk: the loads of chunks c+1..c+3 are in flight while chunk c is
+// worked on (one chunk of 18 rows is only 9 KB, so a single chunk ahead would
+// leave too few bytes in flight per CU to cover HBM latency).  Every wave issues
+// the same number of loads per chunk (rows past the workgroup's read zeros), so
+// the wait for chunk c is a fixed count of younger loads.
+constexpr int kFKC = 256;                    // K elements per chunk
+constexpr int kFWaves = 8;
+constexpr int kFRowBytes = kFKC * 2;         // 512
+constexpr int kFOp = 32 * kFRowBytes;        // one operand's rows of a chunk
+constexpr int kFDepth = 4;                   // ring stages
+constexpr int kFXLoads = 32 / 2 / kFWaves;   // X load instructions per wave per chunk
 
-// A workgroup owns `rows` (<= 32) consecutive rows and all of K; rows is chosen
-// so the workgroups spread evenly over the CUs (lanes past it idle).  Each of the 16
-// waves takes every 16th pair of blocks, keeping the X bytes of three pairs in
-// flight per lane.
 template <int FMT, int R, bool SMOOTH = false>
-__global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
+__global__ __launch_bounds__(kFWaves * 64) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int rows,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const uint32_t* __restrict__ partials,
     int nparts, float* __restrict__ tensor_scale, const uint16_t* __restrict__ l1t, float* __restrict__ t,
     const float* __restrict__ inv_s) {
-  __shared__ float red[R > 0 ? kQWaves * 32 * 32 : 1];
+  constexpr int kStage = (R > 0 ? 2 : 1) * kFOp;            // X, then L1^T
+  constexpr int kLoads = kFXLoads + R / 2 / kFWaves;        // per wave per chunk
+  static_assert(R % (2 * kFWaves) == 0, "L1^T rows split evenly over the waves");
+  static_assert(kFDepth * kStage >= kFWaves * 32 * 32 * 4, "t partials fit the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFDepth * kStage];
   __shared__ uint32_t lds4[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 31, h = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.x * rows;
-  const int64_t row = m0 + i;
-  const bool row_ok = i < rows && row < M;
+  const int nr = (int)min<int64_t>(rows, M - m0);
   const int64_t nblk = K >> 5;
-  const int64_t npair = (nblk + 1) >> 1;
   const int64_t sbytes = FMT == 0 ? nblk : 2 * nblk;   // scale bytes per row
+  const int nchunk = (int)((K + kFKC - 1) / kFKC);
 
   float s_t = 1.0f, d6 = 6.0f;
   if constexpr (FMT == 1) {
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
     // reduce them); workgroup 0 stores it
     uint32_t m = 0;
     if (threadIdx.x < 256) {
-      for (int i = threadIdx.x; i < nparts; i += 256) m = max(m, partials[i]);
+      for (int q = threadIdx.x; q < nparts; q += 256) m = max(m, partials[q]);
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
       if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = m;
@@ -448,66 +450,111 @@ __global__ __launch_bounds__(kQWaves * 64) void quant_act_kernel(
     d6 = 6.0f * s_t;
     if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
   }
-  v16f acc = {};
 
-  auto load = [&](int64_t p, uint32_t* w) {
-    load_block(x, row, ldx, 2 * p + h, row_ok && p < npair && 2 * p + h < nblk, w);
+  // buffer views: the workgroup's rows of X (through the last row's K), and L1^T
+  const auto rx = make_rsrc(x + m0 * ldx, (uint32_t)(((int64_t)(nr - 1) * ldx + K) * 2));
+  const auto rl = make_rsrc(l1t, (uint32_t)(R > 0 ? (int64_t)R * K * 2 : 0));
+  const uint32_t ldb = (uint32_t)(ldx * 2), kb2 = (uint32_t)(K * 2);
+
+  // chunk c into stage st: instruction j covers rows 2j, 2j+1 (lane l: row 2j + l/32,
+  // LDS slot l % 32, which holds the row's 16-byte chunk (l % 32) ^ (row & 15)).
+  // Rows past nr of X read past the view (zeros); bytes past K within a row are
+  // never used (blocks and K steps past K are skipped).
+  auto load_chunk = [&](int c, int st) {
+    uint8_t* base = lds + st * kStage;
+    const int p = lane & 31;
+#pragma unroll
+    for (int jj = 0; jj < kFXLoads; ++jj) {
+      const int j = wave + jj * kFWaves;
+      const int rr = 2 * j + (lane >> 5);
+      const uint32_t off = rr < nr ? (uint32_t)rr * ldb + (uint32_t)(c * kFKC + 8 * (p ^ (rr & 15))) * 2 : kOOB;
+      dma_ld16(rx, base + j * 1024, off);
+    }
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int jj = 0; jj < R / 2 / kFWaves; ++jj) {
+        const int j = wave + jj * kFWaves;
+        const int rr = 2 * j + (lane >> 5);
+        dma_ld16(rl, base + kFOp + j * 1024, (uint32_t)rr * kb2 + (uint32_t)(c * kFKC + 8 * (p ^ (rr & 15))) * 2);
+      }
+    }
   };
-  auto step = [&](int64_t p, uint32_t* w) {
-    if (p >= npair) return;
-    const int64_t blk = 2 * p + h;
-    const bool blk_ok = blk < nblk;
-    if (row_ok && blk_ok) {
-      u32x4 c;
+
+  v16f acc = {};
+  auto process_chunk = [&](int c, int st) {
+    const uint8_t* base = lds + st * kStage;
+    // encodes: one lane per (row, block of the chunk)
+    for (int item = threadIdx.x; item < nr * 8; item += kFWaves * 64) {
+      const int rr = item >> 3, b = item & 7;
+      const int64_t blk = (int64_t)c * 8 + b;
+      if (blk >= nblk) continue;
+      uint32_t w[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = ld16(base + rr * kFRowBytes + (((4 * b + q) ^ (rr & 15)) << 4));
+        w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+      }
+      const int64_t row = m0 + rr;
+      u32x4 cw;
       if (FMT == 0 && SMOOTH) {
-        const int E = mx_encode_smoothed(w, inv_s + blk * 32, &c);
+        const int E = mx_encode_smoothed(w, inv_s + blk * 32, &cw);
         scales[row * sbytes + blk] = (uint8_t)(E + 127);
       } else if (FMT == 0) {
         const int E = mx_block_exponent(bf16_amax_bits<16>(w));
         const float sc = exp2i(E);
-        c = u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
-                  fp4_encode8_pow2(w + 8, sc), fp4_encode8_pow2(w + 12, sc)};
+        cw = u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
+                   fp4_encode8_pow2(w + 8, sc), fp4_encode8_pow2(w + 12, sc)};
         scales[row * sbytes + blk] = (uint8_t)(E + 127);
       } else {
-        const uint32_t sc = nv_encode32(w, s_t, d6, &c);
+        const uint32_t sc = nv_encode32(w, s_t, d6, &cw);
         *reinterpret_cast<uint16_t*>(scales + row * sbytes + 2 * blk) = (uint16_t)sc;
       }
-      st16(codes + row * (K >> 1) + blk * 16, c);
+      st16(codes + row * (K >> 1) + blk * 16, cw);
     }
-    if (R > 0) {
+    if constexpr (R > 0) {
+      // K steps 2 wave, 2 wave + 1 of the chunk: lane half h holds elements 8h..8h+7
+      // of the step, i.e. chunk 2s + h of the row
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 a = u32x4{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]};
-        u32x4 b = u32x4{0, 0, 0, 0};
-        if (i < R && blk_ok) b = ld16(l1t + (int64_t)i * K + blk * 32 + 8 * s);
+      for (int ss = 0; ss < 2; ++ss) {
+        const int s = 2 * wave + ss;
+        if ((int64_t)c * kFKC + 16 * s >= K) break;
+        const int slot = (2 * s + h) ^ (i & 15);
+        const u32x4 a = ld16(base + i * kFRowBytes + (slot << 4));
+        const u32x4 b = ld16(base + kFOp + i * kFRowBytes + (slot << 4));
         acc = mfma_bf16_32x32x16(a, b, acc);
       }
     }
-    load(p + 3 * kQWaves, w);                 // refill this buffer three steps ahead
   };
-  uint32_t w0[16], w1[16], w2[16];
-  const int64_t p0 = wave;
-  load(p0, w0);
-  load(p0 + kQWaves, w1);
-  load(p0 + 2 * kQWaves, w2);
-  for (int64_t p = p0; p < npair; p += 3 * kQWaves) {
-    step(p, w0);
-    step(p + kQWaves, w1);
-    step(p + 2 * kQWaves, w2);
+
+  for (int c = 0; c < kFDepth - 1 && c < nchunk; ++c) load_chunk(c, c);
+  for (int c = 0; c < nchunk; ++c) {
+    // chunk c has landed for every wave (loads complete in issue order, so it is
+    // done once at most the younger chunks' loads are pending), and every wave is
+    // done with chunk c-1, whose stage the next load reuses
+    const int younger = min(kFDepth - 2, nchunk - 1 - c);
+    if (younger >= 2) wait_vmcnt<2 * kLoads>();
+    else if (younger == 1) wait_vmcnt<kLoads>();
+    else wait_vmem();
+    barrier_after_wait();
+    if (c + kFDepth - 1 < nchunk) load_chunk(c + kFDepth - 1, (c + kFDepth - 1) % kFDepth);
+    process_chunk(c, c % kFDepth);
   }
 
-  if (R > 0) {
+  if constexpr (R > 0) {
+    // the ring is free once every wave is past its last chunk
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);
     // acc: rows = x rows (8*(v/4) + 4*h + v%4), column = t column (lane % 32)
 #pragma unroll
     for (int v = 0; v < 16; ++v) red[wave * 1024 + acc_row(v, lane) * 32 + i] = acc[v];
     __syncthreads();
     constexpr int kR = R > 0 ? R : 1;
-    for (int idx = threadIdx.x; idx < 32 * R; idx += kQWaves * 64) {
+    for (int idx = threadIdx.x; idx < 32 * R; idx += kFWaves * 64) {
       const int rr = idx / kR, cc = idx % kR;
       float sum = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < kQWaves; ++wv) sum += red[wv * 1024 + rr * 32 + cc];
-      if (rr < rows && m0 + rr < M) t[(m0 + rr) * R + cc] = sum;
+      for (int wv = 0; wv < kFWaves; ++wv) sum += red[wv * 1024 + rr * 32 + cc];
+      if (rr < nr) t[(m0 + rr) * R + cc] = sum;
     }
   }
 }
@@ -528,7 +575,7 @@ static void queue_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   while ((M + cus * waves - 1) / (cus * waves) > kQRows) ++waves;
   const int rows = (int)std::max<int64_t>(1, (M + cus * waves - 1) / (cus * waves));
   const unsigned grid = (unsigned)((M + rows - 1) / rows);
-  hipLaunchKernelGGL((quant_act_kernel<FMT, R, SMOOTH>), dim3(grid), dim3(kQWaves * 64), 0, s, x, M, K, ldx,
+  hipLaunchKernelGGL((quant_act_kernel<FMT, R, SMOOTH>), dim3(grid), dim3(kFWaves * 64), 0, s, x, M, K, ldx,
                      rows, codes, scales, partials, nparts, tensor_scale, l1t, t, inv_s);
 }
 
