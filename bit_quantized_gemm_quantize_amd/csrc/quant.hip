@@ -20,6 +20,7 @@ namespace q4 {
 constexpr int kNvPartials = kNvScratchWords;
 constexpr int kQRows = 32;
 constexpr float kNvTensorDiv = 2688.0f;   // 6 (largest E2M1) * 448 (largest E4M3)
+constexpr int64_t kNvEncodeGroups = 2048;
 
 // ---------------------------------------------------------------------------- NVFP4 helpers
 // E4M3FN code of a non-negative fp32 value, round to nearest even, saturating at 448.
@@ -99,6 +100,61 @@ __device__ __forceinline__ uint32_t nv_encode32(const uint32_t* w, float s_t, fl
     uint32_t code = e4m3_code(amax / d6);
     float den = e4m3_value(code) * s_t;
     nv_encode16(w + 8 * b, den, c + 2 * b);
+    sc |= code << (8 * b);
+  }
+  *codes = u32x4{c[0], c[1], c[2], c[3]};
+  return sc;
+}
+
+// Per-code reciprocals of an NVFP4 encode launch, filled by threads 0..127 of each
+// workgroup: for a block scale of E4M3 code c the encoder divides by
+// den_c = fp32(value(c) * s_t); where den_c lies in [2^-100, 2^100], rcp[c] holds
+// RN(1/den_c) (one IEEE division per code and workgroup instead of one per block), and
+// 0 marks the codes whose blocks divide element by element (den_c = 0 gives signed
+// zero codes, as in nv_encode16).
+__device__ __forceinline__ void nv_fill_rcp(float* rcp, float s_t) {
+  if (threadIdx.x < 128) {
+    const float den = e4m3_value(threadIdx.x) * s_t;
+    rcp[threadIdx.x] = (den >= 0x1p-100f && den <= 0x1p100f) ? 1.0f / den : 0.0f;
+  }
+}
+
+// nv_encode32 with the block scale's quotient amax / d6 through y6 = RN(1/d6) when
+// y6 > 0 (d6 in [2^-80, 2^100]: every quotient that decides a nonzero code, at least
+// 2^-10, is then a normal number and so is the correction's residual), and the
+// elements' quotients through rcp.  Same codes as nv_encode32.
+__device__ __forceinline__ uint32_t nv_encode32_rcp(const uint32_t* w, float s_t, float d6, float y6,
+                                                    const float* rcp, u32x4* codes) {
+  uint32_t sc = 0;
+  uint32_t c[4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float amax = __uint_as_float(bf16_amax_bits<8>(w + 8 * b) << 16);
+    const uint32_t code = e4m3_code(y6 > 0.0f ? nv_quotient(amax, d6, y6) : amax / d6);
+    const float den = e4m3_value(code) * s_t;
+    const float y = rcp[code];
+    const uint32_t* v = w + 8 * b;
+    if (y != 0.0f) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        uint32_t r = 0;
+        r = nv_encode_pair_rcp<0>(r, v[4 * d + 0], den, y);
+        r = nv_encode_pair_rcp<1>(r, v[4 * d + 1], den, y);
+        r = nv_encode_pair_rcp<2>(r, v[4 * d + 2], den, y);
+        r = nv_encode_pair_rcp<3>(r, v[4 * d + 3], den, y);
+        c[2 * b + d] = r;
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        uint32_t r = 0;
+        r = nv_encode_pair<0>(r, v[4 * d + 0], den);
+        r = nv_encode_pair<1>(r, v[4 * d + 1], den);
+        r = nv_encode_pair<2>(r, v[4 * d + 2], den);
+        r = nv_encode_pair<3>(r, v[4 * d + 3], den);
+        c[2 * b + d] = r;
+      }
+    }
     sc |= code << (8 * b);
   }
   *codes = u32x4{c[0], c[1], c[2], c[3]};
@@ -340,30 +396,52 @@ __global__ __launch_bounds__(256) void nv_encode_kernel(const uint16_t* __restri
                                                         const uint32_t* __restrict__ partials, int nparts,
                                                         float* __restrict__ tensor_scale) {
   __shared__ uint32_t lds4[4];
-  const float s_t = nv_tensor_scale(__uint_as_float(reduce_partials(partials, nparts, lds4)));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
-  const float d6 = 6.0f * s_t;
+  __shared__ float rcp[128];
   const int64_t nb = K >> 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if ((nb & 1) == 0) {
-    // a pair of blocks per thread: 64 bytes of X in, 16 code bytes and 2 scale bytes out
+    // a pair of blocks per thread and step: 64 bytes of X in, 16 code bytes and 2
+    // scale bytes out; the next step's loads are issued before the current step is
+    // encoded, and the first step's before the tensor scale is reduced
     const int64_t np = nb >> 1, work = rows * np;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += stride) {
-      const int64_t r = q / np, p = q % np;
-      const uint16_t* src = x + r * ldx + p * 32;
-      uint32_t w[16];
+    auto load = [&](int64_t q, uint32_t* w) {
+      if (q < work) {
+        const uint16_t* src = x + (q / np) * ldx + (q % np) * 32;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 v = ld16(src + 8 * c);
-        w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 v = ld16(src + 8 * c);
+          w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j] = 0;
       }
+    };
+    int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t w[16];
+    load(q, w);
+    const float s_t = nv_tensor_scale(__uint_as_float(reduce_partials(partials, nparts, lds4)));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+    const float d6 = 6.0f * s_t;
+    const float y6 = (d6 >= 0x1p-80f && d6 <= 0x1p100f) ? 1.0f / d6 : 0.0f;
+    nv_fill_rcp(rcp, s_t);
+    __syncthreads();
+    for (; q < work; q += stride) {
+      uint32_t wn[16];
+      load(q + stride, wn);
       u32x4 c;
-      const uint32_t sc = nv_encode32(w, s_t, d6, &c);
+      const uint32_t sc = nv_encode32_rcp(w, s_t, d6, y6, rcp, &c);
+      const int64_t r = q / np, p = q % np;
       st16(codes + r * (K >> 1) + p * 16, c);
       *reinterpret_cast<uint16_t*>(scales + r * nb + 2 * p) = (uint16_t)sc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j] = wn[j];
     }
     return;
   }
+  const float s_t = nv_tensor_scale(__uint_as_float(reduce_partials(partials, nparts, lds4)));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  const float d6 = 6.0f * s_t;
   const int64_t work = rows * nb;
   auto src = [&](int64_t q) { return x + (q / nb) * ldx + (q % nb) * 16; };
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < work; q += 2 * stride) {
@@ -384,9 +462,11 @@ __global__ __launch_bounds__(256) void nv_encode_kernel(const uint16_t* __restri
 static hipError_t queue_nv_encode(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
                                   uint8_t* scales, uint32_t* partials, int nparts, float* tensor_scale,
                                   hipStream_t s) {
-  // one thread per pair of blocks (even block count) or per two blocks
+  // one thread per pair of blocks (even block count) or per two blocks, at most
+  // kNvEncodeGroups workgroups (eight per CU, all resident): each reduces the amax
+  // partials once, then strides over the pairs
   const int64_t work = rows * (K >> 5) + (((K >> 4) & 1) ? rows : 0);
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, int64_t(1) << 20));
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, kNvEncodeGroups));
   hipLaunchKernelGGL(nv_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ldx, codes, scales,
                      partials, nparts, tensor_scale);
   return hipGetLastError();

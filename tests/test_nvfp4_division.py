@@ -5,7 +5,10 @@ one correctly rounded reciprocal per block, y = RN(1/den), as RN(q + r y) with
 q = RN(x y) and r = RN(x - den q) (Markstein's correction, two fmas).  This checks
 on the CPU, with exact rational arithmetic for the final fma, that the result
 equals the IEEE quotient for bf16 numerators over the whole range of quotients
-that decide an E2M1 code, and for denominators with every kind of significand."""
+that decide an E2M1 code, and for denominators with every kind of significand.
+The NVFP4 encoders also take each block scale's quotient amax / (6 s_t) this way when
+6 s_t lies in [2^-80, 2^100]; the second test covers the quotients that decide a
+nonzero E4M3 code (2^-10 to 448)."""
 
 from fractions import Fraction
 
@@ -30,16 +33,15 @@ def rn32(v):
     return sign * float(Fraction(fl) / scale)
 
 
-def test_reciprocal_quotient_is_the_ieee_quotient():
-    rng = np.random.default_rng(7)
+def _check_quotients(mags, exp_lo, exp_hi, seed):
+    rng = np.random.default_rng(seed)
     f32 = np.float32
-    mags = (np.arange(0x3E00, 0x4184, 3, dtype=np.uint32) << 16).view(np.float32)   # 0.125 .. 16.5
     checked = 0
     for trial in range(40):
         if trial % 4 == 0:        # significands all ones, and exact powers of two
-            den = f32(np.ldexp(f32(2.0) - f32(2.0 ** -23) * (trial % 8 // 4), int(rng.integers(-60, 60))))
+            den = f32(np.ldexp(f32(2.0) - f32(2.0 ** -23) * (trial % 8 // 4), int(rng.integers(exp_lo, exp_hi))))
         else:
-            den = f32(np.exp2(rng.uniform(-60, 60)) * rng.uniform(1, 2))
+            den = f32(np.exp2(rng.uniform(exp_lo, exp_hi)) * rng.uniform(1, 2))
         y = f32(1) / den                                             # IEEE: correctly rounded
         xs = (mags * den).astype(np.float32)
         xs = (xs.view(np.uint32) & 0xFFFF0000).view(np.float32)      # bf16 numerators
@@ -52,4 +54,16 @@ def test_reciprocal_quotient_is_the_ieee_quotient():
             got = rn32(Fraction(float(qi)) + Fraction(float(ri)) * Fraction(float(y)))
             assert got == float(ref)
             checked += 1
-    assert checked > 10000
+    return checked
+
+
+def test_reciprocal_quotient_is_the_ieee_quotient():
+    mags = (np.arange(0x3E00, 0x4184, 3, dtype=np.uint32) << 16).view(np.float32)   # 0.125 .. 16.5
+    assert _check_quotients(mags, -60, 60, 7) > 10000
+
+
+def test_block_scale_quotient_is_the_ieee_quotient():
+    """amax / d6 with d6 = 6 s_t: quotients from 2^-10 (half the smallest E4M3
+    subnormal; below it every code is 0) to 448, d6 over [2^-79, 2^99]."""
+    mags = (np.arange(0x3A80, 0x43E1, 7, dtype=np.uint32) << 16).view(np.float32)   # 2^-10 .. 448
+    assert _check_quotients(mags, -79, 99, 11) > 10000
