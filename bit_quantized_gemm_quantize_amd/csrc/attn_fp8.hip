@@ -204,6 +204,11 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
     Q4_ATTN_SCORE_STEP(0)
     Q4_ATTN_SCORE_STEP(1)
 #undef Q4_ATTN_SCORE_STEP
+    // The softmax below runs at raised issue priority: of the two waves sharing a
+    // SIMD, the one in its VALU phase then issues first and the other's MFMAs fill
+    // in behind it (measured 4-5% faster than equal priority; raising it around the
+    // MFMA phases instead made no difference).
+    __builtin_amdgcn_s_setprio(1);
 
     // ---- probabilities.  Element k of tile t is key 32 t + 16 h + k of the block;
     // tile t is 32-key chunk t.  Keys past the sequence (last block only) get -inf.
@@ -265,6 +270,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
     // lane half h supplies the scale of chunk h, relative to 2**mref
     const int psc = (h ? e1 : e0) + (int)(mcur - mref) + 127;
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- O^T += V^T P^T (four 32-channel tiles) and l += sum P^ (the ones tile)
     const uint32_t vsc = *reinterpret_cast<const uint32_t*>(sb + kVsOff + 4 * (32 * h + i));
 #pragma unroll
