@@ -85,9 +85,12 @@ def test_quantize_fused_lowrank_t(M, K, r, fmt):
     # fp32 accumulation of K products: |error| <= K * 2**-24 * sum_k |x l1| (to first order)
     bound = np.abs(X) @ np.abs(L1)
     assert np.all(np.abs(t - t_ref) <= K * 2.0 ** -24 * bound * 1.01 + 1e-30)
-    # the codes are unaffected by the fused branch
-    codes = (Q.mx_quantize(x) if fmt == "mxfp4" else Q.nv_quantize(x))[0]
-    assert np.array_equal(u8(g["codes"]), codes)
+    # the codes, scales and tensor scale are unaffected by the fused branch
+    ref = Q.mx_quantize(x) if fmt == "mxfp4" else Q.nv_quantize(x)
+    assert np.array_equal(u8(g["codes"]), ref[0])
+    assert np.array_equal(u8(g["scales"]), ref[1])
+    if fmt == "nvfp4":
+        assert float(g["ts"].item()) == float(ref[2])
 
 
 # ------------------------------------------------------------------ NVFP4 activations
