@@ -499,8 +499,12 @@ __global__ __launch_bounds__(kFWaves * 64) void quant_act_kernel(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const uint32_t* __restrict__ partials,
     int nparts, float* __restrict__ tensor_scale, const uint16_t* __restrict__ l1t, float* __restrict__ t,
     const float* __restrict__ inv_s) {
-  constexpr int kStage = (R > 0 ? 2 : 1) * kFOp;            // X, then L1^T
-  constexpr int kLoads = kFXLoads + R / 2 / kFWaves;        // per wave per chunk
+  // a stage: X, then L1^T, then (smoothing) the chunk's 256 factors, which wave 0
+  // loads with one more instruction (factors read from global memory inside the
+  // loop would make the compiler's waits for them drain the whole ring)
+  constexpr int kFactOff = (R > 0 ? 2 : 1) * kFOp;
+  constexpr int kStage = kFactOff + (SMOOTH ? kFKC * 4 : 0);
+  constexpr int kLoads = kFXLoads + R / 2 / kFWaves;        // per wave per chunk (wave 0: + SMOOTH)
   static_assert(R % (2 * kFWaves) == 0, "L1^T rows split evenly over the waves");
   static_assert(kFDepth * kStage >= kFWaves * 32 * 32 * 4, "t partials fit the ring");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFDepth * kStage];
@@ -534,6 +538,7 @@ __global__ __launch_bounds__(kFWaves * 64) void quant_act_kernel(
   // buffer views: the workgroup's rows of X (through the last row's K), and L1^T
   const auto rx = make_rsrc(x + m0 * ldx, (uint32_t)(((int64_t)(nr - 1) * ldx + K) * 2));
   const auto rl = make_rsrc(l1t, (uint32_t)(R > 0 ? (int64_t)R * K * 2 : 0));
+  const auto rf = make_rsrc(inv_s, (uint32_t)(SMOOTH ? K * 4 : 0));
   const uint32_t ldb = (uint32_t)(ldx * 2), kb2 = (uint32_t)(K * 2);
 
   // chunk c into stage st: instruction j covers rows 2j, 2j+1 (lane l: row 2j + l/32,
@@ -558,6 +563,10 @@ __global__ __launch_bounds__(kFWaves * 64) void quant_act_kernel(
         dma_ld16(rl, base + kFOp + j * 1024, (uint32_t)rr * kb2 + (uint32_t)(c * kFKC + 8 * (p ^ (rr & 15))) * 2);
       }
     }
+    if constexpr (SMOOTH) {
+      // lane l: factors 4 l .. 4 l + 3 of the chunk (past K: zeros, never used)
+      if (wave == 0) dma_ld16(rf, base + kFactOff, (uint32_t)(c * kFKC + 4 * lane) * 4);
+    }
   };
 
   v16f acc = {};
@@ -577,7 +586,7 @@ __global__ __launch_bounds__(kFWaves * 64) void quant_act_kernel(
       const int64_t row = m0 + rr;
       u32x4 cw;
       if (FMT == 0 && SMOOTH) {
-        const int E = mx_encode_smoothed(w, inv_s + blk * 32, &cw);
+        const int E = mx_encode_smoothed(w, reinterpret_cast<const float*>(base + kFactOff) + 32 * b, &cw);
         scales[row * sbytes + blk] = (uint8_t)(E + 127);
       } else if (FMT == 0) {
         const int E = mx_block_exponent(bf16_amax_bits<16>(w));
@@ -612,9 +621,15 @@ __global__ __launch_bounds__(kFWaves * 64) void quant_act_kernel(
     // done once at most the younger chunks' loads are pending), and every wave is
     // done with chunk c-1, whose stage the next load reuses
     const int younger = min(kFDepth - 2, nchunk - 1 - c);
-    if (younger >= 2) wait_vmcnt<2 * kLoads>();
-    else if (younger == 1) wait_vmcnt<kLoads>();
-    else wait_vmem();
+    if (SMOOTH && wave == 0) {
+      if (younger >= 2) wait_vmcnt<2 * (kLoads + 1)>();
+      else if (younger == 1) wait_vmcnt<kLoads + 1>();
+      else wait_vmem();
+    } else {
+      if (younger >= 2) wait_vmcnt<2 * kLoads>();
+      else if (younger == 1) wait_vmcnt<kLoads>();
+      else wait_vmem();
+    }
     barrier_after_wait();
     if (c + kFDepth - 1 < nchunk) load_chunk(c + kFDepth - 1, (c + kFDepth - 1) % kFDepth);
     process_chunk(c, c % kFDepth);
