@@ -5,8 +5,9 @@
 //   * MXFP4 without the low-rank term: one thread per 32-element block
 //     (mx_rows_kernel, shared with MXFP8 and the weight packer).
 //   * with the low-rank term t = X L1 (or SmoothQuant factors): quant_act_kernel,
-//     rows on lanes, one whole block per lane, the same registers feeding the bf16
-//     MFMA of t.
+//     a workgroup's rows of X (and of L1^T, and the factors) copied chunk by chunk
+//     straight into a ring of LDS stages, each block encoded by one lane from LDS,
+//     and t formed from the same LDS tiles on the bf16 MFMA.
 //   * NVFP4: a tensor-amax launch that leaves per-workgroup partial maxima in a
 //     small scratch array, then the encode launch (16-element blocks).
 #include <algorithm>
@@ -483,9 +484,11 @@ static hipError_t queue_nv_encode(const uint16_t* x, int64_t rows, int64_t K, in
 // partial t, reduced across the waves at the end.  A ring of four stages, one
 // barrier per chunk: the loads of chunks c+1..c+3 are in flight while chunk c is
 // worked on (one chunk of 18 rows is only 9 KB, so a single chunk ahead would
-// leave too few bytes in flight per CU to cover HBM latency).  Every wave issues
-// the same number of loads per chunk (rows past the workgroup's read zeros), so
-// the wait for chunk c is a fixed count of younger loads.
+// leave too few bytes in flight per CU to cover HBM latency: 15.3 us at 4608 x 3072
+// with two stages, 11.5 us with four).  Every wave issues the same number of loads
+// per chunk (rows past the workgroup's read zeros; with smoothing wave 0 issues one
+// more, the chunk's factors), so the wait for chunk c is a fixed count of younger
+// loads.
 constexpr int kFKC = 256;                    // K elements per chunk
 constexpr int kFWaves = 8;
 constexpr int kFRowBytes = kFKC * 2;         // 512
