@@ -65,6 +65,28 @@ def test_quantize_smooth_wide_range_and_padded_rows():
     assert np.array_equal(u8(g["codes"]), codes)
 
 
+@pytest.mark.parametrize("M,K,r", [(4700, 1056, 16), (600, 3104, 32)])
+def test_quantize_smooth_fused_t_ring_shapes(M, K, r):
+    """The smoothed pass with t over shapes that wrap the kernel's load ring and end
+    in a partial chunk (K = 1056, 3104), with 19 rows per workgroup (M = 4700) and
+    with fewer rows than CUs (M = 600): codes and scales bit-exact, t within the
+    fp32 accumulation bound."""
+    dev = device()
+    x = synth.activations(M, K, seed=M + K, outliers=max(1, K // 100))[0]
+    rng = np.random.default_rng(M + 2 * K)
+    inv = np.exp(rng.uniform(-4.0, 3.0, K)).astype(np.float32)
+    l1 = synth.to_bf16_bits(rng.standard_normal((K, r)) * 0.05)
+    say(f"quantize_act_smooth mxfp4 + t=X L1 M={M} K={K} r={r}")
+    g = quantize_smooth(x, inv, dev, l1_bits=l1)
+    codes, scales = Q.mx_quantize_smoothed(x, inv)
+    assert np.array_equal(u8(g["scales"]), scales)
+    assert np.array_equal(u8(g["codes"]), codes)
+    X, L1 = F.bf16_to_f64(x), F.bf16_to_f64(l1)
+    t = g["t"].cpu().numpy().astype(np.float64)
+    bound = np.abs(X) @ np.abs(L1)
+    assert np.all(np.abs(t - L.lowrank_down(X, L1)) <= K * 2.0 ** -24 * bound * 1.01 + 1e-30)
+
+
 def test_quantize_smooth_fused_t_uses_unsmoothed_x():
     dev = device()
     M, K, r = 96, 512, 32
