@@ -346,6 +346,31 @@ def bench_rows(reps=50):
         emit(f"gemm_w4a4 mxfp4 {Mq}x{Kq}x{n} bf16 out", ms, flops=2.0 * Mq * n * Kq,
              peak=MXFP4_PEAK_TFLOPS, note="inputs warm in L2/MALL")
 
+    # ---- the attention-projection step as one measured pass: quantize_act (MXFP4,
+    # no branch) of X, then gemm_w4a4 into bf16, over 8 rotating sets of X (1% outlier
+    # channels) and packed W (8 x 33 MB, more than the last-level cache holds)
+    Na, n_sets_a = 3072, 8
+    sets_a = []
+    for j in range(n_sets_a):
+        da = synth.attn_proj(seed=j, M=Mq, K=Kq, N=Na)
+        wa = bf16_dev(da["wt"])
+        wc_, ws_, _ = B.empty_quant("mxfp4", Na, Kq, dev)
+        B.pack_weights("mxfp4", wa, Kq, Na, 1, Kq, wc_, ws_, stream=stream)
+        xc_, xs_, _ = B.empty_quant("mxfp4", Mq, Kq, dev)
+        sets_a.append((bf16_dev(da["x"]), wc_, ws_, xc_, xs_))
+        del wa
+    ya = torch.empty((Mq, Na), dtype=torch.bfloat16, device=dev)
+
+    def attn_step(i):
+        xa, wc_, ws_, xc_, xs_ = sets_a[i]
+        B.quantize_act("mxfp4", xa, xc_, xs_, stream=stream)
+        B.gemm_w4a4("mxfp4", xc_, xs_, None, wc_, ws_, None, Mq, Na, Kq, ya, stream=stream)
+    ms = timed(attn_step, n_sets_a)
+    emit(f"step quantize_act + gemm_w4a4 mxfp4 {Mq}x{Kq}x{Na}", ms, flops=2.0 * Mq * Na * Kq,
+         peak=MXFP4_PEAK_TFLOPS, note="attention projection at 1024^2 as one pass: X quantized, then "
+                                      "multiplied; 8 rotating sets of X and W, cold in HBM")
+    del sets_a, ya
+
     # ---- f1: the MXFP4-emitting epilogue at the MLP up-projection with the rank-32
     # branch, against the unfused pair (bf16 store, then quantize_act reading it back)
     dm = weight_prep.mlp_up_svd(seed=0)
