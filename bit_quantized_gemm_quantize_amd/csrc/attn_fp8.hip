@@ -310,10 +310,10 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fp8_kernel(AttnView a) {
 // workgroup takes 4 chunks of 32 keys of one (batch, head); wave w chunk w; lane
 // channels 2 lane, 2 lane + 1 (one dword per key: 256 contiguous bytes per key
 // row across the wave).
-__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v, int64_t ldv, int seq,
-                                                      int heads, int seq64, int groups_per_bh,
-                                                      uint8_t* __restrict__ vc, uint8_t* __restrict__ vs) {
-  const int g = blockIdx.x % groups_per_bh, bh = blockIdx.x / groups_per_bh;
+__device__ __forceinline__ void quant_v_group(int vb, const uint16_t* __restrict__ v, int64_t ldv, int seq,
+                                              int heads, int seq64, int groups_per_bh,
+                                              uint8_t* __restrict__ vc, uint8_t* __restrict__ vs) {
+  const int g = vb % groups_per_bh, bh = vb / groups_per_bh;
   const int b = bh / heads, hd = bh % heads;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int chunk = 4 * g + wave;                    // 32-key chunk of this (b, head)
@@ -353,6 +353,28 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
   }
 }
 
+// The three quantizations in one launch: workgroups [0, nqk) take Q's and then K's
+// 32-element row blocks, one per thread (mx_block), the rest V's groups of 32-key
+// chunks (quant_v_group).  One launch instead of three saves two launch gaps and
+// two tails.
+__global__ __launch_bounds__(256) void attn_quant_kernel(const uint16_t* __restrict__ q, int64_t ldq,
+                                                         const uint16_t* __restrict__ k, int64_t ldk,
+                                                         const uint16_t* __restrict__ v, int64_t ldv,
+                                                         int64_t tokens, int64_t width, int seq, int heads,
+                                                         int seq64, int groups, int nqk, uint8_t* __restrict__ qc,
+                                                         uint8_t* __restrict__ qs, uint8_t* __restrict__ kc,
+                                                         uint8_t* __restrict__ ks, uint8_t* __restrict__ vc,
+                                                         uint8_t* __restrict__ vs) {
+  if ((int)blockIdx.x >= nqk) {
+    quant_v_group((int)blockIdx.x - nqk, v, ldv, seq, heads, seq64, groups, vc, vs);
+    return;
+  }
+  const int64_t nblk = width >> 5, work = tokens * nblk;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < work) mx_block<kBlkMXFP8>(q, width, ldq, 1, qc, qs, nblk, i);
+  else if (i < 2 * work) mx_block<kBlkMXFP8>(k, width, ldk, 1, kc, ks, nblk, i - work);
+}
+
 }  // namespace
 
 hipError_t launch_attn_quantize(const uint16_t* q, int64_t ldq, const uint16_t* k, int64_t ldk,
@@ -360,14 +382,13 @@ hipError_t launch_attn_quantize(const uint16_t* q, int64_t ldq, const uint16_t* 
                                 uint8_t* qc, uint8_t* qs, uint8_t* kc, uint8_t* ks, uint8_t* vc,
                                 uint8_t* vs, hipStream_t s) {
   const int64_t tokens = batch * seq, width = heads * kHD;
-  hipError_t e = launch_mxfp8_rows(q, tokens, width, ldq, 1, qc, qs, s);
-  if (e != hipSuccess) return e;
-  e = launch_mxfp8_rows(k, tokens, width, ldk, 1, kc, ks, s);
-  if (e != hipSuccess) return e;
   const int64_t seq64 = (seq + kKB - 1) / kKB * kKB;
   const int64_t groups = (seq64 / 32 + 3) / 4;
-  hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)(batch * heads * groups)), dim3(256), 0, s, v, ldv, (int)seq,
-                     (int)heads, (int)seq64, (int)groups, vc, vs);
+  const int64_t nqk = (2 * tokens * (width >> 5) + 255) / 256;       // Q and K blocks, 256 per workgroup
+  const int64_t grid = nqk + batch * heads * groups;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, q, ldq, k, ldk, v, ldv, tokens, width,
+                     (int)seq, (int)heads, (int)seq64, (int)groups, (int)nqk, qc, qs, kc, ks, vc, vs);
   return hipGetLastError();
 }
 

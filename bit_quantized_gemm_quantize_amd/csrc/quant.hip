@@ -212,64 +212,7 @@ __device__ __forceinline__ int mx_encode_smoothed(const uint32_t* w, const float
 }
 
 // ---------------------------------------------------------------------------- per block
-// One thread per (row, 32-element block) of a strided bf16 matrix, consecutive
-// threads on consecutive blocks of a row (contiguous loads and stores).
-//   MXFP8: E = floor(log2 amax) - 8 (emax of E4M3FN) clamped to [-127, 127], codes
-//   E4M3_RNE(x * 2**-E) saturated at +-448 (the product is exact in fp32; the clamp
-//   comes before the converter, which rounds to nearest even), 32 code bytes, one
-//   scale byte E + 127.
-//   MXFP4: E = floor(log2 amax) - 2, codes E2M1_RNE(x * 2**-E) by the hardware
-//   converter, 16 code bytes, one scale byte.
-constexpr int kBlkMXFP4 = 0, kBlkMXFP8 = 2;
-template <int KIND>
-__device__ __forceinline__ void mx_block(const uint16_t* __restrict__ x, int64_t K, int64_t sr, int64_t sk,
-                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                         int64_t nblk, int64_t q) {
-  const int64_t r = q / nblk, b = q % nblk;
-  const uint16_t* src = x + r * sr + b * 32 * sk;
-  uint32_t w[16];
-  if (sk == 1 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 v = ld16(src + 8 * c);
-      w[4 * c] = v[0]; w[4 * c + 1] = v[1]; w[4 * c + 2] = v[2]; w[4 * c + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) w[j] = (uint32_t)src[2 * j * sk] | ((uint32_t)src[(2 * j + 1) * sk] << 16);
-  }
-  const uint32_t amax = bf16_amax_bits<16>(w);
-  if (KIND == kBlkMXFP4) {
-    const int E = mx_block_exponent(amax);
-    const float sc = exp2i(E);
-    st16(codes + r * (K >> 1) + b * 16, u32x4{fp4_encode8_pow2(w, sc), fp4_encode8_pow2(w + 4, sc),
-                                               fp4_encode8_pow2(w + 8, sc), fp4_encode8_pow2(w + 12, sc)});
-    scales[r * nblk + b] = (uint8_t)(E + 127);
-    return;
-  }
-  int E = amax == 0 ? -127 : bf16_floor_log2(amax) - 8;
-  E = E < -127 ? -127 : (E > 127 ? 127 : E);
-  const float down = exp2i(-E);
-  uint32_t out[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * d + j;
-      const float xv = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      v[j] = fminf(fmaxf(xv * down, -448.0f), 448.0f);
-    }
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-    out[d] = (uint32_t)word;
-  }
-  uint8_t* dst = codes + r * K + b * 32;
-  st16(dst, u32x4{out[0], out[1], out[2], out[3]});
-  st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
-  scales[r * nblk + b] = (uint8_t)(E + 127);
-}
-
+// mx_block (q4_device.h): one thread per (row, 32-element block).
 template <int KIND>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                       int64_t K, int64_t sr, int64_t sk,
