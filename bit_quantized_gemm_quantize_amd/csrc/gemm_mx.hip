@@ -298,7 +298,10 @@ __device__ __forceinline__ u32x4 mx_stage1_read(const uint8_t* stage, int i, int
 // 32 j .. 32 j + 31 of group j.  A wave's weight sub-tiles (32 rows each, F of them)
 // are F/2 whole groups, so acc[2p] (gate) and acc[2p + 1] (up) hold the same
 // outputs.  With each weight row's bias added first, y = gate / (1 + exp(-gate)) * up
-// in fp32, stored as bf16 [M, N/2] through the standard staging.
+// in fp32, the division taken as a product with the hardware reciprocal (within an
+// ulp; an IEEE division is about ten instructions per element, and this epilogue
+// runs after the K loop with nothing to hide them under), stored as bf16 [M, N/2]
+// through the standard staging.
 template <int F>
 __device__ __forceinline__ void epilogue_store_swiglu(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
                                                       int64_t M, int64_t N, const uint16_t* __restrict__ bias,
@@ -322,7 +325,7 @@ __device__ __forceinline__ void epilogue_store_swiglu(v16f (&acc)[F][4], int64_t
         for (int g = 0; g < 4; ++g) {
           const float gate = acc[2 * p][g][4 * vq + jj] + bg;
           const float up = acc[2 * p + 1][g][4 * vq + jj] + bu;
-          v[p][g][4 * vq + jj] = gate / (1.0f + __expf(-gate)) * up;
+          v[p][g][4 * vq + jj] = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
         }
       }
   epilogue_store<false, P, 128>(v, n_base / 2, m_base, M, N / 2, nullptr, y, ldy, lane, stage);

@@ -140,7 +140,8 @@ def swiglu_ref(y, bound, block=SWIGLU_BLOCK):
     <= 1e-3 bound_u,
         |d out| <= 1e-3 (SILU_SLOPE_MAX bound_g (|up| + 1e-3 bound_u) + |silu(gate)| bound_u)
     plus the fp32 evaluation of silu(gate) * up (an exp whose argument carries a
-    relative error of 2^-23, a division and a product): |out| (|gate| 2^-23 + 2^-20).
+    relative error of 2^-23, a division or a reciprocal within an ulp, and a
+    product): |out| (|gate| 2^-23 + 2^-20).
     """
     y = np.asarray(y, dtype=np.float64)
     bound = np.asarray(bound, dtype=np.float64)
