@@ -361,6 +361,20 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
   const int cl = lane & 3;                               // 32-byte chunk: columns 8 cl .. 8 cl + 7
 #pragma unroll
   for (int pass = 0; pass < S::kPasses; ++pass) {
+    const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
+    int ip[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ip[q] = (int)(((col + 2 * q) % hd) >> 1);
+    // the pass's (cos, sin) pairs, all loaded before its staging so that their
+    // latency is paid once per pass, not once per row (rows past M read row M - 1,
+    // unused)
+    float2 tcs[8][4];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int64_t mr = min(m_base + 16 * it + (lane >> 2), M - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tcs[it][q] = cs[mr * half + ip[q]];
+    }
     if (pass > 0) {
       __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): previous pass read back
       __builtin_amdgcn_wave_barrier();
@@ -368,11 +382,7 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
     epilogue_stage_pass<true, F, 128, false, true>(acc, pass, col0, D, bsec, lane, stage, 1.0f);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
-    const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
-    int ip[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ip[q] = (int)(((col + 2 * q) % hd) >> 1);
-#pragma unroll 2
     for (int it = 0; it < 8; ++it) {
       const int ml = 16 * it + (lane >> 2);
       const int64_t m = m_base + ml;
@@ -383,7 +393,7 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float2 t = cs[m * half + ip[q]];
+          const float2 t = tcs[it][q];
           const v2bf p = {(__bf16)(v[2 * q] * t.x - v[2 * q + 1] * t.y),
                           (__bf16)(v[2 * q] * t.y + v[2 * q + 1] * t.x)};
           w[q] = __builtin_bit_cast(uint32_t, p);
