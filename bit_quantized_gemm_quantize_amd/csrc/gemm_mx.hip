@@ -359,22 +359,24 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
   const int hd = qo.head_dim, half = hd >> 1;
   const float2* cs = reinterpret_cast<const float2*>(qo.cs);
   const int cl = lane & 3;                               // 32-byte chunk: columns 8 cl .. 8 cl + 7
-#pragma unroll
-  for (int pass = 0; pass < S::kPasses; ++pass) {
-    const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
+  // (cos, sin) of pair q of row it of a pass: rows past M read row M - 1 (unused)
+  auto load_table = [&](int pass, float2 (&tcs)[8][4]) {
+    const int64_t col = col0 + 32 * pass + 8 * cl;
     int ip[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) ip[q] = (int)(((col + 2 * q) % hd) >> 1);
-    // the pass's (cos, sin) pairs, all loaded before its staging so that their
-    // latency is paid once per pass, not once per row (rows past M read row M - 1,
-    // unused)
-    float2 tcs[8][4];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int64_t mr = min(m_base + 16 * it + (lane >> 2), M - 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) tcs[it][q] = cs[mr * half + ip[q]];
     }
+  };
+  float2 tcs[8][4];
+  load_table(0, tcs);
+#pragma unroll
+  for (int pass = 0; pass < S::kPasses; ++pass) {
+    const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
     if (pass > 0) {
       __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): previous pass read back
       __builtin_amdgcn_wave_barrier();
@@ -382,24 +384,34 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
     epilogue_stage_pass<true, F, 128, false, true>(acc, pass, col0, D, bsec, lane, stage, 1.0f);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
+    // the next pass's table pairs are loaded into each row's registers as soon as
+    // this pass has used them, so their latency hides behind this pass's stores and
+    // the next pass's staging
+    int ipn[4];
+    const int64_t coln = col + 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ipn[q] = (int)(((coln + 2 * q) % hd) >> 1);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int ml = 16 * it + (lane >> 2);
       const int64_t m = m_base + ml;
-      if (m < M) {
-        const uint8_t* src = stage + ml * S::kStageRowBytes + cl * 32;
-        const v4f va = *reinterpret_cast<const v4f*>(src), vb = *reinterpret_cast<const v4f*>(src + 16);
-        const float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-        uint32_t w[4];
+      const uint8_t* src = stage + ml * S::kStageRowBytes + cl * 32;
+      const v4f va = *reinterpret_cast<const v4f*>(src), vb = *reinterpret_cast<const v4f*>(src + 16);
+      const float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+      uint32_t w[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float2 t = tcs[it][q];
-          const v2bf p = {(__bf16)(v[2 * q] * t.x - v[2 * q + 1] * t.y),
-                          (__bf16)(v[2 * q] * t.y + v[2 * q + 1] * t.x)};
-          w[q] = __builtin_bit_cast(uint32_t, p);
-        }
-        st16_stream(dst + m * ldy + col, u32x4{w[0], w[1], w[2], w[3]});
+      for (int q = 0; q < 4; ++q) {
+        const float2 t = tcs[it][q];
+        const v2bf p = {(__bf16)(v[2 * q] * t.x - v[2 * q + 1] * t.y),
+                        (__bf16)(v[2 * q] * t.y + v[2 * q + 1] * t.x)};
+        w[q] = __builtin_bit_cast(uint32_t, p);
       }
+      if (pass + 1 < S::kPasses) {
+        const int64_t mr = min(m, M - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tcs[it][q] = cs[mr * half + ipn[q]];
+      }
+      if (m < M) st16_stream(dst + m * ldy + col, u32x4{w[0], w[1], w[2], w[3]});
     }
   }
 }
