@@ -268,7 +268,8 @@ q4_status gemm_w4a4_lowrank_qkv_rope(const uint8_t* a_codes, const uint8_t* a_sc
   const int64_t D = N / 3;
   if (M < 0 || N < 0 || K < 0 || (K % 128) != 0 || (N % 384) != 0 || !rank_ok(r)) return Q4_ERR_SHAPE;
   if (M > kMaxRows || N > kMaxRows || K > kMaxK || ldy < D) return Q4_ERR_SHAPE;
-  if (cs && (head_dim < 2 || (head_dim % 2) != 0 || (D % head_dim) != 0)) return Q4_ERR_SHAPE;
+  if (cs && (head_dim < 2 || head_dim > 65536 || (head_dim % 2) != 0 || (D % head_dim) != 0))
+    return Q4_ERR_SHAPE;
   if (!a_codes || !a_scales || !b_codes || !b_scales || !yq || !yk || !yv) return Q4_ERR_NULL;
   if (r > 0 && (!t || !l2t)) return Q4_ERR_NULL;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||

@@ -356,24 +356,32 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
   }
   using S = EpilogueShape<true, F, 128>;
   static_assert(S::kFPerPass == 1, "one 32-column sub-tile per fp32 pass");
-  const int hd = qo.head_dim, half = hd >> 1;
-  const float2* cs = reinterpret_cast<const float2*>(qo.cs);
+  const int hd = qo.head_dim;
   const int cl = lane & 3;                               // 32-byte chunk: columns 8 cl .. 8 cl + 7
-  // (cos, sin) of pair q of row it of a pass: rows past M read row M - 1 (unused)
-  auto load_table = [&](int pass, float2 (&tcs)[8][4]) {
-    const int64_t col = col0 + 32 * pass + 8 * cl;
-    int ip[4];
+  // the table rows of this wave's 128 rows, through a buffer whose bound returns
+  // zeros for rows past M (their outputs are not stored); lane row ml = 16 it +
+  // lane / 4 sits at byte 4 hd ml, pair i of it at + 8 i
+  const auto rcs = make_rsrc(qo.cs + m_base * hd, rows_in(128, M, m_base) * (uint32_t)hd * 4u);
+  const uint32_t row_off = (uint32_t)(lane >> 2) * (uint32_t)hd * 4u;
+  const uint32_t colm = (uint32_t)(col0 % hd);
+  // byte offsets of the lane's four pairs in a pass: pair index ((col + 2 q) mod hd) / 2
+  auto pair_offs = [&](int pass, uint32_t (&off)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ip[q] = (int)(((col + 2 * q) % hd) >> 1);
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int64_t mr = min(m_base + 16 * it + (lane >> 2), M - 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) tcs[it][q] = cs[mr * half + ip[q]];
-    }
+    for (int q = 0; q < 4; ++q)
+      off[q] = row_off + (((colm + 32u * pass + 8u * cl + 2u * q) % (uint32_t)hd) >> 1) * 8u;
+  };
+  auto load_pair = [&](uint32_t off, int it) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rcs, (int)off, 64 * hd * it, 0));
   };
   float2 tcs[8][4];
-  load_table(0, tcs);
+  {
+    uint32_t off[4];
+    pair_offs(0, off);
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tcs[it][q] = load_pair(off[q], it);
+  }
 #pragma unroll
   for (int pass = 0; pass < S::kPasses; ++pass) {
     const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
@@ -387,10 +395,8 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
     // the next pass's table pairs are loaded into each row's registers as soon as
     // this pass has used them, so their latency hides behind this pass's stores and
     // the next pass's staging
-    int ipn[4];
-    const int64_t coln = col + 32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ipn[q] = (int)(((coln + 2 * q) % hd) >> 1);
+    uint32_t offn[4];
+    pair_offs(pass + 1, offn);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int ml = 16 * it + (lane >> 2);
@@ -407,9 +413,8 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
         w[q] = __builtin_bit_cast(uint32_t, p);
       }
       if (pass + 1 < S::kPasses) {
-        const int64_t mr = min(m, M - 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) tcs[it][q] = cs[mr * half + ipn[q]];
+        for (int q = 0; q < 4; ++q) tcs[it][q] = load_pair(offn[q], it);
       }
       if (m < M) st16_stream(dst + m * ldy + col, u32x4{w[0], w[1], w[2], w[3]});
     }

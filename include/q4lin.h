@@ -317,7 +317,7 @@ Q4_API q4_status gemm_w4a4_lowrank_swiglu(const uint8_t* a_codes, const uint8_t*
  *             8-byte aligned; or NULL for the split alone.  In Q and K, columns
  *             (2 i, 2 i + 1) of every head (counted inside the head) become
  *             (a c - b s, a s + b c), after the bias, in fp32.
- *   head_dim  even, dividing D (ignored when cs is NULL).
+ *   head_dim  even, at most 65536, dividing D (ignored when cs is NULL).
  *   yq, yk, yv (out)  bf16 [M, D] each, row stride ldy >= D (a multiple of 8),
  *             16-byte aligned.
  */

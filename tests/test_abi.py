@@ -168,6 +168,7 @@ def test_gemm_qkv_rope_rejections():
     assert gr(ldy=128) == B.Q4_ERR_SHAPE                 # ldy < D
     assert gr(hd=3) == B.Q4_ERR_SHAPE                    # odd head width
     assert gr(hd=96) == B.Q4_ERR_SHAPE                   # does not divide D = 256
+    assert gr(N=3 * 262144, hd=131072, ldy=262144) == B.Q4_ERR_SHAPE   # head wider than 65536
     assert gr(cs=None, hd=3, M=0) == B.Q4_OK             # head_dim ignored without a table
     assert gr(yk=None) == B.Q4_ERR_NULL
     assert gr(yv=None) == B.Q4_ERR_NULL
