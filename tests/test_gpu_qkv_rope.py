@@ -101,7 +101,11 @@ def test_quarter_turn_on_exact_gemm_results():
 
 @pytest.mark.parametrize("M,N,K,hd,r,rope", [(64, 384, 256, 64, 0, True), (300, 768, 384, 128, 32, True),
                                              (513, 1152, 512, 64, 16, True), (1, 384, 128, 2, 0, True),
-                                             (200, 768, 256, 0, 32, False)])
+                                             (200, 768, 256, 0, 32, False),
+                                             # head widths that straddle the 32-column
+                                             # passes, and one head over all of D
+                                             (130, 1152, 256, 96, 0, True), (70, 1152, 128, 6, 16, True),
+                                             (257, 1152, 256, 384, 32, True)])
 def test_qkv_rope_parity(M, N, K, hd, r, rope):
     dev = device()
     x = synth.activations(M, K, seed=M + N + 7, dist="student_t3")[0]
