@@ -385,12 +385,10 @@ __device__ __forceinline__ void epilogue_store_qkv(v16f (&acc)[F][4], int64_t n_
 #pragma unroll
   for (int pass = 0; pass < S::kPasses; ++pass) {
     const int64_t col = col0 + 32 * pass + 8 * cl;       // pairs (col + 2 q, col + 2 q + 1), q < 4
-    if (pass > 0) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): previous pass read back
-      __builtin_amdgcn_wave_barrier();
-    }
+    // a wave's LDS accesses take effect in order: the writes of a pass need no wait
+    // for the reads of the previous one, nor the reads for the writes
+    if (pass > 0) __builtin_amdgcn_wave_barrier();
     epilogue_stage_pass<true, F, 128, false, true>(acc, pass, col0, D, bsec, lane, stage, 1.0f);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
     // the next pass's table pairs are loaded into each row's registers as soon as
     // this pass has used them, so their latency hides behind this pass's stores and
