@@ -1,4 +1,6 @@
-// Main loop of the bf16-MFMA GEMMs (the exact NVFP4 path and the W4A16 path).
+// Main loop of the 16-bit-MFMA GEMMs: the W4A16 path on the bf16 MFMA and the exact
+// NVFP4 path on the fp16 MFMA (Loader::kF16 picks the instruction; the operand
+// layout is the same).
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), 128 x 128 per
 // wave as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16; or, to fill the CUs when tiles
@@ -8,7 +10,8 @@
 // 16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ lds_swz<8>(r), for the
 // 64-bank LDS), two stages, one barrier per K-tile.
 //
-// A loader policy turns global data into bf16 LDS rows:
+// A loader policy turns global data into 16-bit LDS rows (Loader::kF16: fp16, else
+// bf16):
 //   Loader::issue_regs(kt)            issue the global reads of K-tile kt that land
 //                                    in registers (Loader::kRegLoads instructions)
 //   Loader::issue_lds(kt, lds_a, lds_b)  issue those that go straight into LDS
@@ -59,14 +62,22 @@ __device__ __forceinline__ void bf16_read_frags(Bf16Frags<F>& fr, const uint8_t*
   for (int f = 0; f < F; ++f) fr.b[BUF][f] = ld16(pb + f * 32 * kBf16RowBytes);
 }
 
+__device__ __forceinline__ v16f mfma_f16_32x32x16(u32x4 a, u32x4 b, v16f c) {
+  typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0,
+                                                0, 0);
+}
+
 // acc[f][g] holds D[n][m] (A operand = weight rows, B operand = activation rows);
-// weight sub-tiles f in [F0, F1).
-template <int BUF, int F, int F0 = 0, int F1 = F>
+// weight sub-tiles f in [F0, F1); fp16 operands when F16, else bf16.
+template <int BUF, int F, int F0 = 0, int F1 = F, bool F16 = false>
 __device__ __forceinline__ void bf16_mma(v16f (&acc)[F][4], const Bf16Frags<F>& fr) {
 #pragma unroll
   for (int f = F0; f < F1; ++f)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) acc[f][g] = mfma_bf16_32x32x16(fr.b[BUF][f], fr.a[BUF][g], acc[f][g]);
+    for (int g = 0; g < 4; ++g)
+      acc[f][g] = F16 ? mfma_f16_32x32x16(fr.b[BUF][f], fr.a[BUF][g], acc[f][g])
+                      : mfma_bf16_32x32x16(fr.b[BUF][f], fr.a[BUF][g], acc[f][g]);
 }
 
 // Stage st of the operand tiles: A at lds + st * tile, B at lds + (2 + st) * tile,
@@ -89,14 +100,14 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, 
   constexpr int kH = F / 2;                                    // sub-tiles of step 3 before the barrier
   // step 0
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
-  bf16_mma<0, F>(acc, fr);
+  bf16_mma<0, F, 0, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);       // fragment reads first
   __builtin_amdgcn_sched_group_barrier(0x008, kMma, 0);
   __builtin_amdgcn_sched_barrier(0);
   // step 1: half 0 of K-tile kt+1 into the other stage
   bf16_read_frags<0, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
   ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
-  bf16_mma<1, F>(acc, fr);
+  bf16_mma<1, F, 0, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
@@ -108,7 +119,7 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, 
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
   ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   ld.issue_regs(kt + 2);
-  bf16_mma<0, F>(acc, fr);
+  bf16_mma<0, F, 0, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -118,7 +129,7 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, 
   __builtin_amdgcn_sched_group_barrier(0x020, Loader::kRegLoads, 0);
   __builtin_amdgcn_sched_barrier(0);
   // step 3
-  bf16_mma<1, F, 0, kH>(acc, fr);
+  bf16_mma<1, F, 0, kH, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x008, 4 * kH, 0);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<Loader::kRegLoads>();           // K-tile kt+1's loads into LDS have landed
@@ -126,7 +137,7 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][4], Bf16Frags<F>& fr, 
   lds_barrier();
   bf16_read_frags<0, F>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
   ld.issue_lds(kt + 2, bf16_a<CUR>(lds), bf16_b<CUR>(lds));
-  bf16_mma<1, F, kH, F>(acc, fr);
+  bf16_mma<1, F, kH, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 4 * (F - kH), 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -145,7 +156,7 @@ __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][4], Bf16Frags<F>&
   ld.issue_regs(kt + 1);
   ld.issue_lds(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
-  bf16_mma<0, F>(acc, fr);
+  bf16_mma<0, F, 0, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -154,13 +165,13 @@ __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][4], Bf16Frags<F>&
   }
   __builtin_amdgcn_sched_barrier(0);
   bf16_read_frags<0, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 2, wx, wy, lane);
-  bf16_mma<1, F>(acc, fr);
+  bf16_mma<1, F, 0, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, kMma, 0);
   __builtin_amdgcn_sched_barrier(0);
   bf16_read_frags<1, F>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
   ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
-  bf16_mma<0, F>(acc, fr);
+  bf16_mma<0, F, 0, F, Loader::kF16>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + F, 0);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -169,7 +180,7 @@ __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][4], Bf16Frags<F>&
   __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
   ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
-  bf16_mma<1, F>(acc, fr);
+  bf16_mma<1, F, 0, F, Loader::kF16>(acc, fr);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);

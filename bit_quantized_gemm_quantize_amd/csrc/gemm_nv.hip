@@ -1,22 +1,32 @@
-// NVFP4-style GEMM, exact: every operand value e2m1 * s_b (two significant bits
-// times the four of an E4M3 scale) fits bf16 exactly, so each K-tile is dequantized
-// to bf16 in LDS and multiplied on the bf16 MFMA; the two fp32 tensor scales
-// multiply the fp32 result in the epilogue.  The block-scaled FP4 MFMA cannot take
-// this format directly: its scales are powers of two per 32 elements, while an
+// NVFP4-style GEMM, exact: every operand value e2m1 * s_b is zero or has at most six
+// significant bits (two of the E2M1 value times the four of an E4M3 scale) and lies
+// in [2^-10, 2688], inside fp16's normal range.  So each K-tile is dequantized
+// exactly to fp16 in LDS and multiplied on the fp16 MFMA; the two fp32 tensor
+// scales multiply the fp32 result in the epilogue.  The block-scaled FP4 MFMA cannot
+// take this format directly: its scales are powers of two per 32 elements, while an
 // NVFP4 block scale carries mantissa bits and covers 16 elements.
 #include "gemm_bf16_core.h"
 
 namespace q4 {
 
-// 32 E2M1 codes (one 16-byte chunk) times their two block scales -> 4 chunks of bf16.
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+template <int B>
+__device__ __forceinline__ uint32_t nv_pair_f16(uint32_t codes, v2h s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, B) * s);
+}
+
+// 32 E2M1 codes (one 16-byte chunk) times their two block scales -> 4 chunks of fp16.
+// The conversions are exact (scale 1): the two E4M3 scale bytes become an fp16 pair,
+// each pair of codes an fp16 pair (low nibble first), and one packed fp16 multiply by
+// the block's scale gives the exact products (no rounding: they are representable).
 __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x4* out4) {
-  const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)(sc2 & 0xFFu), 0);
-  const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)((sc2 >> 8) & 0xFFu), 0);
+  const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sc2, 1.0f, false);
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const float s = d < 2 ? s0 : s1;
-    out4[d] = u32x4{nv_dequant_pair<0>(codes[d], s), nv_dequant_pair<1>(codes[d], s),
-                    nv_dequant_pair<2>(codes[d], s), nv_dequant_pair<3>(codes[d], s)};
+    const v2h s = d < 2 ? v2h{s01[0], s01[0]} : v2h{s01[1], s01[1]};
+    out4[d] = u32x4{nv_pair_f16<0>(codes[d], s), nv_pair_f16<1>(codes[d], s), nv_pair_f16<2>(codes[d], s),
+                    nv_pair_f16<3>(codes[d], s)};
   }
 }
 
@@ -26,9 +36,10 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
 // checks).
 template <int TN>
 struct NvLoader {
-  static constexpr int kValuPerStore = 192;   // VALU ops of one store part (about)
+  static constexpr int kValuPerStore = 72;    // VALU ops of one store part (about)
   static constexpr int kRegLoads = 4 + 2 * (TN / 128);   // VMEM instructions of issue_regs
-  static constexpr bool kLateStores = true;   // heavy conversion: see bf16_ktile_late
+  static constexpr bool kLateStores = true;   // two operands to convert: see bf16_ktile_late
+  static constexpr bool kF16 = true;          // fp16 operands and MFMA
   __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
   uint32_t kb, sbytes, nchunk;
   int tid;

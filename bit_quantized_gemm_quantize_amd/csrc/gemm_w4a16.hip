@@ -36,6 +36,7 @@ struct W4A16Loader {
   static constexpr int kValuPerStore = 96;   // VALU ops of one store part (about)
   static constexpr int kRegLoads = 3 * (TN / 128);   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = false;
+  static constexpr bool kF16 = false;         // bf16 operands and MFMA
   __amdgpu_buffer_rsrc_t rx, rc, rs, rz;
   uint32_t ldxb, kb, ngrp;
   int tid;
