@@ -30,18 +30,22 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
 // 8 rows x 128 bytes per instruction (lane i -> row i/8, stored position i%8, which
 // holds global chunk (i%8) ^ lds_swz<8>(row)); the weight tile is TN rows x 2 chunks of
 // 32 codes, thread tid owning chunk tid & 1 of rows tid/2 (and tid/2 + 128), with
-// each row's (s, z).  Reads past M / N / K return zeros.
-template <int TN>
+// each row's (s, z).  Reads past M / N / K, and rows past TN, return zeros.  SETS
+// register sets of weight codes and (s, z) rotate, so that a weight load is issued
+// SETS K-tiles before its conversion.
+template <int TN, int SETS>
 struct W4A16Loader {
+  static constexpr int kSets = SETS;
+  static constexpr int kRowGroups = (TN + 127) / 128;   // weight rows per thread
   static constexpr int kValuPerStore = 96;   // VALU ops of one store part (about)
-  static constexpr int kRegLoads = 3 * (TN / 128);   // VMEM instructions of issue_regs
+  static constexpr int kRegLoads = 3 * kRowGroups;   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = false;
   static constexpr bool kF16 = false;         // bf16 operands and MFMA
   __amdgpu_buffer_rsrc_t rx, rc, rs, rz;
   uint32_t ldxb, kb, ngrp;
   int tid;
-  u32x4 cb[2];
-  uint32_t sb[2], zb[2];
+  u32x4 cb[SETS][kRowGroups];
+  uint32_t sb[SETS][kRowGroups], zb[SETS][kRowGroups];
 
   __device__ __forceinline__ void init(const uint16_t* x, int64_t ldx, const uint8_t* wc,
                                        const uint16_t* ws, const uint16_t* wz, int64_t M,
@@ -66,48 +70,53 @@ struct W4A16Loader {
       buf_ld16_lds(rx, la + (64 * wave + 8 * j) * kBf16RowBytes, off);
     }
   }
+  template <int SET>
   __device__ __forceinline__ void issue_regs(int kt) {
     const uint32_t cw = tid & 1;
 #pragma unroll
-    for (int j = 0; j < TN / 128; ++j) {
+    for (int j = 0; j < kRowGroups; ++j) {
       const uint32_t row = (tid >> 1) + 128 * j;
-      cb[j] = buf_ld16(rc, in_range_or_oob(row * kb + (uint32_t)kt * 32 + cw * 16, (uint32_t)kt, ngrp));
+      cb[SET][j] = buf_ld16(rc, in_range_or_oob(row * kb + (uint32_t)kt * 32 + cw * 16, (uint32_t)kt, ngrp));
       const uint32_t go = in_range_or_oob((row * ngrp + (uint32_t)kt) * 2, (uint32_t)kt, ngrp);
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
-      zb[j] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)go, 0, 0);
+      sb[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
+      zb[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rz, (int)go, 0, 0);
     }
   }
   // half P: the weight chunk of row tid/2 + 128 P
-  template <int P>
+  template <int P, int SET>
   __device__ __forceinline__ void store(uint8_t*, uint8_t* lb) {
-    if (P >= TN / 128) return;
+    if (P >= kRowGroups) return;
     const int cw = tid & 1, r = tid >> 1;
     const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
-    const float sc = __uint_as_float(sb[P] << 16);
-    const float zs = __uint_as_float(zb[P] << 16) * sc;
+    const float sc = __uint_as_float(sb[SET][P] << 16);
+    const float zs = __uint_as_float(zb[SET][P] << 16) * sc;
     u32x4 o[4];
-    int4_dequant_chunk(cb[P], sc, zs, o);
+    int4_dequant_chunk(cb[SET][P], sc, zs, o);
 #pragma unroll
     for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * cw + d) ^ lds_swz<8>(r)) << 4), o[d]);
   }
 };
 
-// One output tile of 256 activation rows x 64 F weight rows at (m0, n0).
-template <bool OUT_F32, int F>
+// One output tile of 256 activation rows at (m0, n0).  G = 4: the 4 waves as 2 x 2,
+// each 128 x 32 F (64 F weight rows); G = 2: the 4 waves stacked along M, each
+// 64 x 32 F (32 F weight rows).
+template <bool OUT_F32, int F, int G>
 __device__ __forceinline__ void w4a16_tile(
     uint8_t* lds, const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
+  static_assert(G == 4 || G == 2, "two wave layouts");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wy = wave >> 1, wx = wave & 1;
-  W4A16Loader<64 * F> ld;
+  const int wy = G == 4 ? wave >> 1 : 0, wx = G == 4 ? wave & 1 : wave;
+  // the narrow tile's accumulators leave room for a second register set
+  W4A16Loader<(G == 4 ? 64 : 32) * F, G == 4 ? 1 : 2> ld;
   ld.init(x, ldx, wc, ws, wz, M, N, K, m0, n0, tid);
-  v16f acc[F][4];
+  v16f acc[F][G];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
-  const int64_t n_base = n0 + wy * 32 * F, m_base = m0 + wx * 128;
+  const int64_t n_base = n0 + wy * 32 * F, m_base = m0 + wx * 32 * G;
   __syncthreads();                           // all waves are done reading operand tiles
-  epilogue_store<OUT_F32>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
-                          lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
+  epilogue_store<OUT_F32, F, 128, false, G>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                                            lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
 }
 
 // Whole 256 x 256 tiles and halves (256 x 128) of the leftover ones: see tile_unit.
@@ -123,19 +132,47 @@ __global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
   const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
   tile_of(vt, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   if (!is_half) {
-    w4a16_tile<OUT_F32, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
-                           (int64_t)tn * kBf16BN);
+    w4a16_tile<OUT_F32, 4, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
+                              (int64_t)tn * kBf16BN);
   } else {
     if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
-    w4a16_tile<OUT_F32, 2>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
-                           (int64_t)tn * kBf16BN + 128 * half);
+    w4a16_tile<OUT_F32, 2, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
+                              (int64_t)tn * kBf16BN + 128 * half);
   }
+}
+
+// Few activation rows (M = 512 at N = 12288): tiles of 256 x 96, whose count fits
+// one round over the CUs, where 256 x 256 tiles and their halves would leave CUs idle
+// (96 tiles -> 192 halves of 256 x 128 on 256 CUs; 256 tiles of 256 x 96 do 0.75 of
+// a half's work each).
+constexpr int kW4NarrowN = 96;
+template <bool OUT_F32>
+__global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_narrow_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
+    const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
+  w4a16_tile<OUT_F32, kW4NarrowN / 32, 2>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy,
+                                          (int64_t)tm * kBf16BM, (int64_t)tn * kW4NarrowN);
 }
 
 hipError_t launch_gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* wc,
                              const uint16_t* ws, const uint16_t* wz, int64_t M, int64_t N,
                              int64_t K, const EpilogueArgs& ep, hipStream_t s) {
   const int tiles_m = (int)((M + kBf16BM - 1) / kBf16BM), tiles_n = (int)((N + kBf16BN - 1) / kBf16BN);
+  const int64_t narrow_n = (N + kW4NarrowN - 1) / kW4NarrowN;
+  if ((int64_t)tiles_m * narrow_n <= bf16_cus()) {
+    const int tn = (int)narrow_n, grid = tiles_m * tn;
+    if (ep.out_f32)
+      hipLaunchKernelGGL(gemm_w4a16_narrow_kernel<true>, dim3(grid), dim3(kBf16Threads), 0, s, x, ldx, wc,
+                         ws, wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tn);
+    else
+      hipLaunchKernelGGL(gemm_w4a16_narrow_kernel<false>, dim3(grid), dim3(kBf16Threads), 0, s, x, ldx, wc,
+                         ws, wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tn);
+    return hipGetLastError();
+  }
   int full, grid;
   bf16_tile_split(tiles_m * tiles_n, &full, &grid);
   if (ep.out_f32)

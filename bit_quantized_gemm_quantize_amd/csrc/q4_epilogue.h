@@ -127,8 +127,15 @@ template <bool OUT_F32, int F, int ROW_BYTES>
 struct EpilogueShape {
   static constexpr int kElem = OUT_F32 ? 4 : 2;
   static constexpr int kFPerPassMax = ROW_BYTES / (32 * kElem);          // 32-column blocks
-  static constexpr int kFPerPass = F < kFPerPassMax ? F : kFPerPassMax;
+  // the largest count of sub-tiles per pass that fits the row and divides F
+  static constexpr int per_pass() {
+    int d = F < kFPerPassMax ? F : kFPerPassMax;
+    while (F % d != 0) --d;
+    return d;
+  }
+  static constexpr int kFPerPass = per_pass();
   static constexpr int kPasses = F / kFPerPass;
+  static_assert(kPasses * kFPerPass == F, "every sub-tile is staged");
   static constexpr int kRowBytes = 32 * kFPerPass * kElem;
   static constexpr int kStageRowBytes = kRowBytes + 16;
   static constexpr int kStageWaveBytes = 128 * kStageRowBytes;
@@ -139,9 +146,10 @@ constexpr int kEpilogueLdsBytes = 4 * EpilogueShape<true, 4, 128>::kStageWaveByt
 
 // One staging pass: the accumulators of weight sub-tiles pass * kFPerPass ..
 // + kFPerPass - 1, scaled (SCALED) and with the bias added (BIAS), into this wave's
-// LDS rows: row m_local = 32 g + lane%32, columns 32 f' + 8 vq + 4 h .. +3.
-template <bool OUT_F32, int F, int ROW_BYTES, bool SCALED, bool BIAS>
-__device__ __forceinline__ void epilogue_stage_pass(v16f (&acc)[F][4], int pass, int64_t n_base,
+// LDS rows: row m_local = 32 g + lane%32 (G activation sub-tiles of 32 rows),
+// columns 32 f' + 8 vq + 4 h .. +3.
+template <bool OUT_F32, int F, int ROW_BYTES, bool SCALED, bool BIAS, int G = 4>
+__device__ __forceinline__ void epilogue_stage_pass(v16f (&acc)[F][G], int pass, int64_t n_base,
                                                     int64_t N, const uint16_t* __restrict__ bias,
                                                     int lane, uint8_t* stage, float scale) {
   using S = EpilogueShape<OUT_F32, F, ROW_BYTES>;
@@ -161,7 +169,7 @@ __device__ __forceinline__ void epilogue_stage_pass(v16f (&acc)[F][4], int pass,
           if (n + j < N) b[j] = __uint_as_float((uint32_t)bias[n + j] << 16);
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G; ++g) {
         uint8_t* dst = stage + (32 * g + r32) * S::kStageRowBytes + (32 * fp + 8 * vq + 4 * h) * kElem;
         float a[4];
 #pragma unroll
@@ -184,11 +192,12 @@ __device__ __forceinline__ void epilogue_stage_pass(v16f (&acc)[F][4], int pass,
   }
 }
 
-// y = scale * acc + bias (SCALED), or acc + bias.  The bias is added, and the
-// scale applied, pass by pass, so only the accumulators being staged are moved out
-// of the matrix registers; without a bias the add is skipped.
-template <bool OUT_F32, int F, int ROW_BYTES = 128, bool SCALED = false>
-__device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base, int64_t m_base,
+// y = scale * acc + bias (SCALED), or acc + bias, for a wave region of 32 G rows.
+// The bias is added, and the scale applied, pass by pass, so only the accumulators
+// being staged are moved out of the matrix registers; without a bias the add is
+// skipped.
+template <bool OUT_F32, int F, int ROW_BYTES = 128, bool SCALED = false, int G = 4>
+__device__ __forceinline__ void epilogue_store(v16f (&acc)[F][G], int64_t n_base, int64_t m_base,
                                                int64_t M, int64_t N,
                                                const uint16_t* __restrict__ bias, void* y,
                                                int64_t ldy, int lane, uint8_t* stage,
@@ -209,16 +218,16 @@ __device__ __forceinline__ void epilogue_store(v16f (&acc)[F][4], int64_t n_base
     // fp32 output keeps one path (a second copy of the pass made the compiler spill);
     // it reads the bias only when there is one
     if (OUT_F32 || bias)
-      epilogue_stage_pass<OUT_F32, F, ROW_BYTES, SCALED, true>(acc, pass, n_base, N, bias, lane, stage, scale);
+      epilogue_stage_pass<OUT_F32, F, ROW_BYTES, SCALED, true, G>(acc, pass, n_base, N, bias, lane, stage, scale);
     else
-      epilogue_stage_pass<OUT_F32, F, ROW_BYTES, SCALED, false>(acc, pass, n_base, N, bias, lane, stage, scale);
+      epilogue_stage_pass<OUT_F32, F, ROW_BYTES, SCALED, false, G>(acc, pass, n_base, N, bias, lane, stage, scale);
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     // LDS -> global: kLanesPerRow lanes per row (16 bytes each), whole row segments
     const int col_bytes = (lane % kLanesPerRow) * 16;
     const int64_t n = n_base + pass * kColsPerPass + col_bytes / kElem;
 #pragma unroll 4
-    for (int it = 0; it < 128 / kRowsPerStore; ++it) {
+    for (int it = 0; it < 32 * G / kRowsPerStore; ++it) {
       const int ml = kRowsPerStore * it + lane / kLanesPerRow;
       const int64_t m = m_base + ml;
       const u32x4 v = ld16(stage + ml * kStageRow + col_bytes);

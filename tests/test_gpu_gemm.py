@@ -277,12 +277,29 @@ def test_gemm_w4a16_parity(M, N, K):
         _check(y, y_ref, bound, not f32, f"w4a16 {M}x{N}x{K}")
 
 
-def test_full_w4a16_sampled_rows():
+# Both tilings of the W4A16 GEMM, with ragged M and N: few rows take 256 x 96 tiles
+# (one round over the CUs), more rows 256 x 256 tiles and halves of the leftover
+# ones.  Every element is checked.
+@pytest.mark.parametrize("M,N,K", [(500, 11990, 192), (2100, 8000, 128), (257, 24576, 64)])
+def test_gemm_w4a16_tilings(M, N, K):
+    dev = device()
+    x = synth.activations(M, K, seed=M + 7)[0]
+    wt = synth.weights(N, K, seed=N + 3)
+    bias = synth.bias(N, seed=4)
+    say(f"gemm_w4a16 tilings M={M} N={N} K={K} bf16 bias")
+    y = run_w4a16(x, wt, dev, bias=bias, f32=False)
+    y_ref, bound = ref_w4a16(x, wt, bias=bias)
+    _check(y, y_ref, bound, True, f"w4a16 {M}x{N}x{K}")
+
+
+def test_full_w4a16_layer():
+    """The comparison layer at M = 512 (every element) and M = 4608 (sampled rows)."""
     dev = device()
     for M in (512, 4608):
         d = synth.w4a16_layer(M)
         say(f"full layer w4a16 {M}x3072x12288")
         y = run_w4a16(d["x"], d["wt"], dev, f32=False)
-        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 30)]))
+        rows = (np.arange(M) if M <= 512 else
+                np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 30)])))
         y_ref, bound = ref_w4a16(d["x"], d["wt"], rows=rows)
         _check(y[rows], y_ref, bound, True, f"full W4A16 M={M}")
