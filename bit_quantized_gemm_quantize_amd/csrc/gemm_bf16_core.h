@@ -149,17 +149,21 @@ __device__ __forceinline__ void bf16_ktile(v16f (&acc)[F][G], Bf16Frags<F, G>& f
 }
 
 // The same K-tile for loaders whose conversion is heavy (Loader::kLateStores): the
-// register loads of K-tile kt+1 go out in step 0, its conversion fills steps 2 and
-// 3, and the barrier closes the K-tile.  Converting in steps 1 and 2 instead would
-// leave the heavy arithmetic less latency cover for the loads it waits on.
+// register loads of K-tile kt+S go out in step 0 (S = Loader::kSets register sets),
+// the conversion of K-tile kt+1 fills steps 2 and 3, and the barrier closes the
+// K-tile.  Converting in steps 1 and 2 instead would leave the heavy arithmetic less
+// latency cover for the loads it waits on.
 template <int CUR, int F, int G, class Loader>
 __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][G], Bf16Frags<F, G>& fr, Loader& ld,
                                                 int kt, uint8_t* lds, int wx, int wy, int lane) {
   constexpr int NXT = CUR ^ 1;
   constexpr int kMma = G * F;
   constexpr int kValu = (Loader::kValuPerStore + kMma - 1) / kMma;
-  ld.issue_regs(kt + 1);
+  constexpr int SETL = Loader::kSets == 2 ? CUR : 0;           // receives K-tile kt+S
+  constexpr int SETC = Loader::kSets == 2 ? NXT : 0;           // holds K-tile kt+1
+  // direct loads first: the wait at the end leaves only the register loads in flight
   ld.issue_lds(kt + 1, bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  ld.template issue_regs<SETL>(kt + Loader::kSets);
   bf16_read_frags<1, F, G>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 1, wx, wy, lane);
   bf16_mma<0, F, 0, F, Loader::kF16, G>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, G + F, 0);
@@ -175,7 +179,7 @@ __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][G], Bf16Frags<F, 
   __builtin_amdgcn_sched_group_barrier(0x008, kMma, 0);
   __builtin_amdgcn_sched_barrier(0);
   bf16_read_frags<1, F, G>(fr, bf16_a<CUR>(lds), bf16_b<CUR>(lds), 3, wx, wy, lane);
-  ld.template store<0>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  ld.template store<0, SETC>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_mma<0, F, 0, F, Loader::kF16, G>(acc, fr);
   __builtin_amdgcn_sched_group_barrier(0x100, G + F, 0);
   for (int i = 0; i < kMma; ++i) {
@@ -184,7 +188,7 @@ __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][G], Bf16Frags<F, 
   }
   __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
-  ld.template store<1>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
+  ld.template store<1, SETC>(bf16_a<NXT>(lds), bf16_b<NXT>(lds));
   bf16_mma<1, F, 0, F, Loader::kF16, G>(acc, fr);
   for (int i = 0; i < kMma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -192,7 +196,7 @@ __device__ __forceinline__ void bf16_ktile_late(v16f (&acc)[F][G], Bf16Frags<F, 
   }
   __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmem();
+  wait_vmcnt<(Loader::kSets - 1) * Loader::kRegLoads>();     // K-tile kt+S's loads may stay in flight
   lds_barrier();
   bf16_read_frags<0, F, G>(fr, bf16_a<NXT>(lds), bf16_b<NXT>(lds), 0, wx, wy, lane);
 }
@@ -207,12 +211,14 @@ __device__ __forceinline__ void bf16_mainloop(v16f (&acc)[F][G], Loader& ld, int
     for (int g = 0; g < G; ++g) acc[f][g] = v16f{};
   if (nkt == 0) return;
   Bf16Frags<F, G> fr;
+  static_assert(Loader::kSets == 1 || Loader::kSets == 2, "one or two register sets");
   if constexpr (Loader::kLateStores) {
     ld.issue_lds(0, bf16_a<0>(lds), bf16_b<0>(lds));
-    ld.issue_regs(0);
-    ld.template store<0>(bf16_a<0>(lds), bf16_b<0>(lds));
-    ld.template store<1>(bf16_a<0>(lds), bf16_b<0>(lds));
-    wait_vmem();
+    ld.template issue_regs<0>(0);
+    if constexpr (Loader::kSets == 2) ld.template issue_regs<1>(1);
+    ld.template store<0, 0>(bf16_a<0>(lds), bf16_b<0>(lds));
+    ld.template store<1, 0>(bf16_a<0>(lds), bf16_b<0>(lds));
+    wait_vmcnt<(Loader::kSets - 1) * Loader::kRegLoads>();
     lds_barrier();
     bf16_read_frags<0, F, G>(fr, bf16_a<0>(lds), bf16_b<0>(lds), 0, wx, wy, lane);
     int kt = 0;
@@ -223,8 +229,7 @@ __device__ __forceinline__ void bf16_mainloop(v16f (&acc)[F][G], Loader& ld, int
     if (kt < nkt) bf16_ktile_late<0, F, G>(acc, fr, ld, kt, lds, wx, wy, lane);
   } else {
     // register set (kt % 2 with two sets) of K-tile kt; K-tile 1 goes into set 1
-    // before K-tile 0 is converted, then K-tile S+1 into set 0 (S = kSets)
-    static_assert(Loader::kSets == 1 || Loader::kSets == 2, "one or two register sets");
+    // before K-tile 0 is converted, then K-tile S into set 0 (S = kSets)
     ld.issue_lds(0, bf16_a<0>(lds), bf16_b<0>(lds));
     ld.template issue_regs<0>(0);
     if constexpr (Loader::kSets == 2) ld.template issue_regs<1>(1);

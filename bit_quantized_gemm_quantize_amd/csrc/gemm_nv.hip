@@ -34,8 +34,9 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
 // thread tid owns chunk c = tid & 1 of rows tid/2 and tid/2 + 128, with the two
 // E4M3 scale bytes of each chunk.  Reads past M / N / K return zeros (buffer range
 // checks).
-template <int TN>
+template <int TN, int SETS>
 struct NvLoader {
+  static constexpr int kSets = SETS;          // register sets: loads SETS K-tiles ahead
   static constexpr int kValuPerStore = 72;    // VALU ops of one store part (about)
   static constexpr int kRegLoads = 4 + 2 * (TN / 128);   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = true;   // two operands to convert: see bf16_ktile_late
@@ -43,8 +44,8 @@ struct NvLoader {
   __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
   uint32_t kb, sbytes, nchunk;
   int tid;
-  u32x4 ca[2], cb[2];
-  uint32_t sa[2], sb[2];
+  u32x4 ca[SETS][2], cb[SETS][2];
+  uint32_t sa[SETS][2], sb[SETS][2];
 
   __device__ __forceinline__ void init(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                                        const uint8_t* bs, int64_t M, int64_t N, int64_t K,
@@ -58,6 +59,7 @@ struct NvLoader {
     tid = t;
   }
   __device__ __forceinline__ void issue_lds(int, uint8_t*, uint8_t*) {}   // all through registers
+  template <int SET>
   __device__ __forceinline__ void issue_regs(int kt) {
     const uint32_t chunk = (uint32_t)kt * 2 + (tid & 1);
 #pragma unroll
@@ -65,26 +67,26 @@ struct NvLoader {
       const uint32_t row = (tid >> 1) + 128 * j;
       const uint32_t co = in_range_or_oob(row * kb + chunk * 16, chunk, nchunk);
       const uint32_t so = in_range_or_oob(row * sbytes + chunk * 2, chunk, nchunk);
-      ca[j] = buf_ld16(rca, co);
-      sa[j] = __builtin_amdgcn_raw_buffer_load_b16(rsa, (int)so, 0, 0);
+      ca[SET][j] = buf_ld16(rca, co);
+      sa[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rsa, (int)so, 0, 0);
       if (j < TN / 128) {
-        cb[j] = buf_ld16(rcb, co);
-        sb[j] = __builtin_amdgcn_raw_buffer_load_b16(rsb, (int)so, 0, 0);
+        cb[SET][j] = buf_ld16(rcb, co);
+        sb[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rsb, (int)so, 0, 0);
       }
     }
   }
   // half P: both operands' chunks of row group P
-  template <int P>
+  template <int P, int SET>
   __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb) {
     // row (tid >> 1) + 128 P: its swizzle does not depend on P
     const int c = tid & 1, r = tid >> 1;
     const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
     u32x4 o[4];
-    nv_dequant_chunk(ca[P], sa[P], o);
+    nv_dequant_chunk(ca[SET][P], sa[SET][P], o);
 #pragma unroll
     for (int d = 0; d < 4; ++d) st16(la + off + (((4 * c + d) ^ lds_swz<8>(r)) << 4), o[d]);
     if (P < TN / 128) {
-      nv_dequant_chunk(cb[P], sb[P], o);
+      nv_dequant_chunk(cb[SET][P], sb[SET][P], o);
 #pragma unroll
       for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ lds_swz<8>(r)) << 4), o[d]);
     }
@@ -101,7 +103,8 @@ __device__ __forceinline__ void nv_tile(
     int64_t ldy, int64_t m0, int64_t n0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;
-  NvLoader<64 * F> ld;
+  // one register set: a second one (loads two K-tiles ahead) measured the same
+  NvLoader<64 * F, 1> ld;
   ld.init(ac, as, bc, bs, M, N, K, m0, n0, tid);
   v16f acc[F][4];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
