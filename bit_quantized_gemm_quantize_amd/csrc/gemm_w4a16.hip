@@ -11,8 +11,12 @@ namespace q4 {
 __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float zs, u32x4* out4) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = codes[d] & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6 of the dword
-    const uint32_t hi = (codes[d] >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+    uint32_t lo = codes[d] & 0x0F0F0F0Fu;                // codes 0, 2, 4, 6 of the dword
+    uint32_t hi = (codes[d] >> 4) & 0x0F0F0F0Fu;         // codes 1, 3, 5, 7
+    // opaque to the compiler: it would otherwise see 4-bit fields and extract each
+    // code with a bit-field extract before converting, where the byte-select
+    // conversion (v_cvt_f32_ubyte0..3) reads the byte directly
+    asm volatile("" : "+v"(lo), "+v"(hi));
     uint32_t o[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
