@@ -322,7 +322,7 @@ def bench_rows(reps=50):
     ms = timed(lambda i: B.gemm_w4a4("nvfp4", nc, nsc, nts, bnc, bnsc, bnts, Mn, Nn, Kn, yq,
                                      stream=stream), 1)
     emit(f"gemm_w4a4 nvfp4 {Mn}x{Kn}x{Nn}", ms, flops=2.0 * Mn * Nn * Kn, peak=2500.0,
-         note="exact bf16 dequant + bf16 MFMA; peak = dense bf16")
+         note="exact fp16 dequant + fp16 MFMA; peak = dense bf16 and fp16 (2.5 PF)")
     del xns, xn0, yq, wq
 
     # ---- a4: packers, MLP up-projection residual weight [N, K]
