@@ -592,6 +592,106 @@ def bench_rows(reps=50):
                               "and smoothing + activation-weighted rank-32 split"}), flush=True)
 
 
+def bench_bf16_gemms(reps=50):
+    """The GEMMs on the 16-bit MFMA and the vendor bf16 GEMM they are compared with,
+    timed like the rows (one JSON line each): the NVFP4 GEMM at the fused-QKV shape
+    (16896x3072x9216), W4A16 at M = 512 and 4608 (K = 3072, N = 12288), and torch's
+    bf16 matmul (hipBLASLt) at the W4A16 shapes.  A short pass for counter runs."""
+    import torch
+    from bit_quantized_gemm_quantize_amd import binding as B
+    from bit_quantized_gemm_quantize_amd import synth
+
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        for _ in range(max(3, min(2000, int(80.0 / max(e0.elapsed_time(e1), 1e-3))))):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def emit(row, ms, flops):
+        tf = flops / (ms * 1e-3) / 1e12
+        print(json.dumps({"row": row, "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "peak": 2500.0,
+                          "frac": round(tf / 2500.0, 4)}), flush=True)
+
+    Mn, Kn, Nn = 16896, 3072, 9216
+    xn = bf16_dev(synth.qkv_nvfp4(step=0)["x"])
+    nc, nsc, nts = B.empty_quant("nvfp4", Mn, Kn, dev)
+    B.quantize_act("nvfp4", xn, nc, nsc, nts, stream=stream)
+    wq = bf16_dev(synth.qkv_nvfp4_weight())
+    bnc, bnsc, bnts = B.empty_quant("nvfp4", Nn, Kn, dev)
+    B.pack_weights("nvfp4", wq, Kn, Nn, 1, Kn, bnc, bnsc, tensor_scale=bnts, stream=stream)
+    yq = torch.empty((Mn, Nn), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: B.gemm_w4a4("nvfp4", nc, nsc, nts, bnc, bnsc, bnts, Mn, Nn, Kn, yq, stream=stream))
+    emit(f"gemm_w4a4 nvfp4 {Mn}x{Kn}x{Nn}", ms, 2.0 * Mn * Nn * Kn)
+    del xn, wq, yq
+
+    Kq, Np = 3072, 12288
+    wt = bf16_dev(synth.weights(Np, Kq, seed=0))
+    ic, isc, izc = B.empty_quant("int4_g64", Np, Kq, dev)
+    B.pack_weights("int4_g64", wt, Kq, Np, 1, Kq, ic, isc, izc, stream=stream)
+    for m in (512, 4608):
+        xw = bf16_dev(synth.activations(m, Kq, seed=m)[0])
+        y = torch.empty((m, Np), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda: B.gemm_w4a16(xw, ic, isc, izc, Np, y, stream=stream))
+        emit(f"gemm_w4a16 {m}x{Kq}x{Np}", ms, 2.0 * m * Np * Kq)
+        ms = timed(lambda: torch.matmul(xw, wt.t(), out=y))
+        emit(f"torch bf16 matmul {m}x{Kq}x{Np}", ms, 2.0 * m * Np * Kq)
+
+
+def summarize_kernel_util(util_csv, stats_csv, command, title):
+    """Per kernel of a rocprofv3 --pmc run of the utilisation counters: the MFMA pipe's
+    busy cycles against the shader engines' busy cycles and the GPU's, and the share
+    of wave cycles spent waiting, averaged over the last quarter of each kernel's
+    dispatches; with the kernel's average duration from a --stats run."""
+    acc = {}
+    for r in _csv_rows(util_csv):
+        d = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in _csv_rows(stats_csv)} if stats_csv else {}
+    lines = [f"# rocprofv3 summary: {title}", "",
+             "commands (R = the repository root; each run after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    lines += ["    " + c for c in command]
+    lines += ["", "Counters per dispatch, summed over the chip: SQ_VALU_MFMA_BUSY_CYCLES over the 1024 "
+                  "SIMDs, SQ_BUSY_CYCLES over the 32 shader engines, GRBM_GUI_ACTIVE over the 8 XCDs; "
+                  "the last quarter of each kernel's dispatches (settled clocks).", "",
+              "| kernel | dispatches | average us (stats run) | MFMA busy / SQ busy | MFMA busy / GPU busy | "
+              "SQ_WAIT_ANY / SQ_WAVE_CYCLES |", "|---|---|---|---|---|---|"]
+    for name, per in sorted(acc.items(), key=lambda kv: -len(kv[1])):
+        disp = [per[k] for k in sorted(per, key=int)]
+        disp = [d for d in disp[-max(1, len(disp) // 4):] if "SQ_VALU_MFMA_BUSY_CYCLES" in d]
+        if not disp or not any(d["SQ_VALU_MFMA_BUSY_CYCLES"] > 0 for d in disp):
+            continue
+        mean = {c: float(np.mean([d[c] for d in disp])) for c in disp[0]}
+        mfma = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        us = dur.get(name)
+        lines.append(f"| `{short[:90]}` | {len(per)} | {'' if us is None else f'{us:.2f}'} | "
+                     f"{100 * mfma / (mean['SQ_BUSY_CYCLES'] / 32.0):.1f}% | "
+                     f"{100 * mfma / (mean['GRBM_GUI_ACTIVE'] / 8.0):.1f}% | "
+                     f"{100 * mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.1f}% |")
+    lines += ["", "Kernels named `Cijk_*` are hipBLASLt's bf16 GEMMs behind torch.matmul."]
+    return "\n".join(lines) + "\n"
+
+
 def summarize_rows_profile(stats_csv, command):
     """rocprofv3 --kernel-trace --stats of `bench.py --rows` -> a text table of every
     kernel's average duration (the per-row numbers' own kernels)."""
@@ -622,6 +722,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true",
                     help="time every other step of the path, one JSON line per row")
+    ap.add_argument("--bf16-gemms", action="store_true",
+                    help="time the NVFP4 and W4A16 GEMMs and the vendor bf16 GEMM, one JSON line each")
+    ap.add_argument("--summarize-util", nargs=2, metavar=("UTIL_CSV", "STATS_CSV"),
+                    help="write the per-kernel counter summary of a `--bf16-gemms` run under profiles/")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the rocprofv3 summary under profiles/ (no GPU needed)")
     ap.add_argument("--summarize-rows", metavar="STATS_CSV",
@@ -652,8 +756,19 @@ def main():
             f.write(text)
         print(text)
         return
+    if a.summarize_util:
+        text = summarize_kernel_util(*a.summarize_util, a.command,
+                                     "MFMA utilisation of the 16-bit-MFMA GEMMs and the vendor bf16 GEMM "
+                                     "(`bench.py --bf16-gemms`, one MI355X)")
+        with open(os.path.join(ROOT, "profiles", "bf16_gemms_counters.md"), "w") as f:
+            f.write(text)
+        print(text)
+        return
     if a.rows:
         bench_rows()
+        return
+    if a.bf16_gemms:
+        bench_bf16_gemms()
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
