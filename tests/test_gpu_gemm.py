@@ -261,6 +261,33 @@ def test_full_qkv_nvfp4(step):
     print(f"full QKV NVFP4: worst |err|/tol = {worst:.4g}")
 
 
+def _blockwise_range(rows, K, seed):
+    """bf16 [rows, K]: N(0, 1) values, each 16-element block scaled by its own 2**u,
+    u ~ U(-20, 0), so that the NVFP4 block scales (relative to the tensor maximum)
+    run from E4M3 subnormals to the top of the range."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(-20, 0, size=(rows, K // 16))
+    return synth.to_bf16_bits(rng.standard_normal((rows, K)) * np.repeat(2.0 ** u, 16, axis=1))
+
+
+def test_gemm_nvfp4_block_scales_over_the_e4m3_range():
+    """The NVFP4 GEMM dequantizes e2m1 * s_b exactly in fp16: check it where the block
+    scales reach both ends of E4M3 (subnormal scales, products down to 2**-10, and
+    scales near 448) in both operands, with ragged M and N."""
+    dev = device()
+    M, N, K = 200, 264, 512
+    x = _blockwise_range(M, K, 21)
+    wt = _blockwise_range(N, K, 22)
+    for bits in (x, wt):
+        sb = Q.nv_quantize(bits)[1]
+        assert np.any(((sb & 0x78) == 0) & ((sb & 0x07) != 0))          # subnormal scales
+        assert np.any((sb & 0x7F) >= 0x70)                               # scales of 256 and up
+    say("gemm_w4a4 nvfp4 block scales over the E4M3 range, f32")
+    y = run_w4a4("nvfp4", x, wt, dev, f32=True)
+    y_ref, bound = ref_w4a4("nvfp4", x, wt)
+    _check(y, y_ref, bound, False, "nvfp4 E4M3 range")
+
+
 # ------------------------------------------------------------------ W4A16
 def run_w4a16(x, wt, dev, bias=None, f32=True):
     M, K = x.shape
