@@ -207,8 +207,9 @@ Q4_API q4_status pack_weights(q4_format fmt, const uint16_t* w, int64_t K, int64
  * branch carries about 95% of the compute per the decomposition figure).
  *
  *   fmt       Q4_MXFP4: block-scaled FP4 MFMA.  Q4_NVFP4: exact dequantization
- *             to bf16 (every E2M1 x E4M3 product fits bf16) and bf16 MFMA; the two
- *             tensor scales multiply the fp32 result.
+ *             to fp16 (every E2M1 x E4M3 product is an fp16 normal or zero) and
+ *             fp16 MFMA -- bf16 when K is not a multiple of 128; the two tensor
+ *             scales multiply the fp32 result.
  *             Q4_INT4_SYM: int4 codes widened to int8 for the INT8 MFMA, int32
  *             sums, fp32 row scales (a_scales float [M], b_scales float [N])
  *             applied in the epilogue (gemm_w4a4 only).
