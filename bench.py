@@ -657,15 +657,30 @@ def bench_bf16_gemms(reps=50):
         emit(f"torch bf16 matmul {m}x{Kq}x{Np}", ms, 2.0 * m * Np * Kq)
 
 
-def summarize_kernel_util(util_csv, stats_csv, command, title):
+def _per_kernel_means(csv_path):
+    """Counter means per kernel over the last quarter of its dispatches (each counter
+    summed over the chip per dispatch), and the kernel's dispatch count."""
+    acc = {}
+    for r in _csv_rows(csv_path):
+        d = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for name, per in acc.items():
+        disp = [per[k] for k in sorted(per, key=int)]
+        disp = disp[-max(1, len(disp) // 4):]
+        out[name] = ({c: float(np.mean([d.get(c, 0.0) for d in disp])) for c in disp[0]}, len(per))
+    return out
+
+
+def summarize_kernel_util(util_csv, stats_csv, command, title, lds_csv=None):
     """Per kernel of a rocprofv3 --pmc run of the utilisation counters: the MFMA pipe's
     busy cycles against the shader engines' busy cycles and the GPU's, and the share
     of wave cycles spent waiting, averaged over the last quarter of each kernel's
-    dispatches; with the kernel's average duration from a --stats run."""
-    acc = {}
-    for r in _csv_rows(util_csv):
-        d = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
-        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dispatches; with the kernel's average duration from a --stats run and, from a
+    second --pmc run (lds_csv), its LDS-active cycles per shader-engine busy cycle and
+    the bank-conflict share of them."""
+    util = _per_kernel_means(util_csv)
+    lds = _per_kernel_means(lds_csv) if lds_csv else {}
     dur = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in _csv_rows(stats_csv)} if stats_csv else {}
     lines = [f"# rocprofv3 summary: {title}", "",
              "commands (R = the repository root; each run after `cd /tmp && export TMPDIR=/tmp`):", ""]
@@ -674,21 +689,25 @@ def summarize_kernel_util(util_csv, stats_csv, command, title):
                   "SIMDs, SQ_BUSY_CYCLES over the 32 shader engines, GRBM_GUI_ACTIVE over the 8 XCDs; "
                   "the last quarter of each kernel's dispatches (settled clocks).", "",
               "| kernel | dispatches | average us (stats run) | MFMA busy / SQ busy | MFMA busy / GPU busy | "
-              "SQ_WAIT_ANY / SQ_WAVE_CYCLES |", "|---|---|---|---|---|---|"]
-    for name, per in sorted(acc.items(), key=lambda kv: -len(kv[1])):
-        disp = [per[k] for k in sorted(per, key=int)]
-        disp = [d for d in disp[-max(1, len(disp) // 4):] if "SQ_VALU_MFMA_BUSY_CYCLES" in d]
-        if not disp or not any(d["SQ_VALU_MFMA_BUSY_CYCLES"] > 0 for d in disp):
+              "SQ_WAIT_ANY / SQ_WAVE_CYCLES | SQ_LDS_IDX_ACTIVE / SQ_BUSY_CYCLES | "
+              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE |", "|---|---|---|---|---|---|---|---|"]
+    for name, (mean, n) in sorted(util.items(), key=lambda kv: -kv[1][1]):
+        if mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) <= 0:
             continue
-        mean = {c: float(np.mean([d[c] for d in disp])) for c in disp[0]}
         mfma = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         us = dur.get(name)
-        lines.append(f"| `{short[:90]}` | {len(per)} | {'' if us is None else f'{us:.2f}'} | "
+        lm = lds.get(name, ({}, 0))[0]
+        lds_cols = (f"{lm['SQ_LDS_IDX_ACTIVE'] / lm['SQ_BUSY_CYCLES']:.2f} | "
+                    f"{lm['SQ_LDS_BANK_CONFLICT'] / max(lm['SQ_LDS_IDX_ACTIVE'], 1.0):.2f}"
+                    if lm.get("SQ_BUSY_CYCLES") else " | ")
+        lines.append(f"| `{short[:90]}` | {n} | {'' if us is None else f'{us:.2f}'} | "
                      f"{100 * mfma / (mean['SQ_BUSY_CYCLES'] / 32.0):.1f}% | "
                      f"{100 * mfma / (mean['GRBM_GUI_ACTIVE'] / 8.0):.1f}% | "
-                     f"{100 * mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.1f}% |")
-    lines += ["", "Kernels named `Cijk_*` are hipBLASLt's bf16 GEMMs behind torch.matmul."]
+                     f"{100 * mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.1f}% | {lds_cols} |")
+    lines += ["", "The LDS ratios are on the counters' own scale (both summed over the chip), for "
+                  "comparing kernels with one another.", "",
+              "Kernels named `Cijk_*` are hipBLASLt's bf16 GEMMs behind torch.matmul."]
     return "\n".join(lines) + "\n"
 
 
@@ -726,6 +745,9 @@ def main():
                     help="time the NVFP4 and W4A16 GEMMs and the vendor bf16 GEMM, one JSON line each")
     ap.add_argument("--summarize-util", nargs=2, metavar=("UTIL_CSV", "STATS_CSV"),
                     help="write the per-kernel counter summary of a `--bf16-gemms` run under profiles/")
+    ap.add_argument("--lds", metavar="LDS_CSV",
+                    help="with --summarize-util: the counter_collection CSV of the --pmc "
+                         "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES run")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the rocprofv3 summary under profiles/ (no GPU needed)")
     ap.add_argument("--summarize-rows", metavar="STATS_CSV",
@@ -759,7 +781,7 @@ def main():
     if a.summarize_util:
         text = summarize_kernel_util(*a.summarize_util, a.command,
                                      "MFMA utilisation of the 16-bit-MFMA GEMMs and the vendor bf16 GEMM "
-                                     "(`bench.py --bf16-gemms`, one MI355X)")
+                                     "(`bench.py --bf16-gemms`, one MI355X)", lds_csv=a.lds)
         with open(os.path.join(ROOT, "profiles", "bf16_gemms_counters.md"), "w") as f:
             f.write(text)
         print(text)
