@@ -33,14 +33,16 @@ __device__ __forceinline__ void int4_dequant_chunk(u32x4 codes, float s, float z
 // bytes of bf16) goes straight into LDS, each wave moving rows 64 w .. 64 w + 63 as
 // 8 rows x 128 bytes per instruction (lane i -> row i/8, stored position i%8, which
 // holds global chunk (i%8) ^ lds_swz<8>(row)); the weight tile is TN rows x 2 chunks of
-// 32 codes, thread tid owning chunk tid & 1 of rows tid/2 (and tid/2 + 128), with
-// each row's (s, z).  Reads past M / N / K, and rows past TN, return zeros.  SETS
-// register sets of weight codes and (s, z) rotate, so that a weight load is issued
-// SETS K-tiles before its conversion.
-template <int TN, int SETS>
+// 32 codes, thread tid owning chunk tid & 1 of rows tid/2 (and tid/2 + THREADS/2),
+// with each row's (s, z).  Reads past M / N / K, and rows past TN, return zeros.
+// SETS register sets of weight codes and (s, z) rotate, so that a weight load is
+// issued SETS K-tiles before its conversion.  THREADS: 256 (4 waves) or 512 (8).
+template <int TN, int SETS, int THREADS = 256>
 struct W4A16Loader {
   static constexpr int kSets = SETS;
-  static constexpr int kRowGroups = (TN + 127) / 128;   // weight rows per thread
+  static constexpr int kRowsPerGroup = THREADS / 2;
+  static constexpr int kRowGroups = (TN + kRowsPerGroup - 1) / kRowsPerGroup;   // weight rows per thread
+  static constexpr int kRowsPerWave = kBf16BM / (THREADS / 64);               // activation rows per wave
   static constexpr int kValuPerStore = 96;   // VALU ops of one store part (about)
   static constexpr int kRegLoads = 3 * kRowGroups;   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = false;
@@ -67,11 +69,12 @@ struct W4A16Loader {
     const int lane = tid & 63, wave = tid >> 6;
     const uint32_t lr = lane >> 3, lp = lane & 7;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t row = 64 * wave + 8 * j + lr;         // lds_swz<8>(row) == 4 (j % 2) + lr / 2
+    for (int j = 0; j < kRowsPerWave / 8; ++j) {
+      // kRowsPerWave is a multiple of 16: lds_swz<8>(row) == 4 (j % 2) + lr / 2
+      const uint32_t row = kRowsPerWave * wave + 8 * j + lr;
       const uint32_t off = in_range_or_oob(row * ldxb + (uint32_t)kt * 128 + ((lp ^ (4 * (j & 1) + (lr >> 1))) << 4),
                                            (uint32_t)kt, ngrp);
-      buf_ld16_lds(rx, la + (64 * wave + 8 * j) * kBf16RowBytes, off);
+      buf_ld16_lds(rx, la + (kRowsPerWave * wave + 8 * j) * kBf16RowBytes, off);
     }
   }
   template <int SET>
@@ -79,7 +82,7 @@ struct W4A16Loader {
     const uint32_t cw = tid & 1;
 #pragma unroll
     for (int j = 0; j < kRowGroups; ++j) {
-      const uint32_t row = (tid >> 1) + 128 * j;
+      const uint32_t row = (tid >> 1) + kRowsPerGroup * j;
       cb[SET][j] = buf_ld16(rc, in_range_or_oob(row * kb + (uint32_t)kt * 32 + cw * 16, (uint32_t)kt, ngrp));
       const uint32_t go = in_range_or_oob((row * ngrp + (uint32_t)kt) * 2, (uint32_t)kt, ngrp);
       sb[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
@@ -91,7 +94,7 @@ struct W4A16Loader {
   __device__ __forceinline__ void store(uint8_t*, uint8_t* lb) {
     if (P >= kRowGroups) return;
     const int cw = tid & 1, r = tid >> 1;
-    const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
+    const int off = r * kBf16RowBytes + P * kRowsPerGroup * kBf16RowBytes;
     const float sc = __uint_as_float(sb[SET][P] << 16);
     const float zs = __uint_as_float(zb[SET][P] << 16) * sc;
     u32x4 o[4];
@@ -101,9 +104,10 @@ struct W4A16Loader {
   }
 };
 
-// One output tile of 256 activation rows at (m0, n0).  G = 4: the 4 waves as 2 x 2,
-// each 128 x 32 F (64 F weight rows); G = 2: the 4 waves stacked along M, each
-// 64 x 32 F (32 F weight rows).
+// One output tile of 256 activation rows at (m0, n0) for 4 waves: G = 2, the waves
+// stacked along M, each 64 x 32 F (32 F weight rows; the narrow tiles below).  G = 4
+// (2 x 2 waves of 128 x 32 F) is the 4-wave form of the whole tiles, which run with 8
+// waves instead.
 template <bool OUT_F32, int F, int G>
 __device__ __forceinline__ void w4a16_tile(
     uint8_t* lds, const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
@@ -123,25 +127,53 @@ __device__ __forceinline__ void w4a16_tile(
                                             lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
 }
 
-// Whole 256 x 256 tiles and halves (256 x 128) of the leftover ones: see tile_unit.
+// Whole 256 x 256 tiles and halves (256 x 128) of the leftover ones (see tile_unit),
+// with 8 waves, two per SIMD: wave w owns m in [128 (w % 2), +128) and n in
+// [32 F (w / 2), +32 F).  Its 128 accumulators per lane (F = 2) leave room for the
+// SIMD's second wave, so one wave's weight conversion and loads issue while the
+// other's MFMAs run (327-329 against 348-350 us at M = 4608 for 4 waves of 128 x 128,
+// same box); each thread converts one 32-code chunk per K-tile.
+constexpr int kW4Threads8 = 512;
+constexpr int kW4Lds8 = 8 * EpilogueShape<true, 2, 128>::kStageWaveBytes > kBf16MainLds
+                            ? 8 * EpilogueShape<true, 2, 128>::kStageWaveBytes
+                            : kBf16MainLds;                             // 144 KB
+template <bool OUT_F32, int F>
+__device__ __forceinline__ void w4a16_tile8(
+    uint8_t* lds, const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
+    const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int64_t m0, int64_t n0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
+  W4A16Loader<128 * F, 1, kW4Threads8> ld;
+  ld.init(x, ldx, wc, ws, wz, M, N, K, m0, n0, tid);
+  v16f acc[F][4];
+  bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
+  const int64_t n_base = n0 + wy * 32 * F, m_base = m0 + wx * 128;
+  __syncthreads();                           // all waves are done reading operand tiles
+  epilogue_store<OUT_F32, F, 128, false, 4>(acc, n_base, m_base, M, N, bias, y, ldy, lane,
+                                            lds + wave * EpilogueShape<OUT_F32, F, 128>::kStageWaveBytes);
+}
+
 template <bool OUT_F32>
-__global__ __launch_bounds__(kBf16Threads, 1) void gemm_w4a16_kernel(
+__global__ __launch_bounds__(kW4Threads8, 1) void gemm_w4a16_kernel8(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
     const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wz, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
     int full) {
-  static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
+  static_assert(8 * EpilogueShape<true, 2, 128>::kStageWaveBytes <= kW4Lds8 &&
+                    8 * EpilogueShape<false, 2, 128>::kStageWaveBytes <= kW4Lds8,
+                "the epilogue stages each wave's output in the operand LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kW4Lds8];
   int vt, half, tm, tn;
   const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
   tile_of(vt, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   if (!is_half) {
-    w4a16_tile<OUT_F32, 4, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
-                              (int64_t)tn * kBf16BN);
+    w4a16_tile8<OUT_F32, 2>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
+                            (int64_t)tn * kBf16BN);
   } else {
     if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
-    w4a16_tile<OUT_F32, 2, 4>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
-                              (int64_t)tn * kBf16BN + 128 * half);
+    w4a16_tile8<OUT_F32, 1>(lds, x, ldx, wc, ws, wz, M, N, K, bias, y, ldy, (int64_t)tm * kBf16BM,
+                            (int64_t)tn * kBf16BN + 128 * half);
   }
 }
 
@@ -180,10 +212,10 @@ hipError_t launch_gemm_w4a16(const uint16_t* x, int64_t ldx, const uint8_t* wc,
   int full, grid;
   bf16_tile_split(tiles_m * tiles_n, &full, &grid);
   if (ep.out_f32)
-    hipLaunchKernelGGL(gemm_w4a16_kernel<true>, dim3(grid), dim3(kBf16Threads), 0, s, x, ldx, wc, ws,
+    hipLaunchKernelGGL(gemm_w4a16_kernel8<true>, dim3(grid), dim3(kW4Threads8), 0, s, x, ldx, wc, ws,
                        wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
   else
-    hipLaunchKernelGGL(gemm_w4a16_kernel<false>, dim3(grid), dim3(kBf16Threads), 0, s, x, ldx, wc, ws,
+    hipLaunchKernelGGL(gemm_w4a16_kernel8<false>, dim3(grid), dim3(kW4Threads8), 0, s, x, ldx, wc, ws,
                        wz, M, N, K, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
   return hipGetLastError();
 }
