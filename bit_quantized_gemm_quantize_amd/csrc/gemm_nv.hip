@@ -31,21 +31,24 @@ __device__ __forceinline__ void nv_dequant_chunk(u32x4 codes, uint32_t sc2, u32x
 }
 
 // Per K-tile (64 K) and operand: 256 (weights: TN) rows x 2 chunks of 32 codes;
-// thread tid owns chunk c = tid & 1 of rows tid/2 and tid/2 + 128, with the two
-// E4M3 scale bytes of each chunk.  Reads past M / N / K return zeros (buffer range
-// checks).
-template <int TN, int SETS>
+// thread tid owns chunk c = tid & 1 of rows tid/2 (and tid/2 + 128 with 256
+// threads), with the two E4M3 scale bytes of each chunk.  Reads past M / N / K, and
+// weight rows past TN, return zeros (buffer range checks).
+template <int TN, int SETS, int THREADS>
 struct NvLoader {
   static constexpr int kSets = SETS;          // register sets: loads SETS K-tiles ahead
+  static constexpr int kRowsPerGroup = THREADS / 2;
+  static constexpr int kGroupsA = kBf16BM / kRowsPerGroup;                      // rows per thread
+  static constexpr int kGroupsB = (TN + kRowsPerGroup - 1) / kRowsPerGroup;
   static constexpr int kValuPerStore = 72;    // VALU ops of one store part (about)
-  static constexpr int kRegLoads = 4 + 2 * (TN / 128);   // VMEM instructions of issue_regs
+  static constexpr int kRegLoads = 2 * kGroupsA + 2 * kGroupsB;   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = true;   // two operands to convert: see bf16_ktile_late
   static constexpr bool kF16 = true;          // fp16 operands and MFMA
   __amdgpu_buffer_rsrc_t rca, rsa, rcb, rsb;
   uint32_t kb, sbytes, nchunk;
   int tid;
-  u32x4 ca[SETS][2], cb[SETS][2];
-  uint32_t sa[SETS][2], sb[SETS][2];
+  u32x4 ca[SETS][kGroupsA], cb[SETS][kGroupsB];
+  uint32_t sa[SETS][kGroupsA], sb[SETS][kGroupsB];
 
   __device__ __forceinline__ void init(const uint8_t* ac, const uint8_t* as, const uint8_t* bc,
                                        const uint8_t* bs, int64_t M, int64_t N, int64_t K,
@@ -63,13 +66,13 @@ struct NvLoader {
   __device__ __forceinline__ void issue_regs(int kt) {
     const uint32_t chunk = (uint32_t)kt * 2 + (tid & 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t row = (tid >> 1) + 128 * j;
+    for (int j = 0; j < kGroupsA; ++j) {
+      const uint32_t row = (tid >> 1) + kRowsPerGroup * j;
       const uint32_t co = in_range_or_oob(row * kb + chunk * 16, chunk, nchunk);
       const uint32_t so = in_range_or_oob(row * sbytes + chunk * 2, chunk, nchunk);
       ca[SET][j] = buf_ld16(rca, co);
       sa[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rsa, (int)so, 0, 0);
-      if (j < TN / 128) {
+      if (j < kGroupsB) {
         cb[SET][j] = buf_ld16(rcb, co);
         sb[SET][j] = __builtin_amdgcn_raw_buffer_load_b16(rsb, (int)so, 0, 0);
       }
@@ -78,14 +81,15 @@ struct NvLoader {
   // half P: both operands' chunks of row group P
   template <int P, int SET>
   __device__ __forceinline__ void store(uint8_t* la, uint8_t* lb) {
-    // row (tid >> 1) + 128 P: its swizzle does not depend on P
+    // row (tid >> 1) + kRowsPerGroup P: its swizzle does not depend on P
+    if (P >= kGroupsA) return;
     const int c = tid & 1, r = tid >> 1;
-    const int off = r * kBf16RowBytes + P * 128 * kBf16RowBytes;
+    const int off = r * kBf16RowBytes + P * kRowsPerGroup * kBf16RowBytes;
     u32x4 o[4];
     nv_dequant_chunk(ca[SET][P], sa[SET][P], o);
 #pragma unroll
     for (int d = 0; d < 4; ++d) st16(la + off + (((4 * c + d) ^ lds_swz<8>(r)) << 4), o[d]);
-    if (P < TN / 128) {
+    if (P < kGroupsB) {
       nv_dequant_chunk(cb[SET][P], sb[SET][P], o);
 #pragma unroll
       for (int d = 0; d < 4; ++d) st16(lb + off + (((4 * c + d) ^ lds_swz<8>(r)) << 4), o[d]);
@@ -93,7 +97,15 @@ struct NvLoader {
   }
 };
 
-// One output tile of 256 activation rows x 64 F weight rows at (m0, n0).
+// One output tile of 256 activation rows x 128 F weight rows at (m0, n0), with 8
+// waves, two per SIMD: wave w owns m in [128 (w % 2), +128) and n in [32 F (w / 2),
+// +32 F), 128 accumulators per lane (F = 2), so one wave's conversion and loads issue
+// while the SIMD's other wave runs MFMAs; each thread converts one chunk of each
+// operand per K-tile.
+constexpr int kNvThreads = 512;
+constexpr int kNvLds = 8 * EpilogueShape<true, 2, 128>::kStageWaveBytes > kBf16MainLds
+                           ? 8 * EpilogueShape<true, 2, 128>::kStageWaveBytes
+                           : kBf16MainLds;                              // 144 KB
 template <int R, bool OUT_F32, int F>
 __device__ __forceinline__ void nv_tile(
     uint8_t* lds, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
@@ -104,7 +116,7 @@ __device__ __forceinline__ void nv_tile(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;
   // one register set: a second one (loads two K-tiles ahead) measured the same
-  NvLoader<64 * F, 1> ld;
+  NvLoader<128 * F, 1, kNvThreads> ld;
   ld.init(ac, as, bc, bs, M, N, K, m0, n0, tid);
   v16f acc[F][4];
   bf16_mainloop(acc, ld, K, lds, wx, wy, lane);
@@ -127,23 +139,25 @@ __device__ __forceinline__ void nv_tile(
 
 // Whole 256 x 256 tiles and halves (256 x 128) of the leftover ones: see tile_unit.
 template <int R, bool OUT_F32>
-__global__ __launch_bounds__(kBf16Threads, 1) void gemm_nv_kernel(
+__global__ __launch_bounds__(kNvThreads, 1) void gemm_nv_kernel(
     const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, const float* __restrict__ ats,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, const float* __restrict__ bts,
     int64_t M, int64_t N, int64_t K, const float* __restrict__ t, const uint16_t* __restrict__ l2t,
     const uint16_t* __restrict__ bias, void* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
     int full) {
-  static_assert(kEpilogueLdsBytes <= kBf16MainLds, "the epilogue stages its output in the operand LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBf16MainLds];
+  static_assert(8 * EpilogueShape<true, 2, 128>::kStageWaveBytes <= kNvLds &&
+                    8 * EpilogueShape<false, 2, 128>::kStageWaveBytes <= kNvLds,
+                "the epilogue stages each wave's output in the operand LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kNvLds];
   int vt, half, tm, tn;
   const bool is_half = tile_unit(blockIdx.x, tiles_m * tiles_n, full, &vt, &half);
   tile_of(vt, tiles_m, tiles_n, kBf16GroupM, &tm, &tn);
   if (!is_half) {
-    nv_tile<R, OUT_F32, 4>(lds, ac, as, ats, bc, bs, bts, M, N, K, t, l2t, bias, y, ldy,
+    nv_tile<R, OUT_F32, 2>(lds, ac, as, ats, bc, bs, bts, M, N, K, t, l2t, bias, y, ldy,
                            (int64_t)tm * kBf16BM, (int64_t)tn * kBf16BN);
   } else {
     if ((int64_t)tn * 256 + 128 * half >= N) return;       // half past the last weight row
-    nv_tile<R, OUT_F32, 2>(lds, ac, as, ats, bc, bs, bts, M, N, K, t, l2t, bias, y, ldy,
+    nv_tile<R, OUT_F32, 1>(lds, ac, as, ats, bc, bs, bts, M, N, K, t, l2t, bias, y, ldy,
                            (int64_t)tm * kBf16BM, (int64_t)tn * kBf16BN + 128 * half);
   }
 }
@@ -155,7 +169,7 @@ static void queue(const uint8_t* ac, const uint8_t* as, const float* ats, const 
   const int tiles_m = (int)((M + kBf16BM - 1) / kBf16BM), tiles_n = (int)((N + kBf16BN - 1) / kBf16BN);
   int full, grid;
   bf16_tile_split(tiles_m * tiles_n, &full, &grid);
-  hipLaunchKernelGGL((gemm_nv_kernel<R, F32>), dim3(grid), dim3(kBf16Threads), 0, s, ac, as, ats, bc,
+  hipLaunchKernelGGL((gemm_nv_kernel<R, F32>), dim3(grid), dim3(kNvThreads), 0, s, ac, as, ats, bc,
                      bs, bts, M, N, K, ep.t, ep.l2t, ep.bias, ep.y, ep.ldy, tiles_m, tiles_n, full);
 }
 
