@@ -2,11 +2,11 @@
 // NVFP4 path on the fp16 MFMA (Loader::kF16 picks the instruction; the operand
 // layout is the same).
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), 128 x 128 per
-// wave as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16; or, to fill the CUs when tiles
-// are few, half tiles of 256 x 128 (128 x 64 per wave, F = 2 weight sub-tiles
-// instead of 4), or tiles of 256 x 96 with the waves stacked along M (64 x 96 per
-// wave: G = 2 activation sub-tiles of 32 rows, F = 3).  K advances in tiles of 64
+// Tiling: a wave owns G activation sub-tiles of 32 rows and F weight sub-tiles of 32
+// columns (32 x 32 tiles of v_mfma_f32_32x32x16_bf16 / _f16); the callers use 256 x
+// 256 output tiles on 8 waves (two per SIMD) of 128 x 64 (G = 4, F = 2), half tiles of
+// 256 x 128 on the same 8 waves (F = 1) to fill the CUs when tiles are few, and tiles
+// of 256 x 96 on 4 waves stacked along M (64 x 96 per wave: G = 2, F = 3).  K advances in tiles of 64
 // elements: each operand tile is 256 rows x 64 bf16 (128 bytes per row) in LDS,
 // 16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ lds_swz<8>(r), for the
 // 64-bank LDS), two stages, one barrier per K-tile.
