@@ -25,10 +25,16 @@ namespace q4 {
 namespace {
 
 constexpr int kI4BM = 256, kI4BN = 256, kI4KT = 256, kI4KTB = kI4KT / 2;
-constexpr int kI4Waves = 4, kI4Threads = 64 * kI4Waves;
-constexpr int kI4Lds = 2 * 2 * kI4BM * kI4KTB;                      // [operand][stage]
-static_assert(kI4Waves * EpilogueShape<true, 4, 128>::kStageWaveBytes <= kI4Lds &&
-                  kI4Waves * EpilogueShape<false, 4, 128>::kStageWaveBytes <= kI4Lds,
+// 8 waves, two per SIMD: wave (wm, wn) = (w % 2, w / 2) owns 128 x 32 F (F = 2 in a
+// whole tile, 128 int32 accumulators per lane), so one wave's nibble widening issues
+// while the SIMD's other wave runs MFMAs.  The code also builds with 4 waves of
+// 128 x 128 (F = 4).
+constexpr int kI4Waves = 8, kI4Threads = 64 * kI4Waves;
+constexpr int kI4FFull = 512 / (32 * kI4Waves), kI4FHalf = kI4FFull / 2;   // weight sub-tiles per wave
+constexpr int kI4OperandLds = 2 * 2 * kI4BM * kI4KTB;               // [operand][stage]
+constexpr int kI4StageLds = kI4Waves * EpilogueShape<true, kI4FFull, 128>::kStageWaveBytes;
+constexpr int kI4Lds = kI4StageLds > kI4OperandLds ? kI4StageLds : kI4OperandLds;
+static_assert(kI4Waves * EpilogueShape<false, kI4FFull, 128>::kStageWaveBytes <= kI4Lds,
               "the epilogue stages each wave's output in the operand LDS");
 
 // 8 packed signed nibbles -> 8 int8: the even nibbles in lo, the odd ones in hi.
@@ -61,7 +67,8 @@ __device__ __forceinline__ void i4_tile(uint8_t* lds_raw, const uint8_t* __restr
                                         const float* __restrict__ bs, int64_t M, int64_t N, int64_t K,
                                         const uint16_t* __restrict__ bias, void* __restrict__ y,
                                         int64_t ldy, int64_t m0, int64_t n0) {
-  constexpr int kTN = 64 * F, kRowsB = kTN / kI4Waves;     // weight rows: per tile, per wave
+  constexpr int kTN = 32 * F * (kI4Waves / 2), kRowsB = kTN / kI4Waves;   // weight rows: per tile, per wave
+  constexpr int kRowsA = kI4BM / kI4Waves;                               // activation rows per wave
   auto& lds = *reinterpret_cast<uint8_t(*)[2][2][kI4BM * kI4KTB]>(lds_raw);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -73,7 +80,7 @@ __device__ __forceinline__ void i4_tile(uint8_t* lds_raw, const uint8_t* __restr
   const auto rc_a = make_rsrc(ac + m0 * kbytes, rows_a * kbytes);
   const auto rc_b = make_rsrc(bc + n0 * kbytes, rows_b * kbytes);
 
-  // K-tile kt -> stage: each wave moves 64 activation and kRowsB weight rows, 8 rows
+  // K-tile kt -> stage: each wave moves kRowsA activation and kRowsB weight rows, 8 rows
   // of 128 bytes per instruction (lane i: row i / 8, stored chunk i % 8 holding
   // global chunk (i % 8) ^ lds_swz<8>(row)); rows and blocks past the matrix read as zero
   const int lr = lane >> 3, lp = lane & 7;
@@ -86,9 +93,9 @@ __device__ __forceinline__ void i4_tile(uint8_t* lds_raw, const uint8_t* __restr
       koff[jp] = blk < nblk ? blk * 16 : kOOB;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t row = 64 * wave + 8 * j + lr;
-      buf_ld16_lds(rc_a, &lds[0][stage][(64 * wave + 8 * j) * kI4KTB], row * kbytes + koff[j & 1]);
+    for (int j = 0; j < kRowsA / 8; ++j) {
+      const uint32_t row = kRowsA * wave + 8 * j + lr;
+      buf_ld16_lds(rc_a, &lds[0][stage][(kRowsA * wave + 8 * j) * kI4KTB], row * kbytes + koff[j & 1]);
     }
 #pragma unroll
     for (int j = 0; j < kRowsB / 8; ++j) {
@@ -203,9 +210,9 @@ __global__ __launch_bounds__(kI4Threads) void gemm_i4_kernel(
   const int64_t m0 = (int64_t)tm * kI4BM, n0 = (int64_t)tn * kI4BN + (is_half ? 128 * half : 0);
   if (n0 >= N) return;                                   // a half past the last weight row
   if (is_half)
-    i4_tile<OUT_F32, 2>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0);
+    i4_tile<OUT_F32, kI4FHalf>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0);
   else
-    i4_tile<OUT_F32, 4>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0);
+    i4_tile<OUT_F32, kI4FFull>(lds_raw, ac, as, bc, bs, M, N, K, bias, y, ldy, m0, n0);
 }
 
 }  // namespace
