@@ -40,7 +40,7 @@ struct NvLoader {
   static constexpr int kRowsPerGroup = THREADS / 2;
   static constexpr int kGroupsA = kBf16BM / kRowsPerGroup;                      // rows per thread
   static constexpr int kGroupsB = (TN + kRowsPerGroup - 1) / kRowsPerGroup;
-  static constexpr int kValuPerStore = 72;    // VALU ops of one store part (about)
+  static constexpr int kValuPerStore = 36;    // VALU ops spread over one store part's MFMAs (tuned)
   static constexpr int kRegLoads = 2 * kGroupsA + 2 * kGroupsB;   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = true;   // two operands to convert: see bf16_ktile_late
   static constexpr bool kF16 = true;          // fp16 operands and MFMA

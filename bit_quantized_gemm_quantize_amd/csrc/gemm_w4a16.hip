@@ -43,7 +43,7 @@ struct W4A16Loader {
   static constexpr int kRowsPerGroup = THREADS / 2;
   static constexpr int kRowGroups = (TN + kRowsPerGroup - 1) / kRowsPerGroup;   // weight rows per thread
   static constexpr int kRowsPerWave = kBf16BM / (THREADS / 64);               // activation rows per wave
-  static constexpr int kValuPerStore = 96;   // VALU ops of one store part (about)
+  static constexpr int kValuPerStore = 48;   // VALU ops spread over one store part's MFMAs (tuned)
   static constexpr int kRegLoads = 3 * kRowGroups;   // VMEM instructions of issue_regs
   static constexpr bool kLateStores = false;
   static constexpr bool kF16 = false;         // bf16 operands and MFMA
